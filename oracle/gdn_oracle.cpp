@@ -1,0 +1,184 @@
+// Sequential CPU oracle for the Gated DeltaNet recurrent forward step.
+//
+// TEST INFRASTRUCTURE ONLY. This file is the checker the HIP path is compared
+// against. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+// may load it; the product path never links, imports or calls it, and it shares
+// no code, header, table or helper with the HIP library.
+//
+// What it computes (mlx-native 0.9.2, "gated_delta_net_decode_capture.metal",
+// the token loop of gated_delta_net_decode_capture_impl; recurrence also stated
+// in mlx-native 0.4.0 "src/ops/gated_delta_net.rs", module doc): for every
+// sequence s and value head vh, a D_v x D_k state X (row i = the D_k keys of
+// value channel i) is carried across tokens t. Per token:
+//
+//   alpha   = exp(-g[s,t,vh]),  b = beta[s,t,vh]
+//   X[i,:]  = alpha * X[i,:]                       (decay first)
+//   sk_i    = sum_j X[i,j] * k[s,t,kh,j]           (read-out of the decayed state)
+//   d_i     = (v[s,t,vh,i] - sk_i) * b
+//   X[i,:]  = X[i,:] + d_i * k[s,t,kh,:]           (rank-1 delta write)
+//   y_i     = sum_j X[i,j] * q[s,t,kh,j]           (read-out of the updated state)
+//   out[s,t,vh,i] = y_i * q_scale
+//
+// with q_scale = 1 when the params word q_scale_bits is 0 and the IEEE-754
+// binary32 value of those bits otherwise (mlx-native 0.21.1
+// "src/ops/gated_delta_net_decode.rs", module doc "Buffer / params contract";
+// capture kernel, q_scale fold-in). When a capture buffer is given, the state
+// after token t's update is copied to capture[s,t,vh] (capture kernel header,
+// "Memory layout for state_capture"). The final state goes to state_out.
+//
+// The GQA key head kh is chosen by an explicit head-map argument because the
+// pages show two maps: kh = vh % n_k_heads (capture kernel) and
+// kh = vh / (n_v_heads / n_k_heads) (0.4.0 module doc "GQA broadcast" and its
+// scalar CPU reference).
+//
+// Layouts are the pages' innermost-first ones (0.4.0 module doc "Memory layouts"):
+//   q, k          [D_k, n_k_heads, n_tokens, n_seqs]   (d_k fastest)
+//   v, output     [D_v, n_v_heads, n_tokens, n_seqs]
+//   g, beta       [n_v_heads, n_tokens, n_seqs]
+//   state_in/out  [D_k, D_v, n_v_heads, n_seqs]
+//   state_capture [D_k, D_v, n_v_heads, n_tokens, n_seqs]
+//
+// Arithmetic: one template, instantiated for float (the oracle proper: every
+// operation rounded to binary32, sums taken over j in increasing order, built
+// with -ffp-contract=off so no multiply-add is fused) and for double (a shadow
+// that widens the f32 inputs once and keeps everything in binary64; it only
+// measures the error of the f32 results).
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "gdn_oracle.h"
+
+namespace {
+
+template <typename real>
+real decay_factor(float g);
+
+template <>
+float decay_factor<float>(float g) {
+  return expf(-g);
+}
+
+template <>
+double decay_factor<double>(float g) {
+  return exp(-static_cast<double>(g));
+}
+
+float scale_from_bits(uint32_t bits) {
+  if (bits == 0u) return 1.0f;
+  float f;
+  std::memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+template <typename real>
+int run(const float *q, const float *k, const float *v, const float *g,
+        const float *beta, const float *state_in, const oracle_gdn_shape *p,
+        int head_map, real *output, real *state_out, real *capture) {
+  if (p == nullptr || q == nullptr || k == nullptr || v == nullptr ||
+      g == nullptr || beta == nullptr || state_in == nullptr ||
+      output == nullptr || state_out == nullptr)
+    return 1;
+  if (p->d_k == 0 || p->d_v == 0 || p->n_k_heads == 0 || p->n_v_heads == 0 ||
+      p->n_tokens == 0 || p->n_seqs == 0)
+    return 2;
+  if (p->n_v_heads % p->n_k_heads != 0) return 3;
+  if (head_map != ORACLE_HEAD_MAP_MOD && head_map != ORACLE_HEAD_MAP_DIV)
+    return 4;
+
+  const uint64_t Dk = p->d_k, Dv = p->d_v, Hk = p->n_k_heads,
+                 Hv = p->n_v_heads, T = p->n_tokens, S = p->n_seqs;
+  const uint64_t group_ratio = Hv / Hk;
+  const real q_scale = static_cast<real>(scale_from_bits(p->q_scale_bits));
+
+  // Flat offsets of the innermost-first layouts.
+  auto at_qk = [&](uint64_t s, uint64_t t, uint64_t kh, uint64_t j) {
+    return ((s * T + t) * Hk + kh) * Dk + j;
+  };
+  auto at_v = [&](uint64_t s, uint64_t t, uint64_t vh, uint64_t i) {
+    return ((s * T + t) * Hv + vh) * Dv + i;
+  };
+  auto at_scalar = [&](uint64_t s, uint64_t t, uint64_t vh) {
+    return (s * T + t) * Hv + vh;
+  };
+  auto at_state = [&](uint64_t s, uint64_t vh, uint64_t i, uint64_t j) {
+    return ((s * Hv + vh) * Dv + i) * Dk + j;
+  };
+  auto at_capture = [&](uint64_t s, uint64_t t, uint64_t vh, uint64_t i,
+                        uint64_t j) {
+    return (((s * T + t) * Hv + vh) * Dv + i) * Dk + j;
+  };
+
+  std::vector<real> X(Dv * Dk);
+  for (uint64_t s = 0; s < S; ++s) {
+    for (uint64_t vh = 0; vh < Hv; ++vh) {
+      const uint64_t kh =
+          head_map == ORACLE_HEAD_MAP_MOD ? vh % Hk : vh / group_ratio;
+
+      for (uint64_t i = 0; i < Dv; ++i)
+        for (uint64_t j = 0; j < Dk; ++j)
+          X[i * Dk + j] = static_cast<real>(state_in[at_state(s, vh, i, j)]);
+
+      for (uint64_t t = 0; t < T; ++t) {
+        const real alpha = decay_factor<real>(g[at_scalar(s, t, vh)]);
+        const real b = static_cast<real>(beta[at_scalar(s, t, vh)]);
+
+        for (uint64_t i = 0; i < Dv; ++i) {
+          real *row = &X[i * Dk];
+
+          real sk = 0;
+          for (uint64_t j = 0; j < Dk; ++j) {
+            row[j] = alpha * row[j];
+            sk = sk + row[j] * static_cast<real>(k[at_qk(s, t, kh, j)]);
+          }
+
+          const real d = (static_cast<real>(v[at_v(s, t, vh, i)]) - sk) * b;
+
+          real y = 0;
+          for (uint64_t j = 0; j < Dk; ++j) {
+            row[j] = row[j] + d * static_cast<real>(k[at_qk(s, t, kh, j)]);
+            y = y + row[j] * static_cast<real>(q[at_qk(s, t, kh, j)]);
+          }
+
+          output[at_v(s, t, vh, i)] = y * q_scale;
+        }
+
+        if (capture != nullptr)
+          for (uint64_t i = 0; i < Dv; ++i)
+            for (uint64_t j = 0; j < Dk; ++j)
+              capture[at_capture(s, t, vh, i, j)] = X[i * Dk + j];
+      }
+
+      for (uint64_t i = 0; i < Dv; ++i)
+        for (uint64_t j = 0; j < Dk; ++j)
+          state_out[at_state(s, vh, i, j)] = X[i * Dk + j];
+    }
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_gdn_forward_f32(const float *q, const float *k, const float *v,
+                           const float *g, const float *beta,
+                           const float *state_in, const oracle_gdn_shape *p,
+                           int head_map, float *output, float *state_out,
+                           float *state_capture) {
+  return run<float>(q, k, v, g, beta, state_in, p, head_map, output, state_out,
+                    state_capture);
+}
+
+int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
+                           const float *g, const float *beta,
+                           const float *state_in, const oracle_gdn_shape *p,
+                           int head_map, double *output, double *state_out,
+                           double *state_capture) {
+  return run<double>(q, k, v, g, beta, state_in, p, head_map, output,
+                     state_out, state_capture);
+}
+
+}  // extern "C"

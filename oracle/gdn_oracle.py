@@ -1,0 +1,121 @@
+"""ctypes wrapper around the sequential C++ oracle (gdn_oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). Arrays are numpy, in the
+torch-style row-major shapes that equal the pages' innermost-first layouts
+(mlx-native 0.4.0 "src/ops/gated_delta_net.rs", module doc "Memory layouts"):
+
+    q, k          (S, T, H_k, D_k)
+    v             (S, T, H_v, D_v)
+    g, beta       (S, T, H_v)
+    state_in      (S, H_v, D_v, D_k)
+    output        (S, T, H_v, D_v)
+    state_capture (S, T, H_v, D_v, D_k)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "gdn_oracle.cpp")
+HEADER = os.path.join(HERE, "gdn_oracle.h")
+LIBRARY = os.path.join(HERE, "liboracle_gdn.so")
+
+HEAD_MAP_MOD = 0  # kh = vh % n_k_heads (capture kernel, mlx-native 0.9.2)
+HEAD_MAP_DIV = 1  # kh = vh / (n_v_heads / n_k_heads) (mlx-native 0.4.0 doc)
+
+# Plain IEEE arithmetic: no fused multiply-add, no fast-math reassociation.
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
+            "-fno-fast-math"]
+
+_lock = threading.Lock()
+_libs: dict = {}
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_uint32) for name in
+                ("d_k", "d_v", "n_k_heads", "n_v_heads", "n_tokens", "n_seqs",
+                 "q_scale_bits")]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle_gdn.so with g++ and return its path."""
+    if force or not os.path.exists(LIBRARY) or (
+            os.path.getmtime(LIBRARY) < max(os.path.getmtime(SOURCE),
+                                            os.path.getmtime(HEADER))):
+        tmp = LIBRARY + f".tmp{os.getpid()}"
+        subprocess.run(["g++", *CXXFLAGS, SOURCE, "-o", tmp], check=True)
+        os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+def _load(path: str | None = None):
+    """Load (once) the oracle library at path (default: the built one)."""
+    with _lock:
+        key = path or LIBRARY
+        if key not in _libs:
+            if path is None:
+                build(force=False)
+            lib = ctypes.CDLL(key)
+            for name, real in (("oracle_gdn_forward_f32", ctypes.c_float),
+                               ("oracle_gdn_forward_f64", ctypes.c_double)):
+                fn = getattr(lib, name)
+                fp = ctypes.POINTER(ctypes.c_float)
+                rp = ctypes.POINTER(real)
+                fn.argtypes = [fp] * 6 + [ctypes.POINTER(_Shape), ctypes.c_int,
+                                          rp, rp, rp]
+                fn.restype = ctypes.c_int
+            _libs[key] = lib
+    return _libs[key]
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def reference(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
+              head_map: int = HEAD_MAP_MOD, capture: bool = False,
+              precision: str = "f32", library: str | None = None):
+    """Run the oracle. Returns (output, state_out) or (output, state_out, capture).
+
+    Shapes are taken from the arrays: q is (S, T, H_k, D_k), v is (S, T, H_v, D_v).
+    precision="f32" is the oracle proper; "f64" is the binary64 shadow.
+    library selects another build of gdn_oracle.cpp (the planted-mistake
+    tests use this); None means the regular build.
+    """
+    q, k, v, g, beta, state_in = (_f32(a) for a in (q, k, v, g, beta, state_in))
+    S, T, Hk, Dk = q.shape
+    Sv, Tv, Hv, Dv = v.shape
+    if k.shape != q.shape or (Sv, Tv) != (S, T):
+        raise ValueError("q, k, v disagree on (S, T) or q/k shapes differ")
+    if g.shape != (S, T, Hv) or beta.shape != (S, T, Hv):
+        raise ValueError("g and beta must be (S, T, H_v)")
+    if state_in.shape != (S, Hv, Dv, Dk):
+        raise ValueError("state_in must be (S, H_v, D_v, D_k)")
+
+    real, dtype, fname = {
+        "f32": (ctypes.c_float, np.float32, "oracle_gdn_forward_f32"),
+        "f64": (ctypes.c_double, np.float64, "oracle_gdn_forward_f64"),
+    }[precision]
+    out = np.empty((S, T, Hv, Dv), dtype=dtype)
+    st = np.empty((S, Hv, Dv, Dk), dtype=dtype)
+    cap = np.empty((S, T, Hv, Dv, Dk), dtype=dtype) if capture else None
+    shape = _Shape(Dk, Dv, Hk, Hv, T, S, q_scale_bits & 0xFFFFFFFF)
+    fp = ctypes.c_float
+    rc = getattr(_load(library), fname)(
+        _ptr(q, fp), _ptr(k, fp), _ptr(v, fp), _ptr(g, fp), _ptr(beta, fp),
+        _ptr(state_in, fp), ctypes.byref(shape), head_map,
+        _ptr(out, real), _ptr(st, real),
+        _ptr(cap, real) if cap is not None else ctypes.POINTER(real)())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return (out, st, cap) if capture else (out, st)
