@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet forward step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode] [--launch graph]
+
+One step is one forward call of the whole step (decay, read-out, delta, rank-1
+write, output, optional capture, final state) over one input set of the chosen
+workload, with every input already resident in HBM. Steps cycle through enough
+independent input sets ("layers", each with its own state, updated in place)
+that their total size is well above the 256 MB Infinity Cache, so each call
+reads its state from HBM as a decode layer does in a real model, where the
+other layers' traffic evicts it between steps.
+
+The K timed steps are enqueued as one HIP graph (launch-bound decode calls are
+captured in serving loops for the same reason) or, with --launch direct, one
+launch at a time. HIP events on the launch stream bracket the timed region and
+give the kernel's average launch duration, from which the roofline fraction is
+computed. Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from linear_attention_recurrence_forward_amd.workloads import (  # noqa: E402
+    WORKLOADS, make_inputs)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X FP32 vector, published (packed issue)
+INFINITY_CACHE_BYTES = 256 << 20
+RESIDENT_TARGET_BYTES = 1 << 30  # input sets cycled per run: >= 4x the cache
+METRIC = "GDN decode µs/layer + state HBM GB/s (%peak); prefill tokens/s at n_tokens=512"
+KERNEL_NAME = "gdn_recurrent"
+NAMES = ("q", "k", "v", "g", "beta", "state_in")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--launch", default="graph", choices=("graph", "direct"))
+    ap.add_argument("--layers", type=int, default=0,
+                    help="input sets to cycle through (0: enough for 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB "
+                         "(reference kernel for the HBM byte counters)")
+    return ap.parse_args(argv)
+
+
+def kernel_digest() -> str:
+    from linear_attention_recurrence_forward_amd import build
+    return build.source_digest()
+
+
+def traffic_from_profiles(workload: str, digest: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact
+    kernel build (None when absent or taken on another build)."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole calls for small workloads, a prefix of the sequences for large ones.
+    Returns the rate in the benchmark's unit and a description of the sample."""
+    import oracle
+    x = make_inputs(w)
+    bits = x["q_scale_bits"]
+    args = {n: x[n] for n in NAMES}
+    t0 = time.perf_counter()
+    oracle.reference(**{n: a[:1] for n, a in args.items()}, q_scale_bits=bits,
+                     capture=w.capture)
+    per_seq = time.perf_counter() - t0
+    seqs = max(1, min(w.n_seqs, int(budget_s / max(per_seq, 1e-9))))
+    calls = 1 if seqs < w.n_seqs else max(1, int(budget_s / (per_seq * w.n_seqs)))
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        oracle.reference(**{n: a[:seqs] for n, a in args.items()}, q_scale_bits=bits,
+                         capture=w.capture)
+    dt = time.perf_counter() - t0
+    frac = seqs / w.n_seqs
+    if w.name == "prefill":
+        value = calls * frac * w.n_seqs * w.n_tokens / dt
+        unit = "tokens/s"
+    else:
+        value = calls * frac * w.algorithmic_bytes() / dt / 1e9
+        unit = "GB/s"
+    sample = (f"{calls} oracle call(s) over {seqs} of {w.n_seqs} sequence(s) of the "
+              f"{w.name} workload, {dt:.1f} s, single thread")
+    return dict(value=value, unit=unit, cores=1, kind="oracle", sample=sample)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the op shards over sequences and value heads without any exchange, "
+              "so a multi-GPU figure would be N independent copies of this one.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import linear_attention_recurrence_forward_amd as gdn
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    x = make_inputs(w)
+    bits = x["q_scale_bits"]
+    alg_bytes = w.algorithmic_bytes()
+    layers = args.layers or max(2, math.ceil(RESIDENT_TARGET_BYTES / max(alg_bytes, 1)))
+    layers = min(layers, 4096)
+
+    # Resident input sets: same values, distinct memory (state updated in place).
+    host = {n: torch.from_numpy(x[n]) for n in NAMES}
+    sets = []
+    for _ in range(layers):
+        d = {n: host[n].to(dev) for n in NAMES}
+        d["output"] = torch.empty(x["v"].shape, device=dev)
+        d["capture"] = (torch.empty((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
+                                    device=dev) if w.capture else None)
+        sets.append(d)
+    params = gdn.params_for(sets[0]["q"], sets[0]["v"], bits)
+
+    def launch(i, stream):
+        d = sets[i % layers]
+        if w.capture:
+            gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                    d["state_in"], d["output"], d["state_in"],
+                                    d["capture"], params, stream)
+        else:
+            gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                            d["output"], d["state_in"], params, stream)
+
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+
+    def enqueue(n, offset):
+        if args.launch == "graph":
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(graph, stream=stream):
+                    for i in range(n):
+                        launch(offset + i, stream)
+            torch.cuda.synchronize()
+            return graph.replay
+        return lambda: [launch(offset + i, stream) for i in range(n)]
+
+    run_warm = enqueue(args.warmup, 0) if args.warmup > 0 else (lambda: None)
+    run_timed = enqueue(args.steps, args.warmup)
+    with torch.cuda.stream(stream):
+        run_warm()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()  # barrier: one rank only
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        run_timed()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 18  # floats
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    ms_per_step = wall * 1e3 / args.steps
+    digest = kernel_digest()
+    if w.name == "prefill":
+        metric_value = w.n_seqs * w.n_tokens * args.steps / wall
+        unit = "tokens/s"
+        achieved = w.flops() / kernel_s / 1e12
+        roofline = dict(bound="alu", achieved=achieved, peak=FP32_VECTOR_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=achieved / FP32_VECTOR_PEAK_TFLOPS)
+    else:
+        metric_value = alg_bytes * args.steps / wall / 1e9
+        unit = "GB/s"
+        achieved = alg_bytes / kernel_s / 1e9
+        roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=achieved / HBM_PEAK_GBPS)
+    roofline["traffic"] = traffic_from_profiles(w.name, digest)
+    roofline["kernel"] = KERNEL_NAME
+    roofline["kernel_us"] = kernel_s * 1e6
+
+    line = {
+        "metric": METRIC,
+        "value": metric_value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.description,
+            "d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads, "n_v_heads": w.n_v_heads,
+            "n_tokens": w.n_tokens, "n_seqs": w.n_seqs, "q_scale_bits": bits,
+            "capture": w.capture, "launch": args.launch, "resident_sets": layers,
+            "algorithmic_bytes_per_step": alg_bytes, "flops_per_step": w.flops(),
+        },
+        "us_per_layer": ms_per_step * 1e3,
+        "state_gbps": w.state_bytes() / kernel_s / 1e9,
+        "roofline": roofline,
+        "kernel_digest": digest[:16],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,210 @@
+"""ctypes binding of libgdn.so (include/gdn.h).
+
+Argument marshalling only: every step of the forward pass runs in the library's
+HIP kernels. torch supplies device memory and the current HIP stream. If the
+library is missing the calls raise; there is no other implementation to fall
+back to.
+
+The tensor checks here (device, dtype, contiguity, element counts) are the ones
+the pages make on their buffers before encoding (mlx-native 0.21.1
+src/ops/gated_delta_net_decode.rs, validate and
+dispatch_gated_delta_net_decode_with_capture); raw pointers carry no such
+information, so they cannot live in the C library.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import struct
+import threading
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libgdn.so")
+
+STATUS = {
+    0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_ZERO_DIM",
+    3: "GDN_ERR_ZERO_EXTENT", 4: "GDN_ERR_GQA_RATIO", 5: "GDN_ERR_UNSUPPORTED_DK",
+    6: "GDN_ERR_RESERVED_NONZERO", 7: "GDN_ERR_SIZE_OVERFLOW", 8: "GDN_ERR_MISALIGNED",
+    9: "GDN_ERR_ALIASING", 10: "GDN_ERR_LAUNCH",
+}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+
+EXPORTS = ("gdn_check_params", "gdn_forward", "gdn_forward_capture", "gdn_status_string")
+
+
+class GdnParams(ctypes.Structure):
+    """The 9-word params block: d_k, d_v, n_k_heads, n_v_heads, n_tokens,
+    n_seqs, two reserved zeros, q_scale_bits."""
+    _fields_ = [(n, ctypes.c_uint32) for n in
+                ("d_k", "d_v", "n_k_heads", "n_v_heads", "n_tokens", "n_seqs",
+                 "reserved6", "reserved7", "q_scale_bits")]
+
+    def counts(self) -> dict:
+        """Element count of every array for these params."""
+        ts = self.n_tokens * self.n_seqs
+        state = self.d_k * self.d_v * self.n_v_heads * self.n_seqs
+        return dict(q=self.d_k * self.n_k_heads * ts, k=self.d_k * self.n_k_heads * ts,
+                    v=self.d_v * self.n_v_heads * ts, output=self.d_v * self.n_v_heads * ts,
+                    g=self.n_v_heads * ts, beta=self.n_v_heads * ts,
+                    state_in=state, state_out=state, state_capture=state * self.n_tokens)
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{where}: {self.name}: {gdn_status_string(status)}")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY):
+                raise RuntimeError(
+                    f"{LIBRARY} is not built; build it with "
+                    "`python -m linear_attention_recurrence_forward_amd.build` "
+                    "(or __graft_entry__.build())")
+            lib = ctypes.CDLL(LIBRARY)
+            fp, p = ctypes.POINTER(ctypes.c_float), ctypes.POINTER(GdnParams)
+            lib.gdn_check_params.argtypes = [p]
+            lib.gdn_check_params.restype = ctypes.c_int
+            lib.gdn_forward.argtypes = [fp] * 8 + [p, ctypes.c_void_p]
+            lib.gdn_forward.restype = ctypes.c_int
+            lib.gdn_forward_capture.argtypes = [fp] * 9 + [p, ctypes.c_void_p]
+            lib.gdn_forward_capture.restype = ctypes.c_int
+            lib.gdn_status_string.argtypes = [ctypes.c_int]
+            lib.gdn_status_string.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def f32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def make_params(d_k, d_v, n_k_heads, n_v_heads, n_tokens, n_seqs, q_scale_bits=0,
+                reserved6=0, reserved7=0) -> GdnParams:
+    return GdnParams(d_k, d_v, n_k_heads, n_v_heads, n_tokens, n_seqs,
+                     reserved6, reserved7, q_scale_bits & 0xFFFFFFFF)
+
+
+def params_for(q: torch.Tensor, v: torch.Tensor, q_scale_bits: int = 0) -> GdnParams:
+    """Params from torch-shaped q (S, T, H_k, D_k) and v (S, T, H_v, D_v)."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be (S, T, H_k, D_k) and v (S, T, H_v, D_v)")
+    S, T, Hk, Dk = q.shape
+    Sv, Tv, Hv, Dv = v.shape
+    if (Sv, Tv) != (S, T):
+        raise ValueError(f"q {tuple(q.shape)} and v {tuple(v.shape)} disagree on (S, T)")
+    return make_params(Dk, Dv, Hk, Hv, T, S, q_scale_bits)
+
+
+def gdn_check_params(params: GdnParams) -> int:
+    """Status code of the host-only params check (0 = GDN_OK)."""
+    return _load().gdn_check_params(ctypes.byref(params))
+
+
+def gdn_status_string(status: int) -> str:
+    return _load().gdn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float))
+
+
+def _check_tensors(where: str, params: GdnParams, tensors: dict):
+    counts = params.counts()
+    device = None
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{where}: {name} must be a torch.Tensor")
+        if t.dtype != torch.float32:
+            raise ValueError(f"{where}: {name} must be f32 (got {t.dtype})")
+        if t.device.type != "cuda":
+            raise ValueError(f"{where}: {name} must be on the GPU (got {t.device})")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{where}: {name} is on {t.device}, other arrays on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous")
+        if t.numel() != counts[name]:
+            raise ValueError(f"{where}: {name} element count {t.numel()} != expected "
+                             f"{counts[name]}")
+    return device
+
+
+def _stream_handle(device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gdn_forward(q, k, v, g, beta, state_in, output, state_out, params: GdnParams,
+                stream=None) -> None:
+    """Enqueue one forward call (C: gdn_forward). Raises GdnError on a nonzero
+    status; the call is asynchronous on `stream` (default: current stream)."""
+    tensors = dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in, output=output,
+                   state_out=state_out)
+    lib = _load()
+    st = lib.gdn_check_params(ctypes.byref(params))
+    if st != 0:
+        raise GdnError(st, "gdn_forward")
+    device = _check_tensors("gdn_forward", params, tensors)
+    st = lib.gdn_forward(*(_ptr(t) for t in tensors.values()), ctypes.byref(params),
+                         _stream_handle(device, stream))
+    if st != 0:
+        raise GdnError(st, "gdn_forward")
+
+
+def gdn_forward_capture(q, k, v, g, beta, state_in, output, state_out, state_capture,
+                        params: GdnParams, stream=None) -> None:
+    """Enqueue one forward call that also writes the per-token state
+    (C: gdn_forward_capture). state_capture must hold exactly
+    n_tokens * d_k * d_v * n_v_heads * n_seqs floats."""
+    tensors = dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in, output=output,
+                   state_out=state_out, state_capture=state_capture)
+    lib = _load()
+    st = lib.gdn_check_params(ctypes.byref(params))
+    if st != 0:
+        raise GdnError(st, "gdn_forward_capture")
+    device = _check_tensors("gdn_forward_capture", params, tensors)
+    st = lib.gdn_forward_capture(*(_ptr(t) for t in tensors.values()),
+                                 ctypes.byref(params), _stream_handle(device, stream))
+    if st != 0:
+        raise GdnError(st, "gdn_forward_capture")
+
+
+def forward(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0, capture: bool = False,
+            output=None, state_out=None, state_capture=None, stream=None):
+    """Convenience wrapper on torch-shaped tensors:
+    q, k (S, T, H_k, D_k); v (S, T, H_v, D_v); g, beta (S, T, H_v);
+    state_in (S, H_v, D_v, D_k). Allocates missing outputs and returns
+    (output, state_out) or (output, state_out, state_capture)."""
+    params = params_for(q, v, q_scale_bits)
+    S, T, Hv, Dv = v.shape
+    Dk = q.shape[3]
+    if output is None:
+        output = torch.empty((S, T, Hv, Dv), dtype=torch.float32, device=q.device)
+    if state_out is None:
+        state_out = torch.empty((S, Hv, Dv, Dk), dtype=torch.float32, device=q.device)
+    if capture:
+        if state_capture is None:
+            state_capture = torch.empty((S, T, Hv, Dv, Dk), dtype=torch.float32,
+                                        device=q.device)
+        gdn_forward_capture(q, k, v, g, beta, state_in, output, state_out, state_capture,
+                            params, stream)
+        return output, state_out, state_capture
+    gdn_forward(q, k, v, g, beta, state_in, output, state_out, params, stream)
+    return output, state_out

@@ -1,0 +1,175 @@
+// C ABI of the Gated DeltaNet forward library (include/gdn.h): argument
+// validation, then one kernel launch. Mirrors the pages' validate-then-encode
+// dispatchers (mlx-native 0.21.1 src/ops/gated_delta_net_decode.rs: validate,
+// validate_params_buf, dispatch_gated_delta_net_decode[_with_capture]); the
+// element-count and dtype checks on tensors live in the Python binding, since
+// raw pointers carry neither.
+
+#include <stdint.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t *out) {
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+// Element counts of every array for params p (false on 64-bit overflow).
+struct Counts {
+  uint64_t qk, v, scalar, state, capture;
+};
+
+bool counts_of(const gdn_params *p, Counts *c) {
+  const uint64_t ts = (uint64_t)p->n_tokens * p->n_seqs;  // < 2^64
+  if (!mul_ok((uint64_t)p->d_k * p->n_k_heads, ts, &c->qk)) return false;
+  if (!mul_ok((uint64_t)p->d_v * p->n_v_heads, ts, &c->v)) return false;
+  if (!mul_ok((uint64_t)p->n_v_heads, ts, &c->scalar)) return false;
+  if (!mul_ok((uint64_t)p->d_k * p->d_v, (uint64_t)p->n_v_heads * p->n_seqs,
+              &c->state))
+    return false;
+  if (!mul_ok(c->state, p->n_tokens, &c->capture)) return false;
+  // Byte sizes must fit a signed 64-bit offset.
+  const uint64_t max_elems = (uint64_t)INT64_MAX / sizeof(float);
+  for (uint64_t n : {c->qk, c->v, c->scalar, c->state, c->capture})
+    if (n > max_elems) return false;
+  return true;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, uint64_t elems) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)(elems * sizeof(float))};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void *p, uintptr_t n) {
+  return (reinterpret_cast<uintptr_t>(p) % n) == 0;
+}
+
+gdn_status forward(const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, const float *state_in,
+                   float *output, float *state_out, float *capture,
+                   const gdn_params *p, void *stream) {
+  gdn_status st = gdn_check_params(p);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !g || !beta || !state_in || !output || !state_out)
+    return GDN_ERR_NULL_POINTER;
+
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state_in, 16) ||
+      !aligned(state_out, 16) || (capture && !aligned(capture, 16)) ||
+      !aligned(v, 4) || !aligned(g, 4) || !aligned(beta, 4) ||
+      !aligned(output, 4))
+    return GDN_ERR_MISALIGNED;
+
+  Counts c;
+  counts_of(p, &c);  // cannot fail after gdn_check_params
+  const Range inputs[] = {range_of(q, c.qk),        range_of(k, c.qk),
+                          range_of(v, c.v),         range_of(g, c.scalar),
+                          range_of(beta, c.scalar), range_of(state_in, c.state)};
+  const Range r_out = range_of(output, c.v);
+  const Range r_state = range_of(state_out, c.state);
+  const Range r_cap = range_of(capture, capture ? c.capture : 0);
+  for (int i = 0; i < 6; ++i) {
+    const bool in_place = (i == 5) && state_out == state_in;
+    if (overlap(r_out, inputs[i]) || (!in_place && overlap(r_state, inputs[i])) ||
+        (capture && overlap(r_cap, inputs[i])))
+      return GDN_ERR_ALIASING;
+  }
+  if (overlap(r_out, r_state) ||
+      (capture && (overlap(r_cap, r_out) || overlap(r_cap, r_state))))
+    return GDN_ERR_ALIASING;
+
+  float q_scale = 1.0f;  // params[8] == 0: q pre-scaled (mlx-native 0.21.1 doc)
+  if (p->q_scale_bits != 0u) memcpy(&q_scale, &p->q_scale_bits, sizeof q_scale);
+
+  gdn::ForwardArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.state_in = state_in;
+  a.output = output;
+  a.state_out = state_out;
+  a.capture = capture;
+  a.d_k = p->d_k;
+  a.d_v = p->d_v;
+  a.n_k_heads = p->n_k_heads;
+  a.n_v_heads = p->n_v_heads;
+  a.n_tokens = p->n_tokens;
+  a.n_seqs = p->n_seqs;
+  a.q_scale = q_scale;
+  if (gdn::enqueue_forward(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GDN_ERR_LAUNCH;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_check_params(const gdn_params *p) {
+  if (p == nullptr) return GDN_ERR_NULL_POINTER;
+  if (p->d_k == 0 || p->d_v == 0 || p->n_k_heads == 0 || p->n_v_heads == 0)
+    return GDN_ERR_ZERO_DIM;
+  if (p->n_tokens == 0 || p->n_seqs == 0) return GDN_ERR_ZERO_EXTENT;
+  if (p->n_v_heads % p->n_k_heads != 0) return GDN_ERR_GQA_RATIO;
+  if (p->d_k != 32 && p->d_k != 64 && p->d_k != 128)
+    return GDN_ERR_UNSUPPORTED_DK;
+  if (p->reserved6 != 0 || p->reserved7 != 0) return GDN_ERR_RESERVED_NONZERO;
+  Counts c;
+  if (!counts_of(p, &c)) return GDN_ERR_SIZE_OVERFLOW;
+  // The kernels address a head's state with 32-bit element offsets.
+  if ((uint64_t)p->d_v * p->d_k > (uint64_t(1) << 31)) return GDN_ERR_SIZE_OVERFLOW;
+  // One-dimensional grid: blocks * threads (at most 256 per block) must stay
+  // below 2^32 work-items, for either geometry, with or without capture.
+  for (bool cap : {false, true}) {
+    const uint64_t blocks = gdn::grid_blocks(p->d_k, p->d_v, p->n_v_heads,
+                                             p->n_seqs, p->n_tokens, cap);
+    if (blocks >= (uint64_t(1) << 32) / 256u) return GDN_ERR_SIZE_OVERFLOW;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_forward(const float *q, const float *k, const float *v,
+                       const float *g, const float *beta,
+                       const float *state_in, float *output, float *state_out,
+                       const gdn_params *p, void *stream) {
+  return forward(q, k, v, g, beta, state_in, output, state_out, nullptr, p,
+                 stream);
+}
+
+gdn_status gdn_forward_capture(const float *q, const float *k, const float *v,
+                               const float *g, const float *beta,
+                               const float *state_in, float *output,
+                               float *state_out, float *state_capture,
+                               const gdn_params *p, void *stream) {
+  return forward(q, k, v, g, beta, state_in, output, state_out, state_capture,
+                 p, stream);
+}
+
+const char *gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "success";
+    case GDN_ERR_NULL_POINTER: return "params or a required array pointer is NULL";
+    case GDN_ERR_ZERO_DIM: return "dims must all be > 0 (d_k, d_v, n_k_heads, n_v_heads)";
+    case GDN_ERR_ZERO_EXTENT: return "n_tokens and n_seqs must be > 0";
+    case GDN_ERR_GQA_RATIO: return "n_v_heads must be a multiple of n_k_heads";
+    case GDN_ERR_UNSUPPORTED_DK: return "d_k must be 32, 64 or 128";
+    case GDN_ERR_RESERVED_NONZERO: return "params words 6 and 7 are reserved and must be 0";
+    case GDN_ERR_SIZE_OVERFLOW: return "array sizes or launch grid exceed 64-bit/32-bit limits";
+    case GDN_ERR_MISALIGNED: return "q, k, state and capture arrays need 16-byte alignment; v, g, beta, output 4-byte";
+    case GDN_ERR_ALIASING: return "an output array overlaps another array (only state_out == state_in is allowed)";
+    case GDN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+  }
+  return "unknown gdn_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,344 @@
+// Gated DeltaNet recurrent forward step: gfx950 (CDNA4, wave64) kernels.
+//
+// The recurrence (mlx-native 0.9.2, gated_delta_net_decode_capture.metal,
+// token loop of gated_delta_net_decode_capture_impl): per (sequence, value
+// head, value channel i) the D_k state cells of row i are decayed by
+// alpha = exp(-g), read out against k (sk), corrected by
+// delta = (v_i - sk) * beta along k, and read out against q (y_i).
+//
+// Mapping to the hardware.
+//   * A state row (D_k contiguous f32) is owned by L = D_k / C lanes of one
+//     wavefront; each lane keeps its C cells in VGPRs for the whole token loop,
+//     so state is read from HBM once and written once per call, whatever the
+//     number of tokens (the "Threading" note of mlx-native 0.4.0
+//     src/ops/gated_delta_net.rs makes the same point for its thread-per-row
+//     design).
+//   * The lane's cells are C/4 float4 vectors at columns m*4L + 4*sub (sub =
+//     lane index within its row group). For every vector index m the L lanes of
+//     a row touch 4L consecutive floats, so each load/store instruction of a
+//     wave covers whole 128-byte lines: fully coalesced dwordx4 traffic.
+//   * sk and y are sums over the L lanes of a row: butterfly DPP adds
+//     (quad_perm, row_half_mirror, row_mirror) and one ds_swizzle for L = 32.
+//     No LDS traffic, no barriers. Each butterfly step adds a value to its
+//     partner's, so every lane of the row ends with the same bits.
+//   * A workgroup covers rows of one (sequence, value head), so g and beta are
+//     uniform: 64 tokens' worth of alpha = exp(-g) and beta are computed once
+//     per wave (lane t holds token t0+t) and read per token with v_readlane.
+//   * Token t+1's k, q and v are loaded while token t computes (two register
+//     sets used alternately).
+// Two launch geometries instantiate the same template: a short-run one for a
+// single decode token (HBM-bound on the state read and write; small C, many
+// waves in flight) and a long-run one for multi-token calls (VALU-bound; larger
+// C so the per-token reductions are a small share of the work).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// DPP_CTRL encodings (AMD CDNA3/CDNA4 ISA, "DPP" modifier).
+constexpr int kDppXor1 = 0xB1;        // quad_perm:[1,0,3,2]  lane ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm:[2,3,0,1]  lane ^ 2
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane -> 7 - lane (per 8)
+constexpr int kDppMirror = 0x140;     // row_mirror: lane -> 15 - lane (per 16)
+// ds_swizzle bit mode (offset bit 15 = 0): and_mask 0x1f, or_mask 0,
+// xor_mask 0x10 -> lane ^ 16 within each group of 32.
+constexpr int kSwizzleXor16 = 0x1F | (0x10 << 10);
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                         0xF, 0xF, false));
+}
+
+// Sum over the L consecutive lanes of a row group (L a power of two, 2..32).
+// The result is bit-identical in all L lanes.
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(L == 2 || L == 4 || L == 8 || L == 16 || L == 32,
+                "row groups of 2..32 lanes");
+  x += dpp<kDppXor1>(x);
+  if constexpr (L >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (L >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (L >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (L >= 32)
+    x += __builtin_bit_cast(
+        float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
+                                           kSwizzleXor16));
+  return x;
+}
+
+__device__ __forceinline__ float read_lane(float x, uint32_t lane) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+__device__ __forceinline__ f4 load4(const float *p) {
+  return *reinterpret_cast<const f4 *>(p);
+}
+
+__device__ __forceinline__ void store4_stream(float *p, f4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f4 *>(p));
+}
+
+struct KernelArgs {
+  const float *q, *k, *v, *g, *beta, *state_in;
+  float *output, *state_out, *capture;
+  uint32_t d_v, n_k_heads, n_v_heads, n_tokens;
+  uint32_t row_blocks;  // workgroups per (sequence, value head)
+  float q_scale;
+};
+
+// DK: key dim. C: cells per lane per row. R: rows per lane. WAVES: waves per
+// workgroup. CAPTURE: also write the per-token state.
+template <int DK, int C, int R, int WAVES, bool CAPTURE>
+__global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
+  constexpr int L = DK / C;      // lanes sharing one state row
+  constexpr int G = 64 / L;      // row groups per wave
+  constexpr int NV = C / 4;      // float4 vectors per lane per row
+  constexpr int ROWS_PER_WAVE = G * R;
+  constexpr int ROWS = WAVES * ROWS_PER_WAVE;
+  static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
+
+  // Workgroup -> (sequence s, value head vh, block of rows); all uniform.
+  const uint32_t bid = blockIdx.x;
+  const uint32_t rb = bid % a.row_blocks;
+  const uint32_t hs = bid / a.row_blocks;  // s * n_v_heads + vh
+  const uint32_t vh = hs % a.n_v_heads;
+  const uint32_t s = hs / a.n_v_heads;
+  const uint32_t kh = vh % a.n_k_heads;  // GQA map of the capture kernel
+
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t grp = lane / L;
+  const uint32_t sub = lane % L;
+
+  const uint32_t Dv = a.d_v;
+  const uint32_t T = a.n_tokens;
+  const uint64_t Hv = a.n_v_heads, Hk = a.n_k_heads;
+
+  // This lane's rows. Rows past D_v compute on a clamped (valid) row and
+  // store nothing; all lanes stay active for the cross-lane sums.
+  uint32_t row[R];
+  bool ok[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t i = rb * ROWS + wave * ROWS_PER_WAVE + r * G + grp;
+    ok[r] = i < Dv;
+    row[r] = ok[r] ? i : Dv - 1;
+  }
+
+  // Addressing: every array is reached through a wave-uniform base pointer
+  // (scalar registers; advanced per token by a uniform stride) plus a
+  // per-lane 32-bit element offset that stays fixed for the whole loop. The
+  // host guarantees d_v * d_k <= 2^31, so these offsets cannot wrap.
+  const uint64_t tok0 = (uint64_t)s * T;                   // first token of s
+  const float *k_tok = a.k + (tok0 * Hk + kh) * DK;        // token 0
+  const float *q_tok = a.q + (tok0 * Hk + kh) * DK;
+  const uint64_t kq_step = Hk * DK;                        // per token
+  const float *v_tok = a.v + (tok0 * Hv + vh) * Dv;
+  float *o_tok = a.output + (tok0 * Hv + vh) * Dv;
+  const uint64_t v_step = Hv * Dv;
+  const float *g_tok = a.g + tok0 * Hv + vh;
+  const float *b_tok = a.beta + tok0 * Hv + vh;
+  float *c_tok = CAPTURE ? a.capture + (tok0 * Hv + vh) * (uint64_t)Dv * DK : nullptr;
+  const uint64_t cap_step = Hv * Dv * DK;
+  const float *s_in = a.state_in + (uint64_t)hs * Dv * DK;
+  float *s_out = a.state_out + (uint64_t)hs * Dv * DK;
+
+  // Per-lane offsets: column of vector m is m*4L + 4*sub.
+  const uint32_t col = 4 * sub;
+  uint32_t cell[R];  // element offset of this lane's first cell in its row
+#pragma unroll
+  for (int r = 0; r < R; ++r) cell[r] = row[r] * DK + col;
+
+  f4 st[R][NV];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NV; ++m) st[r][m] = load4(s_in + cell[r] + m * 4 * L);
+
+  struct Tok {
+    f4 k[NV], q[NV];
+    float v[R];
+  };
+  auto load_token = [&](uint32_t t, Tok &x) {
+    const float *kt = k_tok + t * kq_step;
+    const float *qt = q_tok + t * kq_step;
+    const float *vt = v_tok + t * v_step;
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      x.k[m] = load4(kt + col + m * 4 * L);
+      x.q[m] = load4(qt + col + m * 4 * L);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) x.v[r] = vt[row[r]];
+  };
+
+  // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
+  // t0 + j (clamped to the last token; lanes past the end are never read).
+  auto load_chunk = [&](uint32_t t0, float &gr, float &br) {
+    const uint32_t t = lane < T - t0 ? t0 + lane : T - 1;
+    gr = g_tok[(uint64_t)t * Hv];
+    br = b_tok[(uint64_t)t * Hv];
+  };
+
+  auto step = [&](uint32_t t, const Tok &x, float alpha, float b) {
+    float d[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          st[r][m][e] *= alpha;                          // decay first
+          part = __builtin_fmaf(st[r][m][e], x.k[m][e], part);
+        }
+      const float sk = group_sum<L>(part);
+      d[r] = (x.v[r] - sk) * b;
+    }
+    float *ot = o_tok + t * v_step;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          st[r][m][e] = __builtin_fmaf(d[r], x.k[m][e], st[r][m][e]);
+          part = __builtin_fmaf(st[r][m][e], x.q[m][e], part);
+        }
+      const float y = group_sum<L>(part);
+      if (ok[r] && sub == 0) ot[row[r]] = y * a.q_scale;
+    }
+    if constexpr (CAPTURE) {
+      float *ct = c_tok + t * cap_step;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (ok[r])
+#pragma unroll
+          for (int m = 0; m < NV; ++m)
+            store4_stream(ct + cell[r] + m * 4 * L, st[r][m]);
+    }
+  };
+
+  float g_raw, b_raw, alphas = 0.f, betas = 0.f;
+  load_chunk(0, g_raw, b_raw);
+  Tok A, B;
+  load_token(0, A);
+  auto next_chunk = [&](uint32_t t) {
+    if ((t & 63u) == 0) {
+      alphas = expf(-g_raw);
+      betas = b_raw;
+      if (T - t > 64) load_chunk(t + 64, g_raw, b_raw);
+    }
+  };
+  // The prefetch is unconditional (the last token is loaded twice at the
+  // end): a skipped prefetch on some paths would make the compiler's memory
+  // counter bookkeeping wait for every outstanding load, prefetch included.
+  for (uint32_t t = 0;;) {
+    next_chunk(t);
+    load_token(t + 1 < T ? t + 1 : t, B);
+    step(t, A, read_lane(alphas, t & 63u), read_lane(betas, t & 63u));
+    if (++t == T) break;
+    next_chunk(t);
+    load_token(t + 1 < T ? t + 1 : t, A);
+    step(t, B, read_lane(alphas, t & 63u), read_lane(betas, t & 63u));
+    if (++t == T) break;
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (ok[r])
+#pragma unroll
+      for (int m = 0; m < NV; ++m) store4_stream(s_out + cell[r] + m * 4 * L, st[r][m]);
+}
+
+// ---------------------------------------------------------------- geometry
+
+struct Geometry {
+  int rows_per_block;  // WAVES * (64 / L) * R
+  int threads;
+  const void *kernel;
+};
+
+template <int DK, int C, int R, int WAVES, bool CAPTURE>
+constexpr Geometry make_geometry() {
+  return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
+                  reinterpret_cast<const void *>(
+                      &gdn_recurrent<DK, C, R, WAVES, CAPTURE>)};
+}
+
+// Calls with at most this many tokens use the short-run geometry.
+constexpr uint32_t kShortRunTokens = 1;
+
+template <bool CAPTURE>
+Geometry pick(uint32_t d_k, uint32_t n_tokens) {
+  const bool short_run = n_tokens <= kShortRunTokens;
+  switch (d_k) {
+    case 32:
+      return short_run ? make_geometry<32, 4, 1, 2, CAPTURE>()
+                       : make_geometry<32, 4, 1, 4, CAPTURE>();
+    case 64:
+      return short_run ? make_geometry<64, 4, 1, 2, CAPTURE>()
+                       : make_geometry<64, 8, 1, 4, CAPTURE>();
+    case 128:
+      return short_run ? make_geometry<128, 8, 1, 2, CAPTURE>()
+                       : make_geometry<128, 16, 1, 4, CAPTURE>();
+    default:
+      return Geometry{0, 0, nullptr};
+  }
+}
+
+Geometry pick_geometry(uint32_t d_k, uint32_t n_tokens, bool capture) {
+  return capture ? pick<true>(d_k, n_tokens) : pick<false>(d_k, n_tokens);
+}
+
+}  // namespace
+
+uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
+                     uint32_t n_seqs, uint32_t n_tokens, bool capture) {
+  const Geometry geo = pick_geometry(d_k, n_tokens, capture);
+  if (geo.kernel == nullptr) return 0;
+  const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
+  return row_blocks * n_v_heads * n_seqs;
+}
+
+hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
+  const bool capture = f.capture != nullptr;
+  const Geometry geo = pick_geometry(f.d_k, f.n_tokens, capture);
+  if (geo.kernel == nullptr) return hipErrorInvalidValue;
+  const uint32_t row_blocks =
+      (f.d_v + geo.rows_per_block - 1) / geo.rows_per_block;
+  const uint64_t blocks = (uint64_t)row_blocks * f.n_v_heads * f.n_seqs;
+
+  KernelArgs a;
+  a.q = f.q;
+  a.k = f.k;
+  a.v = f.v;
+  a.g = f.g;
+  a.beta = f.beta;
+  a.state_in = f.state_in;
+  a.output = f.output;
+  a.state_out = f.state_out;
+  a.capture = f.capture;
+  a.d_v = f.d_v;
+  a.n_k_heads = f.n_k_heads;
+  a.n_v_heads = f.n_v_heads;
+  a.n_tokens = f.n_tokens;
+  a.row_blocks = row_blocks;
+  a.q_scale = f.q_scale;
+
+  void *args[] = {&a};
+  return hipLaunchKernel(geo.kernel, dim3((uint32_t)blocks), dim3(geo.threads),
+                         args, 0, stream);
+}
+
+}  // namespace gdn

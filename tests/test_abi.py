@@ -1,0 +1,185 @@
+"""The C ABI on the host: the library loads, exports what include/gdn.h declares,
+and validates arguments (no GPU needed; no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_recurrence_forward_amd as gdn
+from linear_attention_recurrence_forward_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.LIBRARY):
+        from linear_attention_recurrence_forward_amd import build
+        build.build()
+    return _binding._load()
+
+
+def header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(_binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIBRARY],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in gdn.h but not exported"
+        assert getattr(lib, name) is not None
+
+
+def test_status_enum_matches_header():
+    text = header_text()
+    for code, name in _binding.STATUS.items():
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == code, name
+
+
+def test_params_struct_is_nine_words():
+    assert ctypes.sizeof(_binding.GdnParams) == 36
+    assert [f[0] for f in _binding.GdnParams._fields_][-1] == "q_scale_bits"
+
+
+def test_status_strings(lib):
+    for code in _binding.STATUS:
+        s = gdn.gdn_status_string(code)
+        assert s and s != "unknown gdn_status"
+    assert gdn.gdn_status_string(999) == "unknown gdn_status"
+
+
+OK = dict(d_k=128, d_v=128, n_k_heads=16, n_v_heads=48, n_tokens=1, n_seqs=1)
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, "GDN_OK"),
+    ({"d_k": 0}, "GDN_ERR_ZERO_DIM"),
+    ({"d_v": 0}, "GDN_ERR_ZERO_DIM"),
+    ({"n_k_heads": 0}, "GDN_ERR_ZERO_DIM"),
+    ({"n_v_heads": 0}, "GDN_ERR_ZERO_DIM"),
+    ({"n_tokens": 0}, "GDN_ERR_ZERO_EXTENT"),
+    ({"n_seqs": 0}, "GDN_ERR_ZERO_EXTENT"),
+    ({"n_v_heads": 40}, "GDN_ERR_GQA_RATIO"),
+    ({"d_k": 96}, "GDN_ERR_UNSUPPORTED_DK"),
+    ({"d_k": 16}, "GDN_ERR_UNSUPPORTED_DK"),
+    ({"d_k": 256}, "GDN_ERR_UNSUPPORTED_DK"),
+    ({"d_k": 33}, "GDN_ERR_UNSUPPORTED_DK"),
+    ({"reserved6": 1}, "GDN_ERR_RESERVED_NONZERO"),
+    ({"reserved7": 7}, "GDN_ERR_RESERVED_NONZERO"),
+    ({"n_seqs": 2**32 - 1, "n_tokens": 2**32 - 1}, "GDN_ERR_SIZE_OVERFLOW"),
+    ({"d_v": 2**24 + 1}, "GDN_ERR_SIZE_OVERFLOW"),
+    ({"n_v_heads": 2**20, "n_k_heads": 1, "n_seqs": 2**12}, "GDN_ERR_SIZE_OVERFLOW"),
+    ({"d_k": 32, "d_v": 1, "n_k_heads": 1, "n_v_heads": 1}, "GDN_OK"),
+    ({"d_k": 64, "d_v": 1000, "n_tokens": 4096, "n_seqs": 3}, "GDN_OK"),
+    ({"q_scale_bits": 0xFFFFFFFF}, "GDN_OK"),
+])
+def test_check_params(lib, change, status):
+    p = gdn.make_params(**{**OK, **change})
+    assert _binding.STATUS[gdn.gdn_check_params(p)] == status
+
+
+def test_null_params(lib):
+    assert _binding.STATUS[lib.gdn_check_params(None)] == "GDN_ERR_NULL_POINTER"
+
+
+# Fake, never dereferenced device addresses: every case below fails validation
+# before the library touches the runtime.
+def fake(addr):
+    return ctypes.cast(ctypes.c_void_p(addr), ctypes.POINTER(ctypes.c_float))
+
+
+def layout(p, base=1 << 40, gap=1 << 30, **overrides):
+    """Non-overlapping aligned fake addresses for every array."""
+    names = ["q", "k", "v", "g", "beta", "state_in", "output", "state_out", "state_capture"]
+    addrs = {n: base + i * gap for i, n in enumerate(names)}
+    addrs.update(overrides)
+    return addrs
+
+
+def call(lib, p, addrs, capture=True, null=()):
+    order = ["q", "k", "v", "g", "beta", "state_in", "output", "state_out"]
+    ptrs = [None if n in null else fake(addrs[n]) for n in order]
+    if capture:
+        cap = None if "state_capture" in null else fake(addrs["state_capture"])
+        st = lib.gdn_forward_capture(*ptrs, cap, ctypes.byref(p), None)
+    else:
+        st = lib.gdn_forward(*ptrs, ctypes.byref(p), None)
+    return _binding.STATUS[st]
+
+
+def test_forward_rejects_bad_params_first(lib):
+    p = gdn.make_params(**{**OK, "n_tokens": 0})
+    assert call(lib, p, layout(p), null=("q",)) == "GDN_ERR_ZERO_EXTENT"
+    assert call(lib, p, layout(p), capture=False) == "GDN_ERR_ZERO_EXTENT"
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "state_in", "output",
+                                  "state_out"])
+def test_forward_null_pointer(lib, name):
+    p = gdn.make_params(**OK)
+    assert call(lib, p, layout(p), null=(name,)) == "GDN_ERR_NULL_POINTER"
+    assert call(lib, p, layout(p), capture=False, null=(name,)) == "GDN_ERR_NULL_POINTER"
+
+
+@pytest.mark.parametrize("name,offset", [
+    ("q", 4), ("k", 8), ("state_in", 12), ("state_out", 4), ("state_capture", 8),
+    ("v", 2), ("g", 1), ("beta", 3), ("output", 2),
+])
+def test_forward_misaligned(lib, name, offset):
+    p = gdn.make_params(**OK)
+    a = layout(p)
+    a[name] += offset
+    assert call(lib, p, a) == "GDN_ERR_MISALIGNED"
+
+
+def test_forward_aliasing(lib):
+    p = gdn.make_params(**{**OK, "n_tokens": 4})
+    c = p.counts()
+    a = layout(p)
+    # output overlapping the tail of v
+    b = dict(a, output=a["v"] + 4 * (c["v"] - 4))
+    assert call(lib, p, b) == "GDN_ERR_ALIASING"
+    # state_out shifted into state_in (partial overlap) is refused ...
+    b = dict(a, state_out=a["state_in"] + 16)
+    assert call(lib, p, b) == "GDN_ERR_ALIASING"
+    # capture overlapping state_out
+    b = dict(a, state_capture=a["state_out"] + 4 * c["state_out"] - 16)
+    assert call(lib, p, b) == "GDN_ERR_ALIASING"
+    # output overlapping q
+    b = dict(a, output=a["q"])
+    assert call(lib, p, b) == "GDN_ERR_ALIASING"
+    # capture overlapping k
+    b = dict(a, state_capture=a["k"] + 1024)
+    assert call(lib, p, b) == "GDN_ERR_ALIASING"
+
+
+def test_binding_checks_tensors_before_the_library():
+    torch = pytest.importorskip("torch")
+    p = gdn.make_params(32, 32, 1, 2, 8, 1)
+    c = p.counts()
+    cpu = {n: torch.zeros(c[n]) for n in ("q", "k", "v", "g", "beta", "state_in",
+                                          "output", "state_out")}
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        gdn.gdn_forward(**cpu, params=p)
+    bad = dict(cpu, q=torch.zeros(c["q"], dtype=torch.float64))
+    with pytest.raises(ValueError, match="must be f32"):
+        gdn.gdn_forward(**bad, params=p)
+    with pytest.raises(gdn.GdnError, match="GDN_ERR_ZERO_EXTENT"):
+        gdn.gdn_forward(**cpu, params=gdn.make_params(32, 32, 1, 2, 0, 1))

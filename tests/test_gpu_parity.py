@@ -1,0 +1,377 @@
+"""HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Tolerance (floating point, reduction order and fused multiply-adds only):
+|gpu - oracle| <= 1e-5 + 1e-4 * |oracle| elementwise, on output, state_out and
+state_capture. Cases whose arithmetic is exact (integer or dyadic values, or a
+relation the kernel keeps by construction) are compared for equality.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_recurrence_forward_amd.workloads import (
+    WORKLOADS, Workload, f32_bits, make_inputs, q_scale_bits_for)
+
+from pins import HEAD_MAP_MOD, assert_equal, assert_within, gather_k, kmap
+
+torch = pytest.importorskip("torch")
+gdn = pytest.importorskip("linear_attention_recurrence_forward_amd")
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL = 1e-4, 1e-5
+NAMES = ("q", "k", "v", "g", "beta", "state_in")
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return {n: torch.from_numpy(np.ascontiguousarray(x[n])).cuda() for n in NAMES}
+
+
+def run(x, *, q_scale_bits=None, capture=False, in_place=False, stream=None):
+    """Run the HIP path on numpy inputs; returns numpy results."""
+    bits = x.get("q_scale_bits", 0) if q_scale_bits is None else q_scale_bits
+    d = dev(x)
+    kw = dict(q_scale_bits=bits, capture=capture, stream=stream)
+    if in_place:
+        kw["state_out"] = d["state_in"]
+    res = gdn.forward(*(d[n] for n in NAMES), **kw)
+    if stream is not None:
+        stream.synchronize()
+    torch.cuda.synchronize()
+    return tuple(r.cpu().numpy() for r in res)
+
+
+def ref(x, *, q_scale_bits=None, capture=False, precision="f32"):
+    bits = x.get("q_scale_bits", 0) if q_scale_bits is None else q_scale_bits
+    return oracle.reference(**{n: x[n] for n in NAMES}, q_scale_bits=bits,
+                            capture=capture, precision=precision)
+
+
+def close(gpu, expected, what):
+    assert_within(gpu, expected, ATOL + RTOL * np.abs(np.asarray(expected, np.float64)),
+                  what)
+
+
+def max_rel(a, e):
+    e = np.asarray(e, np.float64)
+    return float(np.max(np.abs(a - e) / (ATOL / RTOL + np.abs(e))))
+
+
+# ------------------------------------------------------------------ native
+
+def test_native_library_is_loaded():
+    x = make_inputs(WORKLOADS["tiny"])
+    run(x)
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert gdn.library_path() in maps, "libgdn.so not mapped"
+    hip = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(hip) == 1, f"expected one HIP runtime, found {sorted(hip)}"
+
+
+# ------------------------------------------------------------------ workloads
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    """Every benchmark workload at full size, every output element."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    got = run(x, capture=w.capture)
+    exp = ref(x, capture=w.capture)
+    shadow = ref(x, capture=w.capture, precision="f64")
+    for g_, e, s, what in zip(got, exp, shadow, ("output", "state_out", "capture")):
+        close(g_, e, f"{name} {what} vs oracle")
+        close(g_, s, f"{name} {what} vs f64 shadow")
+        sys.__stderr__.write(f"  {name} {what}: max scaled err vs oracle "
+                             f"{max_rel(g_, e):.2e}, vs f64 {max_rel(g_, s):.2e}\n")
+    if w.capture:
+        assert_equal(got[2][:, -1], got[1], f"{name} capture[T-1] == state_out")
+
+
+@pytest.mark.parametrize("name", ["decode", "batched_decode", "prefill"])
+def test_workload_in_place(name):
+    """The benchmark updates the state in place (state_out == state_in)."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    a = run(x)
+    b = run(x, in_place=True)
+    for u, v, what in zip(a, b, ("output", "state_out")):
+        assert_equal(v, u, f"{name} in-place {what} == out-of-place")
+
+
+# ------------------------------------------------------------------ shapes
+
+SHAPES = [
+    # d_k, d_v, n_k, n_v, T, S
+    (32, 32, 1, 2, 1, 1),
+    (32, 1, 1, 1, 1, 1),
+    (32, 5, 2, 4, 3, 2),
+    (32, 37, 1, 3, 65, 1),
+    (64, 64, 2, 6, 1, 3),
+    (64, 100, 4, 8, 7, 2),
+    (64, 33, 1, 1, 64, 1),
+    (128, 128, 4, 12, 2, 2),
+    (128, 200, 2, 2, 1, 5),
+    (128, 17, 3, 3, 130, 1),
+    (128, 128, 16, 48, 1, 2),
+    (128, 256, 1, 2, 129, 1),
+]
+
+
+@pytest.mark.parametrize("capture", [False, True], ids=["plain", "capture"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
+def test_shapes(shape, capture):
+    """Ragged D_v (rows past the last full workgroup), token counts around the
+    64-token chunk and the two-token unroll, GQA ratios 1..4, all D_k."""
+    dk, dv, hk, hv, t, s = shape
+    w = Workload("shape", 0, dk, dv, hk, hv, t, s)
+    for bits in (0, q_scale_bits_for(dk)):
+        x = make_inputs(w, seed=hash(shape) % 1000 + bits % 7)
+        got = run(x, q_scale_bits=bits, capture=capture)
+        exp = ref(x, q_scale_bits=bits, capture=capture)
+        for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
+            close(g_, e, f"{shape} bits={bits:#x} {what}")
+        if capture:
+            assert_equal(got[2][:, -1], got[1], "capture[T-1] == state_out")
+
+
+def test_long_run_drift():
+    """A long run (T = 2048) stays within tolerance of the oracle and the f64
+    shadow: no drift from the exp or the reduction order."""
+    w = Workload("long", 0, 128, 128, 2, 4, 2048, 1, fold_q_scale=True, g_high=0.5)
+    x = make_inputs(w, seed=5)
+    got = run(x)
+    for e, what in ((ref(x), "oracle"), (ref(x, precision="f64"), "f64 shadow")):
+        close(got[0], e[0], f"long-run output vs {what}")
+        close(got[1], e[1], f"long-run state vs {what}")
+
+
+# ------------------------------------------------------------------ pins on the GPU
+
+def test_head_map_probe_bit_exact():
+    """P7 on the GPU: each value head reads key/query head vh % n_k_heads."""
+    S, T, Hk, Hv, Dk, Dv = 2, 1, 4, 12, 32, 8
+    rng = np.random.default_rng(7)
+    k = np.zeros((S, T, Hk, Dk), np.float32)
+    q = np.zeros((S, T, Hk, Dk), np.float32)
+    for kh in range(Hk):
+        k[:, :, kh, kh] = 1.0
+        q[:, :, kh, :] = kh + 1
+    v = rng.integers(-8, 9, size=(S, T, Hv, Dv)).astype(np.float32)
+    z = np.zeros((S, T, Hv), np.float32)
+    x = dict(q=q, k=k, v=v, g=z, beta=z + 1, state_in=np.zeros((S, Hv, Dv, Dk), np.float32))
+    for dk_ in (32, 64, 128):  # same probe at every supported D_k
+        xx = dict(x)
+        if dk_ != Dk:
+            pad = dk_ - Dk
+            xx["k"] = np.pad(k, ((0, 0), (0, 0), (0, 0), (0, pad)))
+            xx["q"] = np.pad(q, ((0, 0), (0, 0), (0, 0), (0, pad)))
+            xx["state_in"] = np.zeros((S, Hv, Dv, dk_), np.float32)
+        out, st = run(xx)
+        kh = np.array([kmap(vh, Hk, Hv, HEAD_MAP_MOD) for vh in range(Hv)])
+        assert_equal(out, v * (kh + 1)[None, None, :, None], f"P7 output d_k={dk_}")
+        e_out, e_st = ref(xx)
+        assert_equal(out, e_out, f"P7 output == oracle d_k={dk_}")
+        assert_equal(st, e_st, f"P7 state == oracle d_k={dk_}")
+
+
+def test_linear_attention_bit_exact():
+    """P8 on the GPU: orthogonal unit keys, small integers, every sum exact."""
+    S, T, Hk, Hv, Dk, Dv = 2, 40, 2, 4, 64, 8
+    rng = np.random.default_rng(8)
+    k = np.zeros((S, T, Hk, Dk), np.float32)
+    for t in range(T):
+        k[:, t, :, t] = 1.0
+    q = rng.integers(-4, 5, size=(S, T, Hk, Dk)).astype(np.float32)
+    v = rng.integers(-4, 5, size=(S, T, Hv, Dv)).astype(np.float32)
+    z = np.zeros((S, T, Hv), np.float32)
+    x = dict(q=q, k=k, v=v, g=z, beta=z + 1, state_in=np.zeros((S, Hv, Dv, Dk), np.float32))
+    out, st, cap = run(x, capture=True)
+    e = ref(x, capture=True)
+    for g_, e_, what in zip((out, st, cap), e, ("output", "state", "capture")):
+        assert_equal(g_, e_, f"P8 {what}")
+
+
+def test_identity_and_zeroing():
+    """P1 and P2 on the GPU: beta = 0, g = 0 keeps the state bit for bit;
+    g = +inf, beta = 0 zeroes state and output."""
+    w = Workload("pin", 0, 128, 48, 2, 6, 3, 2)
+    x = make_inputs(w, seed=11)
+    x["g"][:] = 0.0
+    x["beta"][:] = 0.0
+    out, st = run(x)
+    assert_equal(st, x["state_in"], "P1 state unchanged")
+    close(out, ref(x)[0], "P1 output")
+    x["g"][:] = np.inf
+    out, st = run(x)
+    assert_equal(st, np.zeros_like(st), "P2 state zero")
+    assert_equal(out, np.zeros_like(out), "P2 output zero")
+    # alpha = 0 on the last token only: state = fl(fl(v*beta)*k), exactly.
+    x = make_inputs(w, seed=12)
+    x["g"][:, -1, :] = np.inf
+    _, st = run(x)
+    k_last = gather_k(x["k"], 6, HEAD_MAP_MOD)[:, -1]
+    d = (x["v"][:, -1] * x["beta"][:, -1][..., None]).astype(np.float32)
+    assert_equal(st, (d[..., :, None] * k_last[..., None, :]).astype(np.float32),
+                 "P2 state after alpha = 0")
+
+
+def test_delta_rule_projection():
+    """P3 on the GPU: beta = 1 and unit keys give state'.k = v after every token."""
+    w = Workload("pin", 0, 128, 64, 2, 4, 6, 2, g_high=1.5)
+    x = make_inputs(w, seed=13)
+    x["beta"][:] = 1.0
+    _, _, cap = run(x, capture=True)
+    kv = gather_k(x["k"].astype(np.float64), 4, HEAD_MAP_MOD)
+    C = cap.astype(np.float64)
+    sk = np.einsum("sthij,sthj->sthi", C, kv)
+    mag = np.maximum(1.0, np.abs(C * kv[..., None, :]).sum(-1))
+    assert_within(sk, x["v"], 8 * 128 * 2.0 ** -24 * mag, "P3 state'.k == v")
+
+
+def test_chained_decode_matches_multi_token():
+    """P4 on the GPU: T one-token calls (decode geometry) against one T-token
+    call (multi-token geometry): equal within tolerance."""
+    w = Workload("chain", 0, 128, 128, 4, 8, 9, 2, fold_q_scale=True)
+    x = make_inputs(w, seed=14)
+    out, st = run(x)
+    state = x["state_in"]
+    outs = []
+    for t in range(w.n_tokens):
+        step = {n: x[n][:, t:t + 1] for n in ("q", "k", "v", "g", "beta")}
+        o1, state = run(dict(step, state_in=state, q_scale_bits=x["q_scale_bits"]))
+        outs.append(o1)
+    chained = np.concatenate(outs, axis=1)
+    close(chained, out, "P4 chained outputs")
+    close(state, st, "P4 chained final state")
+    sys.__stderr__.write(f"  chained == multi-token bit for bit: output "
+                         f"{np.array_equal(chained, out)}, state {np.array_equal(state, st)}\n")
+
+
+def test_capture_prefixes():
+    """P5 on the GPU: capture slice t equals the state of the same call cut to
+    t+1 tokens (bit for bit from two tokens on, where both calls use the same
+    geometry; within tolerance for the one-token call)."""
+    w = Workload("cap", 0, 64, 32, 2, 4, 5, 2)
+    x = make_inputs(w, seed=15)
+    out, st, cap = run(x, capture=True)
+    assert_equal(cap[:, -1], st, "capture[T-1] == state_out")
+    for t in range(w.n_tokens):
+        cut = {n: x[n][:, :t + 1] for n in ("q", "k", "v", "g", "beta")}
+        o_t, s_t = run(dict(cut, state_in=x["state_in"]))
+        if t >= 1:
+            assert_equal(cap[:, t], s_t, f"capture[{t}] == state after {t + 1} tokens")
+            assert_equal(o_t, out[:, :t + 1], f"outputs of the first {t + 1} tokens")
+        else:
+            close(cap[:, t], s_t, "capture[0] vs one-token call")
+    o2, s2 = run(x)
+    assert_equal(o2, out, "capture leaves the output unchanged")
+    assert_equal(s2, st, "capture leaves state_out unchanged")
+
+
+def test_q_scale_fold_in():
+    """P6 on the GPU: a power-of-two scale folded in equals pre-scaled q bit for
+    bit; the state never depends on q_scale; -0.0 bits give zero outputs."""
+    w = Workload("qs", 0, 128, 64, 2, 4, 4, 2)
+    x = make_inputs(w, seed=16)
+    base_out, base_st = run(x, q_scale_bits=0)
+    for c in (0.5, 0.125, 4.0):
+        o_f, s_f = run(x, q_scale_bits=f32_bits(c))
+        o_p, s_p = run(dict(x, q=(x["q"] * np.float32(c)).astype(np.float32)), q_scale_bits=0)
+        assert_equal(s_f, base_st, f"state independent of q_scale {c}")
+        assert_equal(s_p, base_st, f"state independent of pre-scaled q {c}")
+        assert_equal(o_f, o_p, f"fold-in == pre-scaled q ({c})")
+    o_n, _ = run(x, q_scale_bits=0x80000000)
+    assert_equal(o_n, np.zeros_like(o_n), "scale -0.0")
+    assert np.all(np.signbit(o_n) != np.signbit(base_out))
+
+
+def test_deterministic():
+    w = WORKLOADS["spec_verify"]
+    x = make_inputs(w)
+    a = run(x, capture=True)
+    b = run(x, capture=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
+
+
+# ------------------------------------------------------------------ plumbing
+
+def test_side_stream():
+    """The call runs on the stream it is given."""
+    w = Workload("stream", 0, 128, 128, 4, 8, 3, 2)
+    x = make_inputs(w, seed=17)
+    s = torch.cuda.Stream()
+    got = run(x, stream=s)
+    exp = ref(x)
+    close(got[0], exp[0], "side stream output")
+    close(got[1], exp[1], "side stream state")
+
+
+def test_graph_replay():
+    """Captured into a HIP graph and replayed several times (with eager work and
+    synchronisations between replays): every replay matches the eager call."""
+    w = WORKLOADS["decode"]
+    x = make_inputs(w)
+    d = dev(x)
+    out = torch.empty(x["v"].shape, device="cuda")
+    st = torch.empty(x["state_in"].shape, device="cuda")
+    eager_out, eager_st = (t.clone() for t in gdn.forward(*(d[n] for n in NAMES)))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            gdn.forward(*(d[n] for n in NAMES), output=out, state_out=st)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        out.fill_(float("nan"))
+        st.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {i} output"
+        assert torch.equal(st, eager_st), f"replay {i} state"
+        _ = (d["q"] * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_errors_on_device_tensors():
+    w = WORKLOADS["tiny"]
+    x = make_inputs(w)
+    d = dev(x)
+    p = gdn.params_for(d["q"], d["v"])
+    out = torch.empty(x["v"].shape, device="cuda")
+    st = torch.empty(x["state_in"].shape, device="cuda")
+    with pytest.raises(ValueError, match="element count"):
+        gdn.gdn_forward(d["q"], d["k"], d["v"][:, :4], d["g"], d["beta"], d["state_in"],
+                        out, st, p)
+    cap = torch.empty(10, device="cuda")
+    with pytest.raises(ValueError, match="state_capture element count"):
+        gdn.gdn_forward_capture(*(d[n] for n in NAMES), out, st, cap, p)
+    bad = gdn.make_params(p.d_k, p.d_v, p.n_k_heads, p.n_v_heads, p.n_tokens, p.n_seqs,
+                          reserved6=1)
+    with pytest.raises(gdn.GdnError, match="GDN_ERR_RESERVED_NONZERO"):
+        gdn.gdn_forward(*(d[n] for n in NAMES), out, st, bad)
+    with pytest.raises(gdn.GdnError, match="GDN_ERR_ALIASING"):  # output aliases v
+        gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                        d["v"], st, p)
+    # nothing was launched by the failed calls: outputs untouched
+    out.fill_(7.0)
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_forward(*(d[n] for n in NAMES), out, st, bad)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
