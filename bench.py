@@ -59,6 +59,11 @@ def parse_args(argv=None):
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference kernel for the HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR", default=None,
+                    help="write profiles/ summaries from rocprofv3 CSV output in DIR "
+                         "(kt_<workload>/, pmc_FETCH_SIZE_<workload>/, "
+                         "pmc_WRITE_SIZE_<workload>/ and the bench output of each run "
+                         "in <same name>.log) and exit")
     return ap.parse_args(argv)
 
 
@@ -78,6 +83,78 @@ def traffic_from_profiles(workload: str, digest: str):
     if rec.get("kernel_digest") != digest:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict) -> str:
+    """Summaries under profiles/ from rocprofv3 CSV output (see --summarize-rocprof):
+    the kernel-trace statistics of every kernel, and the HBM bytes per launch of
+    gdn_recurrent from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
+    counter reads for a plain device copy of calib_mib MiB."""
+    w = WORKLOADS[workload]
+    digests = set()
+    for log in (f"kt_{workload}.log", f"pmc_FETCH_SIZE_{workload}.log",
+                f"pmc_WRITE_SIZE_{workload}.log"):
+        with open(os.path.join(src, log)) as f:
+            for ln in f:
+                if ln.startswith("{"):
+                    digests.add(json.loads(ln)["kernel_digest"])
+    if len(digests) != 1:
+        raise SystemExit(f"{workload}: profiled runs disagree on the kernel build: {digests}")
+    digest = digests.pop()
+    stats = _csv(os.path.join(src, f"kt_{workload}", "run_kernel_stats.csv"))
+    lines = [f"# {KERNEL_NAME}: {w.description}", "",
+             f"kernel digest (sha256 of sources + flags) of the profiled build: `{digest}`", "",
+             "## rocprofv3 --kernel-trace --stats", "", "```", commands["kt"], "```", "",
+             "| kernel | calls | average µs | min µs | max µs | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    per = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = _csv(os.path.join(src, f"pmc_{ctr}_{workload}", "run_counter_collection.csv"))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        ours = [float(r["Counter_Value"]) for r in rows if KERNEL_NAME in r["Kernel_Name"]]
+        ref_kib = max(copies)  # the calibration copy is the largest copy
+        factor = (calib_mib * 1024.0) / ref_kib  # true KiB per counted KiB
+        per[ctr] = dict(mean_kib=sum(ours) / len(ours), dispatches=len(ours),
+                        copy_kib=ref_kib, factor=factor)
+    fetch = per["FETCH_SIZE"]["mean_kib"] * per["FETCH_SIZE"]["factor"] * 1024
+    write = per["WRITE_SIZE"]["mean_kib"] * per["WRITE_SIZE"]["factor"] * 1024
+    alg = w.algorithmic_bytes()
+    lines += ["", "## HBM bytes per launch (rocprofv3 --pmc, one counter per run)", "",
+              "```", commands["fetch"], commands["write"], "```", "",
+              f"The plain copy of {calib_mib} MiB (`__amd_rocclr_copyBuffer`) reads and "
+              f"writes {calib_mib} MiB; each counter is scaled by what it reads for that copy.",
+              "", "| counter | gdn_recurrent KiB/dispatch (raw) | copy KiB (raw) | scale | "
+              "bytes/launch |", "|---|---|---|---|---|"]
+    for ctr, b in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        d = per[ctr]
+        lines.append(f"| {ctr} | {d['mean_kib']:.1f} | {d['copy_kib']:.1f} | "
+                     f"{d['factor']:.4f} | {b:,.0f} |")
+    lines += ["", f"Total HBM traffic per launch: {fetch + write:,.0f} B; algorithmic: "
+              f"{alg:,} B (ratio {(fetch + write) / alg:.3f}).", ""]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    md = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines))
+    rec = dict(kernel=KERNEL_NAME, workload=workload, kernel_digest=digest,
+               hbm_bytes_per_launch=fetch + write, fetch_bytes=fetch, write_bytes=write,
+               algorithmic_bytes=alg, counters=per, calibration_copy_mib=calib_mib)
+    with open(os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_hbm_traffic.json"),
+              "w") as f:
+        json.dump(rec, f, indent=1)
+    return md
 
 
 def cpu_baseline(w, budget_s: float):
@@ -113,6 +190,18 @@ def cpu_baseline(w, budget_s: float):
 
 def main(argv=None):
     args = parse_args(argv)
+    if args.summarize_rocprof:
+        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt_{w} -o run "
+               "-- python3 bench.py --workload {w} --steps 200 --warmup 20 --no-cpu-baseline")
+        pmc = ("rocprofv3 --pmc {c} --output-format csv -d <dir>/pmc_{c}_{w} -o run -- "
+               "python3 bench.py --workload {w} --steps 10 --warmup 2 --layers 4 "
+               "--no-cpu-baseline --launch direct --calibrate-copy-mib 1024")
+        for wl in sorted(WORKLOADS):
+            if os.path.isdir(os.path.join(args.summarize_rocprof, f"kt_{wl}")):
+                print(summarize_rocprof(args.summarize_rocprof, wl, 1024, dict(
+                    kt=cmd.format(w=wl), fetch=pmc.format(c="FETCH_SIZE", w=wl),
+                    write=pmc.format(c="WRITE_SIZE", w=wl))))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
               "the op shards over sequences and value heads without any exchange, "
@@ -238,7 +327,7 @@ def main(argv=None):
         "us_per_layer": ms_per_step * 1e3,
         "state_gbps": w.state_bytes() / kernel_s / 1e9,
         "roofline": roofline,
-        "kernel_digest": digest[:16],
+        "kernel_digest": digest,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -23,13 +23,12 @@
 //     partner's, so every lane of the row ends with the same bits.
 //   * A workgroup covers rows of one (sequence, value head), so g and beta are
 //     uniform: 64 tokens' worth of alpha = exp(-g) and beta are computed once
-//     per wave (lane t holds token t0+t) and read per token with v_readlane.
-//   * Token t+1's k, q and v are loaded while token t computes (two register
-//     sets used alternately).
-// Two launch geometries instantiate the same template: a short-run one for a
-// single decode token (HBM-bound on the state read and write; small C, many
-// waves in flight) and a long-run one for multi-token calls (VALU-bound; larger
-// C so the per-token reductions are a small share of the work).
+//     per wave (lane t holds token t0+t), parked in LDS and read per token.
+//   * Token t+NB-1's k, q and v are requested while token t computes (a ring
+//     of NB register sets).
+// Two launch geometries instantiate the same template: one for a single decode
+// token (HBM-bound on the state read and write) and one for multi-token calls
+// (VALU- and latency-bound; two rows per lane share each k/q register).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -74,11 +73,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float read_lane(float x, uint32_t lane) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
-}
-
 __device__ __forceinline__ f4 load4(const float *p) {
   return *reinterpret_cast<const f4 *>(p);
 }
@@ -96,8 +90,9 @@ struct KernelArgs {
 };
 
 // DK: key dim. C: cells per lane per row. R: rows per lane. WAVES: waves per
-// workgroup. CAPTURE: also write the per-token state.
-template <int DK, int C, int R, int WAVES, bool CAPTURE>
+// workgroup. NB: token buffers in the prefetch ring (token t + NB - 1 is
+// requested while token t computes). CAPTURE: also write the per-token state.
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE>
 __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   constexpr int L = DK / C;      // lanes sharing one state row
   constexpr int G = 64 / L;      // row groups per wave
@@ -105,6 +100,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   constexpr int ROWS_PER_WAVE = G * R;
   constexpr int ROWS = WAVES * ROWS_PER_WAVE;
   static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
+  static_assert(NB >= 2, "at least two token buffers");
 
   // Workgroup -> (sequence s, value head vh, block of rows); all uniform.
   const uint32_t bid = blockIdx.x;
@@ -229,30 +225,52 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     }
   };
 
-  float g_raw, b_raw, alphas = 0.f, betas = 0.f;
+  // alpha = exp(-g) and beta for the current 64-token chunk live in a small
+  // per-wave LDS slot: computed once per chunk (one exp per lane), read per
+  // token as one broadcast ds_read_b64. The raw g/beta of the next chunk are
+  // requested a chunk ahead into registers that nothing else reads.
+  __shared__ float2 ab_lds[WAVES][64];
+  float2 *ab = ab_lds[wave];
+  float g_raw, b_raw;
   load_chunk(0, g_raw, b_raw);
-  Tok A, B;
-  load_token(0, A);
   auto next_chunk = [&](uint32_t t) {
     if ((t & 63u) == 0) {
-      alphas = expf(-g_raw);
-      betas = b_raw;
+      ab[lane] = make_float2(expf(-g_raw), b_raw);
       if (T - t > 64) load_chunk(t + 64, g_raw, b_raw);
+      __builtin_amdgcn_wave_barrier();
     }
   };
-  // The prefetch is unconditional (the last token is loaded twice at the
-  // end): a skipped prefetch on some paths would make the compiler's memory
-  // counter bookkeeping wait for every outstanding load, prefetch included.
-  for (uint32_t t = 0;;) {
+  auto run = [&](uint32_t t, const Tok &x) {
     next_chunk(t);
-    load_token(t + 1 < T ? t + 1 : t, B);
-    step(t, A, read_lane(alphas, t & 63u), read_lane(betas, t & 63u));
-    if (++t == T) break;
-    next_chunk(t);
-    load_token(t + 1 < T ? t + 1 : t, A);
-    step(t, B, read_lane(alphas, t & 63u), read_lane(betas, t & 63u));
-    if (++t == T) break;
+    const float2 a_b = ab[t & 63u];
+    step(t, x, a_b.x, a_b.y);
+  };
+
+  // Prefetch ring. Invariant at the top of each group: buf[0 .. NB-2] hold
+  // tokens t .. t+NB-2. Requests past the last token are clamped to it (they
+  // are never used): every request is unconditional, because a request that
+  // some paths skip makes the compiler's memory-counter bookkeeping wait for
+  // all outstanding loads, the prefetches included.
+  Tok buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
+  uint32_t t = 0;
+  while (T - t >= NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const uint32_t ahead = t + NB - 1;
+      load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
+      run(t, buf[u]);
+      ++t;
+    }
   }
+  // Fewer than NB tokens remain, all already requested.
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (t < T) {
+      run(t, buf[u]);
+      ++t;
+    }
 
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -269,29 +287,37 @@ struct Geometry {
   const void *kernel;
 };
 
-template <int DK, int C, int R, int WAVES, bool CAPTURE>
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE>
 constexpr Geometry make_geometry() {
   return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
                   reinterpret_cast<const void *>(
-                      &gdn_recurrent<DK, C, R, WAVES, CAPTURE>)};
+                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE>)};
 }
 
-// Calls with at most this many tokens use the short-run geometry.
-constexpr uint32_t kShortRunTokens = 1;
-
+// Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
+// HBM-resident inputs; D_k = 128 workloads of one-token decode, 64-sequence
+// batched decode, 4-token capture and 512-token prefill):
+//   one token  : C = D_k/16 cells per lane (16 lanes per row), one row per
+//                lane, 4 waves, two token buffers. Pure streaming of the state;
+//                all C and wave counts from 4 to 16 cells and 1 to 4 waves
+//                measured within a few percent of each other.
+//   two or more: two rows per lane (each k/q register feeds two rows, which
+//                halves k/q operand traffic per cell: 418 -> 289 us at 512
+//                tokens against one row per lane), 16 lanes per row, 4 waves,
+//                a four-token prefetch ring.
 template <bool CAPTURE>
 Geometry pick(uint32_t d_k, uint32_t n_tokens) {
-  const bool short_run = n_tokens <= kShortRunTokens;
+  const bool one_token = n_tokens == 1;
   switch (d_k) {
     case 32:
-      return short_run ? make_geometry<32, 4, 1, 2, CAPTURE>()
-                       : make_geometry<32, 4, 1, 4, CAPTURE>();
+      return one_token ? make_geometry<32, 4, 1, 4, 2, CAPTURE>()
+                       : make_geometry<32, 4, 2, 4, 4, CAPTURE>();
     case 64:
-      return short_run ? make_geometry<64, 4, 1, 2, CAPTURE>()
-                       : make_geometry<64, 8, 1, 4, CAPTURE>();
+      return one_token ? make_geometry<64, 4, 1, 4, 2, CAPTURE>()
+                       : make_geometry<64, 4, 2, 4, 4, CAPTURE>();
     case 128:
-      return short_run ? make_geometry<128, 8, 1, 2, CAPTURE>()
-                       : make_geometry<128, 16, 1, 4, CAPTURE>();
+      return one_token ? make_geometry<128, 8, 1, 4, 2, CAPTURE>()
+                       : make_geometry<128, 8, 2, 4, 4, CAPTURE>();
     default:
       return Geometry{0, 0, nullptr};
   }
