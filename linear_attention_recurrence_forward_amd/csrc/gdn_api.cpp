@@ -126,8 +126,9 @@ gdn_status gdn_check_params(const gdn_params *p) {
   if (p->reserved6 != 0 || p->reserved7 != 0) return GDN_ERR_RESERVED_NONZERO;
   Counts c;
   if (!counts_of(p, &c)) return GDN_ERR_SIZE_OVERFLOW;
-  // The kernels address a head's state with 32-bit element offsets.
-  if ((uint64_t)p->d_v * p->d_k > (uint64_t(1) << 31)) return GDN_ERR_SIZE_OVERFLOW;
+  // The kernels address one head's state (d_v * d_k floats) through a buffer
+  // descriptor whose size in bytes is a 32-bit field.
+  if ((uint64_t)p->d_v * p->d_k >= (uint64_t(1) << 30)) return GDN_ERR_SIZE_OVERFLOW;
   // One-dimensional grid: blocks * threads (at most 256 per block) must stay
   // below 2^32 work-items, for either geometry, with or without capture.
   for (bool cap : {false, true}) {

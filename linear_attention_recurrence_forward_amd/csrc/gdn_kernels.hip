@@ -26,9 +26,15 @@
 //     per wave (lane t holds token t0+t), parked in LDS and read per token.
 //   * Token t+NB-1's k, q and v are requested while token t computes (a ring
 //     of NB register sets).
+//   * Every access goes through a buffer resource (a 128-bit scalar
+//     descriptor: base address and size in bytes) plus a 32-bit per-lane byte
+//     offset that is fixed for the whole loop. Per-token bases advance with
+//     scalar arithmetic only, and the hardware range check drops any access
+//     past the descriptor's size (loads return 0, stores are discarded).
 // Two launch geometries instantiate the same template: one for a single decode
-// token (HBM-bound on the state read and write) and one for multi-token calls
-// (VALU- and latency-bound; two rows per lane share each k/q register).
+// token (HBM-bound on the state read and write; straight-line, no ring) and one
+// for multi-token calls (VALU- and latency-bound; two rows per lane share each
+// k/q register).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,6 +45,7 @@ namespace gdn {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
 // DPP_CTRL encodings (AMD CDNA3/CDNA4 ISA, "DPP" modifier).
 constexpr int kDppXor1 = 0xB1;        // quad_perm:[1,0,3,2]  lane ^ 1
@@ -49,11 +56,12 @@ constexpr int kDppMirror = 0x140;     // row_mirror: lane -> 15 - lane (per 16)
 // xor_mask 0x10 -> lane ^ 16 within each group of 32.
 constexpr int kSwizzleXor16 = 0x1F | (0x10 << 10);
 
+// Lane value of the partner selected by CTRL (all source lanes are active).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                         0xF, 0xF, false));
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                      0xF, true));
 }
 
 // Sum over the L consecutive lanes of a row group (L a power of two, 2..32).
@@ -73,12 +81,39 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ f4 load4(const float *p) {
-  return *reinterpret_cast<const f4 *>(p);
+// ---------------------------------------------------------------- buffers
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy bit of buffer stores for non-temporal (streaming) writes.
+constexpr int kNonTemporal = 2;
+
+// Descriptor over `bytes` bytes from `base` (bytes < 2^32).
+__device__ __forceinline__ rsrc_t buffer(const float *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes,
+                                           kBufferWord3);
 }
 
-__device__ __forceinline__ void store4_stream(float *p, f4 x) {
-  __builtin_nontemporal_store(x, reinterpret_cast<f4 *>(p));
+__device__ __forceinline__ f4 load4(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ float load1(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void store1(rsrc_t r, uint32_t byte_off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), r,
+                                        byte_off, 0, 0);
+}
+
+__device__ __forceinline__ void store4_stream(rsrc_t r, uint32_t byte_off, f4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, byte_off,
+                                         0, kNonTemporal);
 }
 
 struct KernelArgs {
@@ -91,7 +126,8 @@ struct KernelArgs {
 
 // DK: key dim. C: cells per lane per row. R: rows per lane. WAVES: waves per
 // workgroup. NB: token buffers in the prefetch ring (token t + NB - 1 is
-// requested while token t computes). CAPTURE: also write the per-token state.
+// requested while token t computes); NB = 1 selects the one-token path, used
+// only for n_tokens == 1. CAPTURE: also write the per-token state.
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE>
 __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   constexpr int L = DK / C;      // lanes sharing one state row
@@ -99,8 +135,9 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   constexpr int NV = C / 4;      // float4 vectors per lane per row
   constexpr int ROWS_PER_WAVE = G * R;
   constexpr int ROWS = WAVES * ROWS_PER_WAVE;
+  constexpr uint32_t ROW_BYTES = DK * 4;
   static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
-  static_assert(NB >= 2, "at least two token buffers");
+  static_assert(R <= L, "one output lane per row");
 
   // Workgroup -> (sequence s, value head vh, block of rows); all uniform.
   const uint32_t bid = blockIdx.x;
@@ -130,14 +167,14 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     row[r] = ok[r] ? i : Dv - 1;
   }
 
-  // Addressing: every array is reached through a wave-uniform base pointer
-  // (scalar registers; advanced per token by a uniform stride) plus a
-  // per-lane 32-bit element offset that stays fixed for the whole loop. The
-  // host guarantees d_v * d_k <= 2^31, so these offsets cannot wrap.
+  // Wave-uniform bases of this (s, vh): token-0 addresses and per-token
+  // strides, in elements. Descriptors per token cover exactly one token's
+  // row of k/q (D_k floats), v/output (D_v floats) or capture (D_v x D_k).
+  // The host guarantees d_v * d_k * 4 < 2^32.
   const uint64_t tok0 = (uint64_t)s * T;                   // first token of s
-  const float *k_tok = a.k + (tok0 * Hk + kh) * DK;        // token 0
+  const float *k_tok = a.k + (tok0 * Hk + kh) * DK;
   const float *q_tok = a.q + (tok0 * Hk + kh) * DK;
-  const uint64_t kq_step = Hk * DK;                        // per token
+  const uint64_t kq_step = Hk * DK;
   const float *v_tok = a.v + (tok0 * Hv + vh) * Dv;
   float *o_tok = a.output + (tok0 * Hv + vh) * Dv;
   const uint64_t v_step = Hv * Dv;
@@ -145,44 +182,50 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   const float *b_tok = a.beta + tok0 * Hv + vh;
   float *c_tok = CAPTURE ? a.capture + (tok0 * Hv + vh) * (uint64_t)Dv * DK : nullptr;
   const uint64_t cap_step = Hv * Dv * DK;
-  const float *s_in = a.state_in + (uint64_t)hs * Dv * DK;
-  float *s_out = a.state_out + (uint64_t)hs * Dv * DK;
+  const uint32_t head_bytes = Dv * ROW_BYTES;
+  const rsrc_t s_in = buffer(a.state_in + (uint64_t)hs * Dv * DK, head_bytes);
+  const rsrc_t s_out = buffer(a.state_out + (uint64_t)hs * Dv * DK, head_bytes);
 
-  // Per-lane offsets: column of vector m is m*4L + 4*sub.
-  const uint32_t col = 4 * sub;
-  uint32_t cell[R];  // element offset of this lane's first cell in its row
+  // Per-lane byte offsets, fixed for the whole call: vector m of row r starts
+  // at column m*4L + 4*sub.
+  const uint32_t col = 16 * sub;
+  uint32_t cell[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) cell[r] = row[r] * DK + col;
+  for (int r = 0; r < R; ++r) cell[r] = row[r] * ROW_BYTES + col;
+  uint32_t vrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) vrow[r] = row[r] * 4;
+  // Output writer: lane sub == r of each row group writes row r's y.
+  uint32_t out_off = vrow[0];
+  bool out_lane = sub == 0 && ok[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r)
+    if (sub == (uint32_t)r) {
+      out_off = vrow[r];
+      out_lane = ok[r];
+    }
 
   f4 st[R][NV];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < NV; ++m) st[r][m] = load4(s_in + cell[r] + m * 4 * L);
+    for (int m = 0; m < NV; ++m) st[r][m] = load4(s_in, cell[r] + m * 16 * L);
 
   struct Tok {
     f4 k[NV], q[NV];
     float v[R];
   };
   auto load_token = [&](uint32_t t, Tok &x) {
-    const float *kt = k_tok + t * kq_step;
-    const float *qt = q_tok + t * kq_step;
-    const float *vt = v_tok + t * v_step;
+    const rsrc_t kt = buffer(k_tok + t * kq_step, ROW_BYTES);
+    const rsrc_t qt = buffer(q_tok + t * kq_step, ROW_BYTES);
+    const rsrc_t vt = buffer(v_tok + t * v_step, Dv * 4);
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
-      x.k[m] = load4(kt + col + m * 4 * L);
-      x.q[m] = load4(qt + col + m * 4 * L);
+      x.k[m] = load4(kt, col + m * 16 * L);
+      x.q[m] = load4(qt, col + m * 16 * L);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) x.v[r] = vt[row[r]];
-  };
-
-  // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
-  // t0 + j (clamped to the last token; lanes past the end are never read).
-  auto load_chunk = [&](uint32_t t0, float &gr, float &br) {
-    const uint32_t t = lane < T - t0 ? t0 + lane : T - 1;
-    gr = g_tok[(uint64_t)t * Hv];
-    br = b_tok[(uint64_t)t * Hv];
+    for (int r = 0; r < R; ++r) x.v[r] = load1(vt, vrow[r]);
   };
 
   auto step = [&](uint32_t t, const Tok &x, float alpha, float b) {
@@ -200,7 +243,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       const float sk = group_sum<L>(part);
       d[r] = (x.v[r] - sk) * b;
     }
-    float *ot = o_tok + t * v_step;
+    float y_out = 0.f;  // lane sub == r keeps row r's output
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float part = 0.f;
@@ -212,71 +255,87 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
           part = __builtin_fmaf(st[r][m][e], x.q[m][e], part);
         }
       const float y = group_sum<L>(part);
-      if (ok[r] && sub == 0) ot[row[r]] = y * a.q_scale;
+      y_out = sub == (uint32_t)r ? y : y_out;
     }
+    if (out_lane) store1(buffer(o_tok + t * v_step, Dv * 4), out_off, y_out * a.q_scale);
     if constexpr (CAPTURE) {
-      float *ct = c_tok + t * cap_step;
+      const rsrc_t ct = buffer(c_tok + t * cap_step, head_bytes);
 #pragma unroll
       for (int r = 0; r < R; ++r)
         if (ok[r])
 #pragma unroll
-          for (int m = 0; m < NV; ++m)
-            store4_stream(ct + cell[r] + m * 4 * L, st[r][m]);
+          for (int m = 0; m < NV; ++m) store4_stream(ct, cell[r] + m * 16 * L, st[r][m]);
     }
   };
 
-  // alpha = exp(-g) and beta for the current 64-token chunk live in a small
-  // per-wave LDS slot: computed once per chunk (one exp per lane), read per
-  // token as one broadcast ds_read_b64. The raw g/beta of the next chunk are
-  // requested a chunk ahead into registers that nothing else reads.
-  __shared__ float2 ab_lds[WAVES][64];
-  float2 *ab = ab_lds[wave];
-  float g_raw, b_raw;
-  load_chunk(0, g_raw, b_raw);
-  auto next_chunk = [&](uint32_t t) {
-    if ((t & 63u) == 0) {
-      ab[lane] = make_float2(expf(-g_raw), b_raw);
-      if (T - t > 64) load_chunk(t + 64, g_raw, b_raw);
-      __builtin_amdgcn_wave_barrier();
-    }
-  };
-  auto run = [&](uint32_t t, const Tok &x) {
-    next_chunk(t);
-    const float2 a_b = ab[t & 63u];
-    step(t, x, a_b.x, a_b.y);
-  };
+  if constexpr (NB == 1) {
+    // One token (n_tokens == 1): straight line, g and beta read directly.
+    Tok x;
+    load_token(0, x);
+    const rsrc_t gb = buffer(g_tok, 4), bb = buffer(b_tok, 4);
+    step(0, x, expf(-load1(gb, 0)), load1(bb, 0));
+  } else {
+    // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
+    // t0 + j (clamped to the last token; lanes past the end are never read).
+    auto load_chunk = [&](uint32_t t0, float &gr, float &br) {
+      const uint32_t t = lane < T - t0 ? t0 + lane : T - 1;
+      gr = *(g_tok + (uint64_t)t * Hv);
+      br = *(b_tok + (uint64_t)t * Hv);
+    };
 
-  // Prefetch ring. Invariant at the top of each group: buf[0 .. NB-2] hold
-  // tokens t .. t+NB-2. Requests past the last token are clamped to it (they
-  // are never used): every request is unconditional, because a request that
-  // some paths skip makes the compiler's memory-counter bookkeeping wait for
-  // all outstanding loads, the prefetches included.
-  Tok buf[NB];
+    // alpha = exp(-g) and beta for the current 64-token chunk live in a small
+    // per-wave LDS slot: computed once per chunk (one exp per lane), read per
+    // token as one broadcast ds_read_b64. The raw g/beta of the next chunk
+    // are requested a chunk ahead into registers that nothing else reads.
+    __shared__ float2 ab_lds[WAVES][64];
+    float2 *ab = ab_lds[wave];
+    float g_raw, b_raw;
+    load_chunk(0, g_raw, b_raw);
+    auto next_chunk = [&](uint32_t t) {
+      if ((t & 63u) == 0) {
+        ab[lane] = make_float2(expf(-g_raw), b_raw);
+        if (T - t > 64) load_chunk(t + 64, g_raw, b_raw);
+        __builtin_amdgcn_wave_barrier();
+      }
+    };
+    auto run = [&](uint32_t t, const Tok &x) {
+      next_chunk(t);
+      const float2 a_b = ab[t & 63u];
+      step(t, x, a_b.x, a_b.y);
+    };
+
+    // Prefetch ring. Invariant at the top of each group: buf[0 .. NB-2] hold
+    // tokens t .. t+NB-2. Requests past the last token are clamped to it
+    // (they are never used): every request is unconditional, because a
+    // request that some paths skip makes the compiler's memory-counter
+    // bookkeeping wait for all outstanding loads, the prefetches included.
+    Tok buf[NB];
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
-  uint32_t t = 0;
-  while (T - t >= NB) {
+    for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
+    uint32_t t = 0;
+    while (T - t >= NB) {
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const uint32_t ahead = t + NB - 1;
-      load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
-      run(t, buf[u]);
-      ++t;
+      for (int u = 0; u < NB; ++u) {
+        const uint32_t ahead = t + NB - 1;
+        load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
+        run(t, buf[u]);
+        ++t;
+      }
     }
+    // Fewer than NB tokens remain, all already requested.
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+      if (t < T) {
+        run(t, buf[u]);
+        ++t;
+      }
   }
-  // Fewer than NB tokens remain, all already requested.
-#pragma unroll
-  for (int u = 0; u < NB - 1; ++u)
-    if (t < T) {
-      run(t, buf[u]);
-      ++t;
-    }
 
 #pragma unroll
   for (int r = 0; r < R; ++r)
     if (ok[r])
 #pragma unroll
-      for (int m = 0; m < NV; ++m) store4_stream(s_out + cell[r] + m * 4 * L, st[r][m]);
+      for (int m = 0; m < NV; ++m) store4_stream(s_out, cell[r] + m * 16 * L, st[r][m]);
 }
 
 // ---------------------------------------------------------------- geometry
@@ -298,7 +357,7 @@ constexpr Geometry make_geometry() {
 // HBM-resident inputs; D_k = 128 workloads of one-token decode, 64-sequence
 // batched decode, 4-token capture and 512-token prefill):
 //   one token  : C = D_k/16 cells per lane (16 lanes per row), one row per
-//                lane, 4 waves, two token buffers. Pure streaming of the state;
+//                lane, 4 waves, straight-line code. Pure streaming of the state;
 //                all C and wave counts from 4 to 16 cells and 1 to 4 waves
 //                measured within a few percent of each other.
 //   two or more: two rows per lane (each k/q register feeds two rows, which
@@ -310,13 +369,13 @@ Geometry pick(uint32_t d_k, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
   switch (d_k) {
     case 32:
-      return one_token ? make_geometry<32, 4, 1, 4, 2, CAPTURE>()
+      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE>()
                        : make_geometry<32, 4, 2, 4, 4, CAPTURE>();
     case 64:
-      return one_token ? make_geometry<64, 4, 1, 4, 2, CAPTURE>()
+      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE>()
                        : make_geometry<64, 4, 2, 4, 4, CAPTURE>();
     case 128:
-      return one_token ? make_geometry<128, 8, 1, 4, 2, CAPTURE>()
+      return one_token ? make_geometry<128, 8, 1, 4, 1, CAPTURE>()
                        : make_geometry<128, 8, 2, 4, 4, CAPTURE>();
     default:
       return Geometry{0, 0, nullptr};
