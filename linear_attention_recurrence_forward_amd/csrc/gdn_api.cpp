@@ -127,8 +127,12 @@ gdn_status gdn_check_params(const gdn_params *p) {
   Counts c;
   if (!counts_of(p, &c)) return GDN_ERR_SIZE_OVERFLOW;
   // The kernels address one head's state (d_v * d_k floats) through a buffer
-  // descriptor whose size in bytes is a 32-bit field.
+  // descriptor whose size in bytes is a 32-bit field, and step through up to
+  // 64 + 8 tokens of k/q or v/output with 32-bit scalar byte offsets.
   if ((uint64_t)p->d_v * p->d_k >= (uint64_t(1) << 30)) return GDN_ERR_SIZE_OVERFLOW;
+  if ((uint64_t)p->n_v_heads * p->d_v >= (uint64_t(1) << 23) ||
+      (uint64_t)p->n_k_heads * p->d_k >= (uint64_t(1) << 23))
+    return GDN_ERR_SIZE_OVERFLOW;
   // One-dimensional grid: blocks * threads (at most 256 per block) must stay
   // below 2^32 work-items, for either geometry, with or without capture.
   for (bool cap : {false, true}) {

@@ -96,19 +96,42 @@ __device__ __forceinline__ rsrc_t buffer(const float *base, uint32_t bytes) {
                                            kBufferWord3);
 }
 
-__device__ __forceinline__ f4 load4(rsrc_t r, uint32_t byte_off) {
+// A value the compiler cannot prove wave-uniform but that is (scalar operand).
+__device__ __forceinline__ uint32_t uniform(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(x);
+}
+
+// The same for a pointer: both 32-bit halves through readfirstlane, widened
+// without sign extension (readfirstlane returns a signed int).
+template <typename P>
+__device__ __forceinline__ P *uniform(P *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P *>((hi << 32) | lo);
+}
+
+// Descriptor size for `elems` floats, clamped to the 32-bit size field.
+__device__ __forceinline__ uint32_t extent(uint64_t elems) {
+  const uint64_t bytes = elems * 4;
+  return bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
+}
+
+// Loads and stores at lane byte offset `off` plus wave-uniform byte offset
+// `soff` (the descriptor's scalar offset operand).
+__device__ __forceinline__ f4 load4(rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_bit_cast(f4,
-                            __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
 }
 
-__device__ __forceinline__ float load1(rsrc_t r, uint32_t byte_off) {
+__device__ __forceinline__ float load1(rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_bit_cast(float,
-                            __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+                            __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
 }
 
-__device__ __forceinline__ void store1(rsrc_t r, uint32_t byte_off, float x) {
+__device__ __forceinline__ void store1(rsrc_t r, uint32_t off, uint32_t soff, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), r,
-                                        byte_off, 0, 0);
+                                        off, soff, 0);
 }
 
 __device__ __forceinline__ void store4_stream(rsrc_t r, uint32_t byte_off, f4 x) {
@@ -215,17 +238,38 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     f4 k[NV], q[NV];
     float v[R];
   };
+  // k, q, v and output are read through descriptors based at token base_t
+  // that reach to the end of this sequence; token t's row is at scalar byte
+  // offset (t - base_t) * stride. Rebased every 64 tokens, so the scalar
+  // offsets stay far below 2^32 (the host bounds the per-token strides).
+  const uint32_t kq_bytes = (uint32_t)kq_step * 4, v_bytes = (uint32_t)v_step * 4;
+  uint32_t base_t = 0, kq_ext = 0, v_ext = 0;
+  const float *k_b = nullptr, *q_b = nullptr, *v_b = nullptr;
+  float *o_b = nullptr;
+  auto rebase = [&](uint32_t t0) {
+    base_t = uniform(t0);
+    const uint64_t rest = T - t0 - 1;  // tokens after t0
+    k_b = uniform(k_tok + t0 * kq_step);
+    q_b = uniform(q_tok + t0 * kq_step);
+    v_b = uniform(v_tok + t0 * v_step);
+    o_b = uniform(o_tok + t0 * v_step);
+    kq_ext = uniform(extent(rest * kq_step + DK));
+    v_ext = uniform(extent(rest * v_step + Dv));
+  };
+  rebase(0);
+
   auto load_token = [&](uint32_t t, Tok &x) {
-    const rsrc_t kt = buffer(k_tok + t * kq_step, ROW_BYTES);
-    const rsrc_t qt = buffer(q_tok + t * kq_step, ROW_BYTES);
-    const rsrc_t vt = buffer(v_tok + t * v_step, Dv * 4);
+    const uint32_t kq_off = uniform((t - base_t) * kq_bytes);
+    const uint32_t v_off = uniform((t - base_t) * v_bytes);
+    const rsrc_t k_rs = buffer(k_b, kq_ext), q_rs = buffer(q_b, kq_ext);
+    const rsrc_t v_rs = buffer(v_b, v_ext);
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
-      x.k[m] = load4(kt, col + m * 16 * L);
-      x.q[m] = load4(qt, col + m * 16 * L);
+      x.k[m] = load4(k_rs, col + m * 16 * L, kq_off);
+      x.q[m] = load4(q_rs, col + m * 16 * L, kq_off);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) x.v[r] = load1(vt, vrow[r]);
+    for (int r = 0; r < R; ++r) x.v[r] = load1(v_rs, vrow[r], v_off);
   };
 
   auto step = [&](uint32_t t, const Tok &x, float alpha, float b) {
@@ -257,7 +301,9 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       const float y = group_sum<L>(part);
       y_out = sub == (uint32_t)r ? y : y_out;
     }
-    if (out_lane) store1(buffer(o_tok + t * v_step, Dv * 4), out_off, y_out * a.q_scale);
+    if (out_lane)
+      store1(buffer(o_b, v_ext), out_off, uniform((t - base_t) * v_bytes),
+             y_out * a.q_scale);
     if constexpr (CAPTURE) {
       const rsrc_t ct = buffer(c_tok + t * cap_step, head_bytes);
 #pragma unroll
@@ -314,6 +360,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
     uint32_t t = 0;
     while (T - t >= NB) {
+      if (t - base_t >= 64) rebase(t);
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const uint32_t ahead = t + NB - 1;

@@ -85,7 +85,9 @@ OK = dict(d_k=128, d_v=128, n_k_heads=16, n_v_heads=48, n_tokens=1, n_seqs=1)
     ({"reserved7": 7}, "GDN_ERR_RESERVED_NONZERO"),
     ({"n_seqs": 2**32 - 1, "n_tokens": 2**32 - 1}, "GDN_ERR_SIZE_OVERFLOW"),
     ({"d_v": 2**23}, "GDN_ERR_SIZE_OVERFLOW"),
-    ({"d_v": 2**23 - 1, "n_v_heads": 16}, "GDN_OK"),
+    ({"d_v": 2**23 - 1, "n_v_heads": 1, "n_k_heads": 1}, "GDN_OK"),
+    ({"d_v": 2**17, "n_v_heads": 64, "n_k_heads": 1}, "GDN_ERR_SIZE_OVERFLOW"),
+    ({"n_k_heads": 2**16, "n_v_heads": 2**16}, "GDN_ERR_SIZE_OVERFLOW"),
     ({"n_v_heads": 2**20, "n_k_heads": 1, "n_seqs": 2**12}, "GDN_ERR_SIZE_OVERFLOW"),
     ({"d_k": 32, "d_v": 1, "n_k_heads": 1, "n_v_heads": 1}, "GDN_OK"),
     ({"d_k": 64, "d_v": 1000, "n_tokens": 4096, "n_seqs": 3}, "GDN_OK"),
