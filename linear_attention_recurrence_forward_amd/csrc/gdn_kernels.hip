@@ -218,15 +218,19 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   uint32_t vrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) vrow[r] = row[r] * 4;
-  // Output writer: lane sub == r of each row group writes row r's y.
-  uint32_t out_off = vrow[0];
-  bool out_lane = sub == 0 && ok[0];
+  // Outputs are written L tokens at a time: lane sub of a row group keeps
+  // the row's output of token t0 + sub (t0 a multiple of L) in yk, and one
+  // store per row writes the L tokens. Stores share the in-order memory
+  // counter with the prefetch loads, so one store per token would hold back
+  // every later prefetch behind its write acknowledgement.
+  constexpr uint32_t TB = L;  // tokens per output batch (divides 64)
+  float yk[R];
+  uint32_t yoff[R];  // lane's output address: row r of token t0 + sub
 #pragma unroll
-  for (int r = 1; r < R; ++r)
-    if (sub == (uint32_t)r) {
-      out_off = vrow[r];
-      out_lane = ok[r];
-    }
+  for (int r = 0; r < R; ++r) {
+    yk[r] = 0.f;
+    yoff[r] = vrow[r] + sub * (uint32_t)(Hv * Dv * 4);
+  }
 
   f4 st[R][NV];
 #pragma unroll
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       const float sk = group_sum<L>(part);
       d[r] = (x.v[r] - sk) * b;
     }
-    float y_out = 0.f;  // lane sub == r keeps row r's output
+    const bool mine = sub == (t & (TB - 1));
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float part = 0.f;
@@ -299,11 +303,19 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
           part = __builtin_fmaf(st[r][m][e], x.q[m][e], part);
         }
       const float y = group_sum<L>(part);
-      y_out = sub == (uint32_t)r ? y : y_out;
+      yk[r] = mine ? y * a.q_scale : yk[r];
     }
-    if (out_lane)
-      store1(buffer(o_b, v_ext), out_off, uniform((t - base_t) * v_bytes),
-             y_out * a.q_scale);
+    if ((t & (TB - 1)) == TB - 1 || t + 1 == T) {
+      // Lanes 0 .. t % TB of each row group hold tokens t0 .. t. base_t is a
+      // multiple of 64 and at most t, so t0 - base_t >= 0.
+      const uint32_t t0 = t & ~(TB - 1);
+      const rsrc_t o_rs = buffer(o_b, v_ext);
+      const uint32_t soff = uniform((t0 - base_t) * v_bytes);
+      if (sub <= (t & (TB - 1)))
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (ok[r]) store1(o_rs, yoff[r], soff, yk[r]);
+    }
     if constexpr (CAPTURE) {
       const rsrc_t ct = buffer(c_tok + t * cap_step, head_bytes);
 #pragma unroll
@@ -350,6 +362,9 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       step(t, x, a_b.x, a_b.y);
     };
 
+    // base_t moves in steps of 64 only if every group starts on a multiple
+    // of NB that divides 64.
+    static_assert(64 % NB == 0, "ring groups align with 64-token chunks");
     // Prefetch ring. Invariant at the top of each group: buf[0 .. NB-2] hold
     // tokens t .. t+NB-2. Requests past the last token are clamped to it
     // (they are never used): every request is unconditional, because a
