@@ -49,7 +49,9 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["rollback"],
+                    help="forward workload, or 'rollback': accepted-prefix rollback "
+                         "on the spec_verify shape")
     ap.add_argument("--launch", default="graph", choices=("graph", "direct"))
     ap.add_argument("--layers", type=int, default=0,
                     help="input sets to cycle through (0: enough for 1 GiB)")
@@ -72,10 +74,10 @@ def kernel_digest() -> str:
     return build.source_digest()
 
 
-def traffic_from_profiles(workload: str, digest: str):
+def traffic_from_profiles(workload: str, digest: str, kernel: str = KERNEL_NAME):
     """HBM bytes per launch measured with rocprofv3 counters for this exact
     kernel build (None when absent or taken on another build)."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -91,12 +93,25 @@ def _csv(path):
         return list(csv.DictReader(f))
 
 
+def workload_info(name: str):
+    """(forward workload, kernel name, algorithmic bytes per launch, description)
+    of a bench workload name; 'rollback' is the rollback copy on the
+    spec_verify shape (one state slice read and written per sequence, plus the
+    index array)."""
+    if name == "rollback":
+        w = WORKLOADS["spec_verify"]
+        return (w, "gdn_rollback_kernel", w.state_bytes() + 4 * w.n_seqs,
+                "accepted-prefix rollback after " + w.description)
+    w = WORKLOADS[name]
+    return w, KERNEL_NAME, w.algorithmic_bytes(), w.description
+
+
 def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict) -> str:
     """Summaries under profiles/ from rocprofv3 CSV output (see --summarize-rocprof):
     the kernel-trace statistics of every kernel, and the HBM bytes per launch of
     gdn_recurrent from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
     counter reads for a plain device copy of calib_mib MiB."""
-    w = WORKLOADS[workload]
+    w, kernel, alg, description = workload_info(workload)
     digests = set()
     for log in (f"kt_{workload}.log", f"pmc_FETCH_SIZE_{workload}.log",
                 f"pmc_WRITE_SIZE_{workload}.log"):
@@ -108,7 +123,7 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict) -
         raise SystemExit(f"{workload}: profiled runs disagree on the kernel build: {digests}")
     digest = digests.pop()
     stats = _csv(os.path.join(src, f"kt_{workload}", "run_kernel_stats.csv"))
-    lines = [f"# {KERNEL_NAME}: {w.description}", "",
+    lines = [f"# {kernel}: {description}", "",
              f"kernel digest (sha256 of sources + flags) of the profiled build: `{digest}`", "",
              "## rocprofv3 --kernel-trace --stats", "", "```", commands["kt"], "```", "",
              "| kernel | calls | average µs | min µs | max µs | share % |",
@@ -124,19 +139,18 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict) -
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = _csv(os.path.join(src, f"pmc_{ctr}_{workload}", "run_counter_collection.csv"))
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        ours = [float(r["Counter_Value"]) for r in rows if KERNEL_NAME in r["Kernel_Name"]]
+        ours = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
         ref_kib = max(copies)  # the calibration copy is the largest copy
         factor = (calib_mib * 1024.0) / ref_kib  # true KiB per counted KiB
         per[ctr] = dict(mean_kib=sum(ours) / len(ours), dispatches=len(ours),
                         copy_kib=ref_kib, factor=factor)
     fetch = per["FETCH_SIZE"]["mean_kib"] * per["FETCH_SIZE"]["factor"] * 1024
     write = per["WRITE_SIZE"]["mean_kib"] * per["WRITE_SIZE"]["factor"] * 1024
-    alg = w.algorithmic_bytes()
     lines += ["", "## HBM bytes per launch (rocprofv3 --pmc, one counter per run)", "",
               "```", commands["fetch"], commands["write"], "```", "",
               f"The plain copy of {calib_mib} MiB (`__amd_rocclr_copyBuffer`) reads and "
               f"writes {calib_mib} MiB; each counter is scaled by what it reads for that copy.",
-              "", "| counter | gdn_recurrent KiB/dispatch (raw) | copy KiB (raw) | scale | "
+              "", f"| counter | {kernel} KiB/dispatch (raw) | copy KiB (raw) | scale | "
               "bytes/launch |", "|---|---|---|---|---|"]
     for ctr, b in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
         d = per[ctr]
@@ -145,13 +159,13 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict) -
     lines += ["", f"Total HBM traffic per launch: {fetch + write:,.0f} B; algorithmic: "
               f"{alg:,} B (ratio {(fetch + write) / alg:.3f}).", ""]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    md = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}.md")
+    md = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
     with open(md, "w") as f:
         f.write("\n".join(lines))
-    rec = dict(kernel=KERNEL_NAME, workload=workload, kernel_digest=digest,
+    rec = dict(kernel=kernel, workload=workload, kernel_digest=digest,
                hbm_bytes_per_launch=fetch + write, fetch_bytes=fetch, write_bytes=write,
                algorithmic_bytes=alg, counters=per, calibration_copy_mib=calib_mib)
-    with open(os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_hbm_traffic.json"),
+    with open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json"),
               "w") as f:
         json.dump(rec, f, indent=1)
     return md
@@ -188,6 +202,26 @@ def cpu_baseline(w, budget_s: float):
     return dict(value=value, unit=unit, cores=1, kind="oracle", sample=sample)
 
 
+def cpu_baseline_rollback(w, budget_s: float):
+    """The oracle's rollback copy, timed on the host like cpu_baseline."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(w.seed)
+    cap = rng.standard_normal((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
+                              dtype=np.float32)
+    state = np.zeros((w.n_seqs, w.n_v_heads, w.d_v, w.d_k), np.float32)
+    acc = rng.integers(0, w.n_tokens, size=w.n_seqs).astype(np.uint32)
+    calls, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.rollback(cap, acc, state)
+        calls += 1
+    dt = time.perf_counter() - t0
+    return dict(value=calls * (w.state_bytes() + 4 * w.n_seqs) / dt / 1e9, unit="GB/s",
+                cores=1, kind="oracle",
+                sample=f"{calls} oracle rollback calls on the spec_verify shape, "
+                       f"{dt:.1f} s, single thread")
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.summarize_rocprof:
@@ -196,7 +230,7 @@ def main(argv=None):
         pmc = ("rocprofv3 --pmc {c} --output-format csv -d <dir>/pmc_{c}_{w} -o run -- "
                "python3 bench.py --workload {w} --steps 10 --warmup 2 --layers 4 "
                "--no-cpu-baseline --launch direct --calibrate-copy-mib 1024")
-        for wl in sorted(WORKLOADS):
+        for wl in sorted(WORKLOADS) + ["rollback"]:
             if os.path.isdir(os.path.join(args.summarize_rocprof, f"kt_{wl}")):
                 print(summarize_rocprof(args.summarize_rocprof, wl, 1024, dict(
                     kt=cmd.format(w=wl), fetch=pmc.format(c="FETCH_SIZE", w=wl),
@@ -217,10 +251,10 @@ def main(argv=None):
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = WORKLOADS[args.workload]
+    rollback = args.workload == "rollback"
+    w, kernel_name, alg_bytes, description = workload_info(args.workload)
     x = make_inputs(w)
     bits = x["q_scale_bits"]
-    alg_bytes = w.algorithmic_bytes()
     layers = args.layers or max(2, math.ceil(RESIDENT_TARGET_BYTES / max(alg_bytes, 1)))
     layers = min(layers, 4096)
 
@@ -234,10 +268,23 @@ def main(argv=None):
                                     device=dev) if w.capture else None)
         sets.append(d)
     params = gdn.params_for(sets[0]["q"], sets[0]["v"], bits)
+    if rollback:
+        # Fill every set's capture with a real forward call, then pick per
+        # sequence a token to roll back to (all inside the call).
+        rng = torch.Generator().manual_seed(w.seed)
+        for d in sets:
+            gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                    d["state_in"], d["output"], d["state_in"],
+                                    d["capture"], params)
+            d["accepted"] = torch.randint(0, w.n_tokens, (w.n_seqs,), generator=rng,
+                                          dtype=torch.int32).to(dev)
+        torch.cuda.synchronize()
 
     def launch(i, stream):
         d = sets[i % layers]
-        if w.capture:
+        if rollback:
+            gdn.gdn_rollback(d["capture"], d["accepted"], d["state_in"], params, stream)
+        elif w.capture:
             gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                     d["state_in"], d["output"], d["state_in"],
                                     d["capture"], params, stream)
@@ -288,7 +335,7 @@ def main(argv=None):
 
     ms_per_step = wall * 1e3 / args.steps
     digest = kernel_digest()
-    if w.name == "prefill":
+    if w.name == "prefill" and not rollback:
         metric_value = w.n_seqs * w.n_tokens * args.steps / wall
         unit = "tokens/s"
         achieved = w.flops() / kernel_s / 1e12
@@ -300,8 +347,8 @@ def main(argv=None):
         achieved = alg_bytes / kernel_s / 1e9
         roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                         frac=achieved / HBM_PEAK_GBPS)
-    roofline["traffic"] = traffic_from_profiles(w.name, digest)
-    roofline["kernel"] = KERNEL_NAME
+    roofline["traffic"] = traffic_from_profiles(args.workload, digest, kernel_name)
+    roofline["kernel"] = kernel_name
     roofline["kernel_us"] = kernel_s * 1e6
 
     line = {
@@ -318,11 +365,12 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.description,
+            "workload": description,
             "d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads, "n_v_heads": w.n_v_heads,
             "n_tokens": w.n_tokens, "n_seqs": w.n_seqs, "q_scale_bits": bits,
             "capture": w.capture, "launch": args.launch, "resident_sets": layers,
-            "algorithmic_bytes_per_step": alg_bytes, "flops_per_step": w.flops(),
+            "algorithmic_bytes_per_step": alg_bytes,
+            "flops_per_step": 0 if rollback else w.flops(),
         },
         "us_per_layer": ms_per_step * 1e3,
         "state_gbps": w.state_bytes() / kernel_s / 1e9,
@@ -330,7 +378,8 @@ def main(argv=None):
         "kernel_digest": digest,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = (cpu_baseline_rollback(w, args.cpu_seconds) if rollback
+                                else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)
     return 0
 

@@ -110,6 +110,21 @@ gdn_status gdn_forward_capture(const float *q, const float *k, const float *v,
                                float *state_out, float *state_capture,
                                const gdn_params *p, void *stream);
 
+/* Accepted-prefix rollback for speculative decoding (mlx-native 0.21.1,
+ * dispatch_gated_delta_net_decode_with_capture doc: on a partial reject the
+ * caller continues from state_capture[..., accepted_idx, ...]). For every
+ * sequence s with accepted[s] < n_tokens, copies the capture slice
+ * state_capture[s][accepted[s]] (n_v_heads x d_v x d_k floats) into
+ * state[s]; sequences with accepted[s] >= n_tokens keep their state.
+ * state_capture is a gdn_forward_capture output for the same params (exactly
+ * n_tokens * d_k * d_v * n_v_heads * n_seqs floats); accepted is device memory
+ * holding n_seqs uint32 indexes (so it can come from a device-side acceptance
+ * step without a host round trip); state holds d_k * d_v * n_v_heads * n_seqs
+ * floats and must not overlap state_capture or accepted (GDN_ERR_ALIASING).
+ * state_capture and state need 16-byte alignment, accepted 4-byte. */
+gdn_status gdn_rollback(const float *state_capture, const uint32_t *accepted,
+                        float *state, const gdn_params *p, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status s);
 

@@ -31,7 +31,8 @@ STATUS = {
 }
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
-EXPORTS = ("gdn_check_params", "gdn_forward", "gdn_forward_capture", "gdn_status_string")
+EXPORTS = ("gdn_check_params", "gdn_forward", "gdn_forward_capture", "gdn_rollback",
+           "gdn_status_string")
 
 
 class GdnParams(ctypes.Structure):
@@ -83,6 +84,9 @@ def _load():
             lib.gdn_forward.restype = ctypes.c_int
             lib.gdn_forward_capture.argtypes = [fp] * 9 + [p, ctypes.c_void_p]
             lib.gdn_forward_capture.restype = ctypes.c_int
+            lib.gdn_rollback.argtypes = [fp, ctypes.POINTER(ctypes.c_uint32), fp, p,
+                                         ctypes.c_void_p]
+            lib.gdn_rollback.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -184,6 +188,31 @@ def gdn_forward_capture(q, k, v, g, beta, state_in, output, state_out, state_cap
                                  ctypes.byref(params), _stream_handle(device, stream))
     if st != 0:
         raise GdnError(st, "gdn_forward_capture")
+
+
+def gdn_rollback(state_capture, accepted, state, params: GdnParams, stream=None) -> None:
+    """Enqueue the accepted-prefix rollback (C: gdn_rollback): for each
+    sequence s with accepted[s] < n_tokens, state[s] = state_capture[s,
+    accepted[s]]. accepted is a device tensor of n_seqs int32/uint32."""
+    lib = _load()
+    st = lib.gdn_check_params(ctypes.byref(params))
+    if st != 0:
+        raise GdnError(st, "gdn_rollback")
+    device = _check_tensors("gdn_rollback", params,
+                            dict(state_capture=state_capture, state_out=state))
+    if not isinstance(accepted, torch.Tensor) or accepted.dtype not in (torch.int32,
+                                                                         torch.uint32):
+        raise ValueError("gdn_rollback: accepted must be an int32 or uint32 tensor")
+    if accepted.device != device or not accepted.is_contiguous():
+        raise ValueError("gdn_rollback: accepted must be contiguous, on the state's device")
+    if accepted.numel() != params.n_seqs:
+        raise ValueError(f"gdn_rollback: accepted element count {accepted.numel()} != "
+                         f"expected {params.n_seqs}")
+    acc = ctypes.cast(ctypes.c_void_p(accepted.data_ptr()), ctypes.POINTER(ctypes.c_uint32))
+    st = lib.gdn_rollback(_ptr(state_capture), acc, _ptr(state), ctypes.byref(params),
+                          _stream_handle(device, stream))
+    if st != 0:
+        raise GdnError(st, "gdn_rollback")
 
 
 def forward(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0, capture: bool = False,

@@ -2,8 +2,8 @@
 
     python -m linear_attention_recurrence_forward_amd.build
 
-Compiles csrc/gdn_kernels.hip and csrc/gdn_api.cpp with hipcc into
-lib/libgdn.so, in-tree. hipcc cross-compiles: no GPU is needed to build.
+Compiles csrc/gdn_kernels.hip, csrc/gdn_rollback.hip and csrc/gdn_api.cpp into
+lib/libgdn.so with hipcc, in-tree. hipcc cross-compiles: no GPU is needed.
 """
 
 from __future__ import annotations
@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIBRARY = os.path.join(LIBDIR, "libgdn.so")
-SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_rollback.hip"),
+           os.path.join(CSRC, "gdn_api.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_launch.h")]
 
 ARCH = "gfx950"

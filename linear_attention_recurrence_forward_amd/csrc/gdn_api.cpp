@@ -115,6 +115,28 @@ gdn_status forward(const float *q, const float *k, const float *v,
 
 extern "C" {
 
+gdn_status gdn_rollback(const float *state_capture, const uint32_t *accepted,
+                        float *state, const gdn_params *p, void *stream) {
+  gdn_status st = gdn_check_params(p);
+  if (st != GDN_OK) return st;
+  if (!state_capture || !accepted || !state) return GDN_ERR_NULL_POINTER;
+  if (!aligned(state_capture, 16) || !aligned(state, 16) || !aligned(accepted, 4))
+    return GDN_ERR_MISALIGNED;
+  Counts c;
+  counts_of(p, &c);
+  const Range r_cap = range_of(state_capture, c.capture);
+  const Range r_state = range_of(state, c.state);
+  const Range r_acc = Range{reinterpret_cast<uintptr_t>(accepted),
+                            reinterpret_cast<uintptr_t>(accepted) +
+                                (uintptr_t)p->n_seqs * sizeof(uint32_t)};
+  if (overlap(r_state, r_cap) || overlap(r_state, r_acc)) return GDN_ERR_ALIASING;
+  if (gdn::enqueue_rollback(state_capture, accepted, state, p->d_k, p->d_v,
+                            p->n_v_heads, p->n_tokens, p->n_seqs,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GDN_ERR_LAUNCH;
+  return GDN_OK;
+}
+
 gdn_status gdn_check_params(const gdn_params *p) {
   if (p == nullptr) return GDN_ERR_NULL_POINTER;
   if (p->d_k == 0 || p->d_v == 0 || p->n_k_heads == 0 || p->n_v_heads == 0)

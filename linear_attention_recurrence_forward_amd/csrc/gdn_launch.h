@@ -25,4 +25,10 @@ uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
 // on `stream`. Returns the runtime's status of the launch.
 hipError_t enqueue_forward(const ForwardArgs &a, hipStream_t stream);
 
+// Enqueue the accepted-prefix rollback copy (validated arguments).
+hipError_t enqueue_rollback(const float *capture, const uint32_t *accepted,
+                            float *state, uint32_t d_k, uint32_t d_v,
+                            uint32_t n_v_heads, uint32_t n_tokens,
+                            uint32_t n_seqs, hipStream_t stream);
+
 }  // namespace gdn

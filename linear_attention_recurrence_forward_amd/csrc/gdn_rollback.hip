@@ -1,0 +1,72 @@
+// Accepted-prefix rollback for speculative decoding (mlx-native 0.21.1,
+// dispatch_gated_delta_net_decode_with_capture doc; mlx-native 0.9.2 capture
+// kernel header): after a verify call with per-token state capture, sequence s
+// continues from the state after its last accepted token a = accepted[s], the
+// capture slice state_capture[s, a]. This kernel copies that slice into the
+// sequence's state slot. An index at or past n_tokens leaves the slot as is.
+//
+// The copy is HBM-bound: every byte of the slice is read once and written
+// once, as 16-byte vectors, four per lane in flight, with non-temporal stores.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kVecsPerThread = 4;  // float4s per lane per pass
+
+__global__ __launch_bounds__(kThreads) void gdn_rollback_kernel(
+    const float *capture, const uint32_t *accepted, float *state,
+    uint32_t n_tokens, uint64_t seq_vecs, uint32_t blocks_per_seq) {
+  const uint32_t s = blockIdx.x / blocks_per_seq;
+  const uint32_t b = blockIdx.x % blocks_per_seq;
+  const uint32_t a = accepted[s];  // same address in every lane
+  if (a >= n_tokens) return;       // uniform: the whole block leaves
+  const f4 *src = reinterpret_cast<const f4 *>(capture) +
+                  ((uint64_t)s * n_tokens + a) * seq_vecs;
+  f4 *dst = reinterpret_cast<f4 *>(state) + (uint64_t)s * seq_vecs;
+  const uint64_t stride = (uint64_t)blocks_per_seq * kThreads * kVecsPerThread;
+  for (uint64_t i0 = ((uint64_t)b * kThreads * kVecsPerThread) + threadIdx.x;
+       i0 < seq_vecs; i0 += stride) {
+    f4 v[kVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+      const uint64_t i = i0 + (uint64_t)u * kThreads;
+      if (i < seq_vecs) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+      const uint64_t i = i0 + (uint64_t)u * kThreads;
+      if (i < seq_vecs) __builtin_nontemporal_store(v[u], dst + i);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t enqueue_rollback(const float *capture, const uint32_t *accepted,
+                            float *state, uint32_t d_k, uint32_t d_v,
+                            uint32_t n_v_heads, uint32_t n_tokens,
+                            uint32_t n_seqs, hipStream_t stream) {
+  // One sequence's state: n_v_heads * d_v * d_k floats, a multiple of 4
+  // because d_k is 32, 64 or 128.
+  const uint64_t seq_vecs = (uint64_t)n_v_heads * d_v * d_k / 4;
+  const uint64_t per_block = (uint64_t)kThreads * kVecsPerThread;
+  uint64_t blocks_per_seq = (seq_vecs + per_block - 1) / per_block;
+  if (blocks_per_seq > 1024) blocks_per_seq = 1024;  // the loop covers the rest
+  const uint64_t blocks = blocks_per_seq * n_seqs;
+  if (blocks == 0 || blocks >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
+  uint32_t bps = (uint32_t)blocks_per_seq;
+  void *args[] = {&capture, &accepted, &state, &n_tokens,
+                  const_cast<uint64_t *>(&seq_vecs), &bps};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_rollback_kernel),
+                         dim3((uint32_t)blocks), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace gdn

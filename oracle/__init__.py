@@ -5,6 +5,6 @@ CPU-baseline leg use it. The product path (the HIP library and its binding)
 never imports it.
 """
 
-from .gdn_oracle import HEAD_MAP_DIV, HEAD_MAP_MOD, build, reference
+from .gdn_oracle import HEAD_MAP_DIV, HEAD_MAP_MOD, build, reference, rollback
 
-__all__ = ["HEAD_MAP_DIV", "HEAD_MAP_MOD", "build", "reference"]
+__all__ = ["HEAD_MAP_DIV", "HEAD_MAP_MOD", "build", "reference", "rollback"]

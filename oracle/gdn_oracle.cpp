@@ -181,4 +181,28 @@ int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
                      state_out, state_capture);
 }
 
+// Accepted-prefix rollback (mlx-native 0.21.1,
+// dispatch_gated_delta_net_decode_with_capture doc; 0.9.2 capture kernel
+// header): after a call with capture, sequence s continues from the state
+// after its accepted token accepted[s], i.e. capture[s, accepted[s]]. An index
+// at or past n_tokens leaves that sequence's state as it was.
+int oracle_gdn_rollback(const float *state_capture, const uint32_t *accepted,
+                        const oracle_gdn_shape *p, float *state) {
+  if (p == nullptr || state_capture == nullptr || accepted == nullptr ||
+      state == nullptr)
+    return 1;
+  if (p->d_k == 0 || p->d_v == 0 || p->n_v_heads == 0 || p->n_tokens == 0 ||
+      p->n_seqs == 0)
+    return 2;
+  const uint64_t head_state = (uint64_t)p->d_k * p->d_v * p->n_v_heads;
+  for (uint64_t s = 0; s < p->n_seqs; ++s) {
+    if (accepted[s] >= p->n_tokens) continue;
+    const float *src =
+        state_capture + (s * p->n_tokens + accepted[s]) * head_state;
+    float *dst = state + s * head_state;
+    for (uint64_t e = 0; e < head_state; ++e) dst[e] = src[e];
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -45,6 +45,12 @@ int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
                            int head_map, double *output, double *state_out,
                            double *state_capture);
 
+/* Accepted-prefix rollback: state[s] = state_capture[s, accepted[s]] for every
+ * sequence whose accepted[s] < n_tokens (others untouched). Uses d_k, d_v,
+ * n_v_heads, n_tokens, n_seqs of p. */
+int oracle_gdn_rollback(const float *state_capture, const uint32_t *accepted,
+                        const oracle_gdn_shape *p, float *state);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,12 @@ def _load(path: str | None = None):
                 fn.argtypes = [fp] * 6 + [ctypes.POINTER(_Shape), ctypes.c_int,
                                           rp, rp, rp]
                 fn.restype = ctypes.c_int
+            if hasattr(lib, "oracle_gdn_rollback"):
+                fn = lib.oracle_gdn_rollback
+                fn.argtypes = [ctypes.POINTER(ctypes.c_float),
+                               ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(_Shape),
+                               ctypes.POINTER(ctypes.c_float)]
+                fn.restype = ctypes.c_int
             _libs[key] = lib
     return _libs[key]
 
@@ -119,3 +125,24 @@ def reference(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return (out, st, cap) if capture else (out, st)
+
+
+def rollback(state_capture, accepted, state, *, library: str | None = None):
+    """Accepted-prefix rollback: returns a copy of state (S, H_v, D_v, D_k) with
+    sequence s replaced by state_capture[s, accepted[s]] when accepted[s] < T.
+    state_capture is (S, T, H_v, D_v, D_k)."""
+    cap = _f32(state_capture)
+    S, T, Hv, Dv, Dk = cap.shape
+    out = np.array(state, dtype=np.float32, copy=True, order="C")
+    if out.shape != (S, Hv, Dv, Dk):
+        raise ValueError("state must be (S, H_v, D_v, D_k) matching the capture")
+    acc = np.ascontiguousarray(accepted, dtype=np.uint32)
+    if acc.shape != (S,):
+        raise ValueError("accepted must hold one index per sequence")
+    shape = _Shape(Dk, Dv, 1, Hv, T, S, 0)
+    rc = _load(library).oracle_gdn_rollback(
+        _ptr(cap, ctypes.c_float), acc.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+        ctypes.byref(shape), _ptr(out, ctypes.c_float))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out

@@ -324,6 +324,32 @@ def pin_matrix_form(ref):
         assert_within(s32, es, 1e-5 + 1e-4 * np.abs(es), f"P10 f32 state ({head_map=})")
 
 
+def pin_rollback(ref, rollback=None):
+    """Accepted-prefix rollback: choosing capture slice a[s] gives exactly the
+    state a call cut to a[s]+1 tokens would have ended with; a[s] = T-1 gives
+    state_out; an index past the call leaves the old state."""
+    import oracle
+    rollback = rollback or oracle.rollback
+    x = gqa_inputs(111, S=4, T=5)
+    out, st, cap = ref(**x, capture=True)
+    T = x["q"].shape[1]
+    old = np.full_like(st, 7.0)
+    # T itself on the first sequence (an index one past the call must be
+    # ignored too); never on the last one, so a wrong read stays in the buffer.
+    acc = np.array([T, 3, T - 1, 0], dtype=np.uint32)
+    got = rollback(cap, acc, old)
+    for s_ in range(4):
+        a_ = int(acc[s_])
+        if a_ >= T:
+            assert_equal(got[s_], old[s_], "rollback past the call keeps the state")
+            continue
+        cut = {n: x[n][s_:s_ + 1, :a_ + 1] for n in ("q", "k", "v", "g", "beta")}
+        _, s_cut = ref(**cut, state_in=x["state_in"][s_:s_ + 1])
+        assert_equal(got[s_], s_cut[0], f"rollback to token {a_} == state after {a_ + 1} tokens")
+    assert_equal(rollback(cap, np.full(4, T - 1, np.uint32), old), st,
+                 "rollback to the last token == state_out")
+
+
 def golden_hand_worked(ref):
     """Hand-derived dyadic example (tests/golden/hand_worked_d2.json), bit-exact."""
     with open(os.path.join(GOLDEN, "hand_worked_d2.json")) as f:
@@ -341,4 +367,4 @@ def golden_hand_worked(ref):
 
 ALL_PINS = [pin_identity, pin_zeroing, pin_delta_rule, pin_chaining, pin_capture,
             pin_q_scale, pin_head_map, pin_linear_attention, pin_pure_decay,
-            pin_matrix_form, golden_hand_worked]
+            pin_matrix_form, pin_rollback, golden_hand_worked]

@@ -186,3 +186,26 @@ def test_binding_checks_tensors_before_the_library():
         gdn.gdn_forward(**bad, params=p)
     with pytest.raises(gdn.GdnError, match="GDN_ERR_ZERO_EXTENT"):
         gdn.gdn_forward(**cpu, params=gdn.make_params(32, 32, 1, 2, 0, 1))
+
+
+def test_rollback_validation(lib):
+    p = gdn.make_params(**{**OK, "n_tokens": 4, "n_seqs": 2})
+    c = p.counts()
+    fp = lambda a: fake(a)  # noqa: E731
+    up = lambda a: ctypes.cast(ctypes.c_void_p(a), ctypes.POINTER(ctypes.c_uint32))  # noqa: E731
+    cap, acc, st = 1 << 40, (1 << 40) + (1 << 32), (1 << 40) + (2 << 32)
+
+    def rb(c_, a_, s_, params=p):
+        return _binding.STATUS[lib.gdn_rollback(c_, a_, s_, ctypes.byref(params), None)]
+
+    assert rb(fp(cap), up(acc), fp(st), gdn.make_params(**{**OK, "n_seqs": 0})) == \
+        "GDN_ERR_ZERO_EXTENT"
+    assert rb(None, up(acc), fp(st)) == "GDN_ERR_NULL_POINTER"
+    assert rb(fp(cap), None, fp(st)) == "GDN_ERR_NULL_POINTER"
+    assert rb(fp(cap), up(acc), None) == "GDN_ERR_NULL_POINTER"
+    assert rb(fp(cap + 4), up(acc), fp(st)) == "GDN_ERR_MISALIGNED"
+    assert rb(fp(cap), up(acc + 2), fp(st)) == "GDN_ERR_MISALIGNED"
+    assert rb(fp(cap), up(acc), fp(st + 8)) == "GDN_ERR_MISALIGNED"
+    # state inside the capture buffer, or over the index array
+    assert rb(fp(cap), up(acc), fp(cap + 4 * c["state_capture"] - 64)) == "GDN_ERR_ALIASING"
+    assert rb(fp(cap), up(st + 16), fp(st)) == "GDN_ERR_ALIASING"

@@ -309,6 +309,47 @@ def test_deterministic():
         assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
 
 
+# ------------------------------------------------------------------ rollback
+
+@pytest.mark.parametrize("name", ["spec_verify", "tiny"])
+def test_rollback(name):
+    """Accepted-prefix rollback on the GPU: bit-exact against the oracle's copy
+    of the GPU capture; equal to the GPU state after the accepted prefix (bit for
+    bit from two tokens on, same geometry); out-of-range indexes keep the state."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    d = dev(x)
+    out, st, cap = gdn.forward(*(d[n] for n in NAMES), q_scale_bits=x["q_scale_bits"],
+                               capture=True)
+    S, T = w.n_seqs, w.n_tokens
+    p = gdn.params_for(d["q"], d["v"], x["q_scale_bits"])
+    rng = np.random.default_rng(3)
+    cases = [np.full(S, T - 1, np.uint32), np.full(S, T, np.uint32),
+             rng.integers(0, T + 2, size=S).astype(np.uint32)]
+    st_np = st.cpu().numpy()
+    cap_np = cap.cpu().numpy()
+    for acc in cases:
+        for dtype in (torch.int32, torch.uint32):
+            slot = torch.full_like(st, 5.0)
+            acc_dev = torch.from_numpy(acc.view(np.int32).copy()).cuda().view(dtype)
+            gdn.gdn_rollback(cap, acc_dev, slot, p)
+            torch.cuda.synchronize()
+            got = slot.cpu().numpy()
+            expect = oracle.rollback(cap_np, acc, np.full(st.shape, 5.0, np.float32))
+            assert np.array_equal(got.view(np.uint32), expect.view(np.uint32)), acc
+        for s_ in range(S):
+            a_ = int(acc[s_])
+            if a_ >= T:
+                assert np.all(got[s_] == 5.0), "index past the call keeps the state"
+            elif a_ == T - 1:
+                assert np.array_equal(got[s_], st_np[s_]), "last token == state_out"
+            elif a_ >= 1:
+                cut = {n: x[n][s_:s_ + 1, :a_ + 1] for n in ("q", "k", "v", "g", "beta")}
+                _, s_cut = run(dict(cut, state_in=x["state_in"][s_:s_ + 1],
+                                    q_scale_bits=x["q_scale_bits"]))
+                assert_equal(got[s_], s_cut[0], f"rollback to {a_} == {a_ + 1}-token state")
+
+
 # ------------------------------------------------------------------ plumbing
 
 def test_side_stream():

@@ -16,7 +16,7 @@ import pytest
 import oracle
 from oracle import gdn_oracle
 
-from pins import ALL_PINS
+from pins import ALL_PINS, pin_rollback
 
 SK = "sk = sk + row[j] * static_cast<real>(k[at_qk(s, t, kh, j)]);"
 DECAY = "row[j] = alpha * row[j];"
@@ -55,6 +55,10 @@ MUTANTS = {
                               "return ((s * Hv + vh) * T + t) * Dv + i;")],
     "scalar_token_head_swapped": [("return (s * T + t) * Hv + vh;",
                                    "return (s * Hv + vh) * T + t;")],
+    "rollback_off_by_one": [("(s * p->n_tokens + accepted[s]) * head_state",
+                             "(s * p->n_tokens + accepted[s] + 1) * head_state")],
+    "rollback_ignores_bound": [("if (accepted[s] >= p->n_tokens) continue;",
+                                "if (accepted[s] > p->n_tokens) continue;")],
     "state_in_ignored": [("X[i * Dk + j] = static_cast<real>(state_in[at_state(s, vh, i, j)]);",
                           "X[i * Dk + j] = 0;")],
 }
@@ -84,10 +88,11 @@ def build_mutant(name, edits, where):
 def test_mutant_is_caught(name, mutant_dir):
     lib = build_mutant(name, MUTANTS[name], str(mutant_dir))
     ref = functools.partial(oracle.reference, library=lib)
+    rb = functools.partial(oracle.rollback, library=lib)
     caught = []
     for pin in ALL_PINS:
         try:
-            pin(ref)
+            pin(ref, rollback=rb) if pin is pin_rollback else pin(ref)
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name!r} passes every pin"
