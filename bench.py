@@ -53,6 +53,8 @@ def parse_args(argv=None):
                     help="forward workload, or 'rollback': accepted-prefix rollback "
                          "on the spec_verify shape")
     ap.add_argument("--launch", default="graph", choices=("graph", "direct"))
+    ap.add_argument("--io", default="f32", choices=("f32", "bf16"),
+                    help="element type of q, k, v and output (state stays f32)")
     ap.add_argument("--layers", type=int, default=0,
                     help="input sets to cycle through (0: enough for 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -93,7 +95,7 @@ def _csv(path):
         return list(csv.DictReader(f))
 
 
-def workload_info(name: str):
+def workload_info(name: str, io: str = "f32"):
     """(forward workload, kernel name, algorithmic bytes per launch, description)
     of a bench workload name; 'rollback' is the rollback copy on the
     spec_verify shape (one state slice read and written per sequence, plus the
@@ -103,6 +105,9 @@ def workload_info(name: str):
         return (w, "gdn_rollback_kernel", w.state_bytes() + 4 * w.n_seqs,
                 "accepted-prefix rollback after " + w.description)
     w = WORKLOADS[name]
+    if io == "bf16":
+        return (w, KERNEL_NAME, w.algorithmic_bytes(io_bytes=2),
+                w.description + ", bf16 q/k/v/output")
     return w, KERNEL_NAME, w.algorithmic_bytes(), w.description
 
 
@@ -252,7 +257,11 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     rollback = args.workload == "rollback"
-    w, kernel_name, alg_bytes, description = workload_info(args.workload)
+    if args.io == "bf16" and args.workload == "rollback":
+        print("bench.py: --io bf16 applies to forward workloads", file=sys.stderr)
+        return 2
+    bf16 = args.io == "bf16"
+    w, kernel_name, alg_bytes, description = workload_info(args.workload, args.io)
     x = make_inputs(w)
     bits = x["q_scale_bits"]
     layers = args.layers or max(2, math.ceil(RESIDENT_TARGET_BYTES / max(alg_bytes, 1)))
@@ -260,10 +269,14 @@ def main(argv=None):
 
     # Resident input sets: same values, distinct memory (state updated in place).
     host = {n: torch.from_numpy(x[n]) for n in NAMES}
+    if bf16:
+        for n in ("q", "k", "v"):
+            host[n] = host[n].to(torch.bfloat16)
     sets = []
     for _ in range(layers):
         d = {n: host[n].to(dev) for n in NAMES}
-        d["output"] = torch.empty(x["v"].shape, device=dev)
+        d["output"] = torch.empty(x["v"].shape, device=dev,
+                                  dtype=torch.bfloat16 if bf16 else torch.float32)
         d["capture"] = (torch.empty((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
                                     device=dev) if w.capture else None)
         sets.append(d)
@@ -284,6 +297,9 @@ def main(argv=None):
         d = sets[i % layers]
         if rollback:
             gdn.gdn_rollback(d["capture"], d["accepted"], d["state_in"], params, stream)
+        elif bf16:
+            gdn.gdn_forward_bf16(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                 d["output"], d["state_in"], d["capture"], params, stream)
         elif w.capture:
             gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                     d["state_in"], d["output"], d["state_in"],
@@ -347,7 +363,8 @@ def main(argv=None):
         achieved = alg_bytes / kernel_s / 1e9
         roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                         frac=achieved / HBM_PEAK_GBPS)
-    roofline["traffic"] = traffic_from_profiles(args.workload, digest, kernel_name)
+    roofline["traffic"] = (None if bf16 else
+                           traffic_from_profiles(args.workload, digest, kernel_name))
     roofline["kernel"] = kernel_name
     roofline["kernel_us"] = kernel_s * 1e6
 
@@ -362,7 +379,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if not bf16 else "bf16 q/k/v/output, f32 state and arithmetic",
         "data": "synthetic",
         "config": {
             "workload": description,
@@ -377,7 +394,7 @@ def main(argv=None):
         "roofline": roofline,
         "kernel_digest": digest,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not bf16:
         line["cpu_baseline"] = (cpu_baseline_rollback(w, args.cpu_seconds) if rollback
                                 else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)

@@ -29,8 +29,8 @@
  *   - Every array pointer is device memory owned by the caller. The library
  *     allocates nothing, keeps no global state and is reentrant.
  *   - q, k, state_in, state_out and state_capture must be 16-byte aligned
- *     (they are read and written as 4-float vectors); v, g, beta and output
- *     4-byte aligned.
+ *     (they are read and written as 4-float vectors; bf16 q and k, 8-byte);
+ *     v, g, beta and output aligned to their element size.
  *   - The call only enqueues work on `stream` (a hipStream_t; NULL means the
  *     null stream) and returns without waiting for it. Every argument error is
  *     detected and returned before anything is enqueued; nothing is launched
@@ -109,6 +109,20 @@ gdn_status gdn_forward_capture(const float *q, const float *k, const float *v,
                                const float *state_in, float *output,
                                float *state_out, float *state_capture,
                                const gdn_params *p, void *stream);
+
+/* As gdn_forward_capture with q, k, v and output in bfloat16 (the pages call
+ * bf16 variants a future addition: mlx-native 0.4.0 src/ops/gated_delta_net.rs,
+ * module doc "Dtype / precision"). Each bf16 element is the high 16 bits of an
+ * IEEE binary32 value; inputs are widened exactly to f32, all arithmetic and
+ * the state (state_in, state_out, state_capture), g and beta stay f32, and each
+ * output is rounded to nearest-even bf16 at writeback. q and k need 8-byte
+ * alignment, v and output 2-byte. state_capture may be NULL. */
+gdn_status gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *g,
+                            const float *beta, const float *state_in,
+                            uint16_t *output, float *state_out,
+                            float *state_capture, const gdn_params *p,
+                            void *stream);
 
 /* Accepted-prefix rollback for speculative decoding (mlx-native 0.21.1,
  * dispatch_gated_delta_net_decode_with_capture doc: on a partial reject the

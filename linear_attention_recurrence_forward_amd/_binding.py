@@ -31,8 +31,9 @@ STATUS = {
 }
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
-EXPORTS = ("gdn_check_params", "gdn_forward", "gdn_forward_capture", "gdn_rollback",
-           "gdn_status_string")
+EXPORTS = ("gdn_check_params", "gdn_forward", "gdn_forward_bf16", "gdn_forward_capture",
+           "gdn_rollback", "gdn_status_string")
+IO_ARRAYS = ("q", "k", "v", "output")  # the arrays gdn_forward_bf16 takes in bf16
 
 
 class GdnParams(ctypes.Structure):
@@ -84,6 +85,9 @@ def _load():
             lib.gdn_forward.restype = ctypes.c_int
             lib.gdn_forward_capture.argtypes = [fp] * 9 + [p, ctypes.c_void_p]
             lib.gdn_forward_capture.restype = ctypes.c_int
+            vp = ctypes.c_void_p
+            lib.gdn_forward_bf16.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, p, vp]
+            lib.gdn_forward_bf16.restype = ctypes.c_int
             lib.gdn_rollback.argtypes = [fp, ctypes.POINTER(ctypes.c_uint32), fp, p,
                                          ctypes.c_void_p]
             lib.gdn_rollback.restype = ctypes.c_int
@@ -127,14 +131,16 @@ def _ptr(t):
     return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float))
 
 
-def _check_tensors(where: str, params: GdnParams, tensors: dict):
+def _check_tensors(where: str, params: GdnParams, tensors: dict, io=torch.float32):
     counts = params.counts()
     device = None
     for name, t in tensors.items():
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{where}: {name} must be a torch.Tensor")
-        if t.dtype != torch.float32:
-            raise ValueError(f"{where}: {name} must be f32 (got {t.dtype})")
+        want = io if name in IO_ARRAYS else torch.float32
+        if t.dtype != want:
+            kind = "bf16" if want == torch.bfloat16 else "f32"
+            raise ValueError(f"{where}: {name} must be {kind} (got {t.dtype})")
         if t.device.type != "cuda":
             raise ValueError(f"{where}: {name} must be on the GPU (got {t.device})")
         if device is None:
@@ -190,6 +196,29 @@ def gdn_forward_capture(q, k, v, g, beta, state_in, output, state_out, state_cap
         raise GdnError(st, "gdn_forward_capture")
 
 
+def gdn_forward_bf16(q, k, v, g, beta, state_in, output, state_out, state_capture,
+                     params: GdnParams, stream=None) -> None:
+    """Enqueue one forward call with bf16 q, k, v and output (C:
+    gdn_forward_bf16); g, beta and the state stay f32. state_capture may be
+    None."""
+    tensors = dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in, output=output,
+                   state_out=state_out)
+    if state_capture is not None:
+        tensors["state_capture"] = state_capture
+    lib = _load()
+    st = lib.gdn_check_params(ctypes.byref(params))
+    if st != 0:
+        raise GdnError(st, "gdn_forward_bf16")
+    device = _check_tensors("gdn_forward_bf16", params, tensors, io=torch.bfloat16)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = lib.gdn_forward_bf16(ptr(q), ptr(k), ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                              ptr(output), _ptr(state_out),
+                              _ptr(state_capture) if state_capture is not None else None,
+                              ctypes.byref(params), _stream_handle(device, stream))
+    if st != 0:
+        raise GdnError(st, "gdn_forward_bf16")
+
+
 def gdn_rollback(state_capture, accepted, state, params: GdnParams, stream=None) -> None:
     """Enqueue the accepted-prefix rollback (C: gdn_rollback): for each
     sequence s with accepted[s] < n_tokens, state[s] = state_capture[s,
@@ -219,19 +248,26 @@ def forward(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0, capture: bool 
             output=None, state_out=None, state_capture=None, stream=None):
     """Convenience wrapper on torch-shaped tensors:
     q, k (S, T, H_k, D_k); v (S, T, H_v, D_v); g, beta (S, T, H_v);
-    state_in (S, H_v, D_v, D_k). Allocates missing outputs and returns
-    (output, state_out) or (output, state_out, state_capture)."""
+    state_in (S, H_v, D_v, D_k). q, k, v in f32, or all three in bf16 (then the
+    output is bf16 too; the state is f32 either way). Allocates missing outputs
+    and returns (output, state_out) or (output, state_out, state_capture)."""
     params = params_for(q, v, q_scale_bits)
     S, T, Hv, Dv = v.shape
     Dk = q.shape[3]
+    bf16 = q.dtype == torch.bfloat16
     if output is None:
-        output = torch.empty((S, T, Hv, Dv), dtype=torch.float32, device=q.device)
+        output = torch.empty((S, T, Hv, Dv), dtype=q.dtype if bf16 else torch.float32,
+                             device=q.device)
     if state_out is None:
         state_out = torch.empty((S, Hv, Dv, Dk), dtype=torch.float32, device=q.device)
+    if capture and state_capture is None:
+        state_capture = torch.empty((S, T, Hv, Dv, Dk), dtype=torch.float32,
+                                    device=q.device)
+    if bf16:
+        gdn_forward_bf16(q, k, v, g, beta, state_in, output, state_out,
+                         state_capture if capture else None, params, stream)
+        return (output, state_out, state_capture) if capture else (output, state_out)
     if capture:
-        if state_capture is None:
-            state_capture = torch.empty((S, T, Hv, Dv, Dk), dtype=torch.float32,
-                                        device=q.device)
         gdn_forward_capture(q, k, v, g, beta, state_in, output, state_out, state_capture,
                             params, stream)
         return output, state_out, state_capture

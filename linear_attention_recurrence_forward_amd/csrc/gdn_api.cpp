@@ -42,9 +42,9 @@ struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
 
-Range range_of(const void *p, uint64_t elems) {
+Range range_of(const void *p, uint64_t elems, uint64_t elem_bytes = sizeof(float)) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return Range{lo, lo + (uintptr_t)(elems * sizeof(float))};
+  return Range{lo, lo + (uintptr_t)(elems * elem_bytes)};
 }
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
@@ -53,27 +53,33 @@ bool aligned(const void *p, uintptr_t n) {
   return (reinterpret_cast<uintptr_t>(p) % n) == 0;
 }
 
-gdn_status forward(const float *q, const float *k, const float *v,
-                   const float *g, const float *beta, const float *state_in,
-                   float *output, float *state_out, float *capture,
-                   const gdn_params *p, void *stream) {
+// Shared by the f32 and bf16 entry points. io_bytes is the element size of q,
+// k, v and output (4 for f32, 2 for bf16); the state, capture, g and beta
+// arrays are always f32.
+gdn_status forward(const void *q, const void *k, const void *v, const float *g,
+                   const float *beta, const float *state_in, void *output,
+                   float *state_out, float *capture, const gdn_params *p,
+                   void *stream, uint32_t io_bytes) {
   gdn_status st = gdn_check_params(p);
   if (st != GDN_OK) return st;
   if (!q || !k || !v || !g || !beta || !state_in || !output || !state_out)
     return GDN_ERR_NULL_POINTER;
 
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state_in, 16) ||
+  // q and k are read as vectors of four elements, the state as 4-float
+  // vectors; v and output element by element.
+  const uintptr_t vec = 4 * io_bytes;
+  if (!aligned(q, vec) || !aligned(k, vec) || !aligned(state_in, 16) ||
       !aligned(state_out, 16) || (capture && !aligned(capture, 16)) ||
-      !aligned(v, 4) || !aligned(g, 4) || !aligned(beta, 4) ||
-      !aligned(output, 4))
+      !aligned(v, io_bytes) || !aligned(g, 4) || !aligned(beta, 4) ||
+      !aligned(output, io_bytes))
     return GDN_ERR_MISALIGNED;
 
   Counts c;
   counts_of(p, &c);  // cannot fail after gdn_check_params
-  const Range inputs[] = {range_of(q, c.qk),        range_of(k, c.qk),
-                          range_of(v, c.v),         range_of(g, c.scalar),
-                          range_of(beta, c.scalar), range_of(state_in, c.state)};
-  const Range r_out = range_of(output, c.v);
+  const Range inputs[] = {range_of(q, c.qk, io_bytes), range_of(k, c.qk, io_bytes),
+                          range_of(v, c.v, io_bytes),  range_of(g, c.scalar),
+                          range_of(beta, c.scalar),    range_of(state_in, c.state)};
+  const Range r_out = range_of(output, c.v, io_bytes);
   const Range r_state = range_of(state_out, c.state);
   const Range r_cap = range_of(capture, capture ? c.capture : 0);
   for (int i = 0; i < 6; ++i) {
@@ -106,6 +112,7 @@ gdn_status forward(const float *q, const float *k, const float *v,
   a.n_tokens = p->n_tokens;
   a.n_seqs = p->n_seqs;
   a.q_scale = q_scale;
+  a.bf16 = io_bytes == 2;
   if (gdn::enqueue_forward(a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GDN_ERR_LAUNCH;
   return GDN_OK;
@@ -170,7 +177,7 @@ gdn_status gdn_forward(const float *q, const float *k, const float *v,
                        const float *state_in, float *output, float *state_out,
                        const gdn_params *p, void *stream) {
   return forward(q, k, v, g, beta, state_in, output, state_out, nullptr, p,
-                 stream);
+                 stream, 4);
 }
 
 gdn_status gdn_forward_capture(const float *q, const float *k, const float *v,
@@ -179,7 +186,17 @@ gdn_status gdn_forward_capture(const float *q, const float *k, const float *v,
                                float *state_out, float *state_capture,
                                const gdn_params *p, void *stream) {
   return forward(q, k, v, g, beta, state_in, output, state_out, state_capture,
-                 p, stream);
+                 p, stream, 4);
+}
+
+gdn_status gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *g,
+                            const float *beta, const float *state_in,
+                            uint16_t *output, float *state_out,
+                            float *state_capture, const gdn_params *p,
+                            void *stream) {
+  return forward(q, k, v, g, beta, state_in, output, state_out, state_capture,
+                 p, stream, 2);
 }
 
 const char *gdn_status_string(gdn_status s) {
@@ -192,7 +209,7 @@ const char *gdn_status_string(gdn_status s) {
     case GDN_ERR_UNSUPPORTED_DK: return "d_k must be 32, 64 or 128";
     case GDN_ERR_RESERVED_NONZERO: return "params words 6 and 7 are reserved and must be 0";
     case GDN_ERR_SIZE_OVERFLOW: return "array sizes or launch grid exceed 64-bit/32-bit limits";
-    case GDN_ERR_MISALIGNED: return "q, k, state and capture arrays need 16-byte alignment; v, g, beta, output 4-byte";
+    case GDN_ERR_MISALIGNED: return "an array breaks the alignment rule (f32: q, k, state, capture 16 bytes; bf16: q, k 8 bytes; every array its element size)";
     case GDN_ERR_ALIASING: return "an output array overlaps another array (only state_out == state_in is allowed)";
     case GDN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
   }

@@ -91,8 +91,8 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
 // Descriptor over `bytes` bytes from `base` (bytes < 2^32).
-__device__ __forceinline__ rsrc_t buffer(const float *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes,
+__device__ __forceinline__ rsrc_t buffer(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes,
                                            kBufferWord3);
 }
 
@@ -111,9 +111,8 @@ __device__ __forceinline__ P *uniform(P *p) {
   return reinterpret_cast<P *>((hi << 32) | lo);
 }
 
-// Descriptor size for `elems` floats, clamped to the 32-bit size field.
-__device__ __forceinline__ uint32_t extent(uint64_t elems) {
-  const uint64_t bytes = elems * 4;
+// Descriptor size for `bytes` bytes, clamped to the 32-bit size field.
+__device__ __forceinline__ uint32_t extent_bytes(uint64_t bytes) {
   return bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
 }
 
@@ -139,9 +138,58 @@ __device__ __forceinline__ void store4_stream(rsrc_t r, uint32_t byte_off, f4 x)
                                          0, kNonTemporal);
 }
 
+// Element access for the arrays that take the caller's I/O type (q, k, v,
+// output): f32, or bf16 widened exactly to f32 on load (the 16 bits become
+// the high half of the f32) and rounded to nearest-even on store. State,
+// capture, g and beta are always f32.
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+template <typename IO>
+struct Io;
+
+template <>
+struct Io<float> {
+  static constexpr uint32_t bytes = 4;
+  static __device__ __forceinline__ f4 load4(rsrc_t r, uint32_t off, uint32_t soff) {
+    return ::gdn::load4(r, off, soff);
+  }
+  static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off, uint32_t soff) {
+    return ::gdn::load1(r, off, soff);
+  }
+  static __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, uint32_t soff,
+                                                float x) {
+    ::gdn::store1(r, off, soff, x);
+  }
+};
+
+template <>
+struct Io<__bf16> {
+  static constexpr uint32_t bytes = 2;
+  static __device__ __forceinline__ float widen(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+  }
+  static __device__ __forceinline__ f4 load4(rsrc_t r, uint32_t off, uint32_t soff) {
+    const u2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    return f4{__builtin_bit_cast(float, w.x << 16),
+              __builtin_bit_cast(float, w.x & 0xFFFF0000u),
+              __builtin_bit_cast(float, w.y << 16),
+              __builtin_bit_cast(float, w.y & 0xFFFF0000u)};
+  }
+  static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off, uint32_t soff) {
+    return widen(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
+  }
+  static __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, uint32_t soff,
+                                                float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(
+        __builtin_bit_cast(unsigned short, static_cast<__bf16>(x)), r, off, soff, 0);
+  }
+};
+
 struct KernelArgs {
-  const float *q, *k, *v, *g, *beta, *state_in;
-  float *output, *state_out, *capture;
+  const void *q, *k, *v;  // IO type
+  const float *g, *beta, *state_in;
+  void *output;           // IO type
+  float *state_out, *capture;
   uint32_t d_v, n_k_heads, n_v_heads, n_tokens;
   uint32_t row_blocks;  // workgroups per (sequence, value head)
   float q_scale;
@@ -150,15 +198,17 @@ struct KernelArgs {
 // DK: key dim. C: cells per lane per row. R: rows per lane. WAVES: waves per
 // workgroup. NB: token buffers in the prefetch ring (token t + NB - 1 is
 // requested while token t computes); NB = 1 selects the one-token path, used
-// only for n_tokens == 1. CAPTURE: also write the per-token state.
-template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE>
+// only for n_tokens == 1. CAPTURE: also write the per-token state. IO: element
+// type of q, k, v and output (float or __bf16).
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO>
 __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   constexpr int L = DK / C;      // lanes sharing one state row
   constexpr int G = 64 / L;      // row groups per wave
   constexpr int NV = C / 4;      // float4 vectors per lane per row
   constexpr int ROWS_PER_WAVE = G * R;
   constexpr int ROWS = WAVES * ROWS_PER_WAVE;
-  constexpr uint32_t ROW_BYTES = DK * 4;
+  constexpr uint32_t ROW_BYTES = DK * 4;       // one f32 state row
+  constexpr uint32_t IB = Io<IO>::bytes;       // bytes per q/k/v/output element
   static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
   static_assert(R <= L, "one output lane per row");
 
@@ -195,11 +245,11 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // row of k/q (D_k floats), v/output (D_v floats) or capture (D_v x D_k).
   // The host guarantees d_v * d_k * 4 < 2^32.
   const uint64_t tok0 = (uint64_t)s * T;                   // first token of s
-  const float *k_tok = a.k + (tok0 * Hk + kh) * DK;
-  const float *q_tok = a.q + (tok0 * Hk + kh) * DK;
+  const char *k_tok = static_cast<const char *>(a.k) + ((tok0 * Hk + kh) * DK) * IB;
+  const char *q_tok = static_cast<const char *>(a.q) + ((tok0 * Hk + kh) * DK) * IB;
   const uint64_t kq_step = Hk * DK;
-  const float *v_tok = a.v + (tok0 * Hv + vh) * Dv;
-  float *o_tok = a.output + (tok0 * Hv + vh) * Dv;
+  const char *v_tok = static_cast<const char *>(a.v) + ((tok0 * Hv + vh) * Dv) * IB;
+  char *o_tok = static_cast<char *>(a.output) + ((tok0 * Hv + vh) * Dv) * IB;
   const uint64_t v_step = Hv * Dv;
   const float *g_tok = a.g + tok0 * Hv + vh;
   const float *b_tok = a.beta + tok0 * Hv + vh;
@@ -210,14 +260,14 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   const rsrc_t s_out = buffer(a.state_out + (uint64_t)hs * Dv * DK, head_bytes);
 
   // Per-lane byte offsets, fixed for the whole call: vector m of row r starts
-  // at column m*4L + 4*sub.
-  const uint32_t col = 16 * sub;
+  // at column m*4L + 4*sub (state: 16 bytes per vector; k/q: 4*IB bytes).
+  const uint32_t col = 16 * sub, col_io = 4 * IB * sub;
   uint32_t cell[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) cell[r] = row[r] * ROW_BYTES + col;
   uint32_t vrow[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) vrow[r] = row[r] * 4;
+  for (int r = 0; r < R; ++r) vrow[r] = row[r] * IB;
   // Outputs are written L tokens at a time: lane sub of a row group keeps
   // the row's output of token t0 + sub (t0 a multiple of L) in yk, and one
   // store per row writes the L tokens. Stores share the in-order memory
@@ -229,7 +279,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     yk[r] = 0.f;
-    yoff[r] = vrow[r] + sub * (uint32_t)(Hv * Dv * 4);
+    yoff[r] = vrow[r] + sub * (uint32_t)(Hv * Dv * IB);
   }
 
   f4 st[R][NV];
@@ -246,19 +296,19 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // that reach to the end of this sequence; token t's row is at scalar byte
   // offset (t - base_t) * stride. Rebased every 64 tokens, so the scalar
   // offsets stay far below 2^32 (the host bounds the per-token strides).
-  const uint32_t kq_bytes = (uint32_t)kq_step * 4, v_bytes = (uint32_t)v_step * 4;
+  const uint32_t kq_bytes = (uint32_t)kq_step * IB, v_bytes = (uint32_t)v_step * IB;
   uint32_t base_t = 0, kq_ext = 0, v_ext = 0;
-  const float *k_b = nullptr, *q_b = nullptr, *v_b = nullptr;
-  float *o_b = nullptr;
+  const char *k_b = nullptr, *q_b = nullptr, *v_b = nullptr;
+  char *o_b = nullptr;
   auto rebase = [&](uint32_t t0) {
     base_t = uniform(t0);
     const uint64_t rest = T - t0 - 1;  // tokens after t0
-    k_b = uniform(k_tok + t0 * kq_step);
-    q_b = uniform(q_tok + t0 * kq_step);
-    v_b = uniform(v_tok + t0 * v_step);
-    o_b = uniform(o_tok + t0 * v_step);
-    kq_ext = uniform(extent(rest * kq_step + DK));
-    v_ext = uniform(extent(rest * v_step + Dv));
+    k_b = uniform(k_tok + t0 * kq_step * IB);
+    q_b = uniform(q_tok + t0 * kq_step * IB);
+    v_b = uniform(v_tok + t0 * v_step * IB);
+    o_b = uniform(o_tok + t0 * v_step * IB);
+    kq_ext = uniform(extent_bytes((rest * kq_step + DK) * IB));
+    v_ext = uniform(extent_bytes((rest * v_step + Dv) * IB));
   };
   rebase(0);
 
@@ -269,11 +319,11 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     const rsrc_t v_rs = buffer(v_b, v_ext);
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
-      x.k[m] = load4(k_rs, col + m * 16 * L, kq_off);
-      x.q[m] = load4(q_rs, col + m * 16 * L, kq_off);
+      x.k[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, kq_off);
+      x.q[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, kq_off);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) x.v[r] = load1(v_rs, vrow[r], v_off);
+    for (int r = 0; r < R; ++r) x.v[r] = Io<IO>::load1(v_rs, vrow[r], v_off);
   };
 
   auto step = [&](uint32_t t, const Tok &x, float alpha, float b) {
@@ -314,7 +364,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       if (sub <= (t & (TB - 1)))
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          if (ok[r]) store1(o_rs, yoff[r], soff, yk[r]);
+          if (ok[r]) Io<IO>::store1(o_rs, yoff[r], soff, yk[r]);
     }
     if constexpr (CAPTURE) {
       const rsrc_t ct = buffer(c_tok + t * cap_step, head_bytes);
@@ -408,11 +458,11 @@ struct Geometry {
   const void *kernel;
 };
 
-template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE>
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO>
 constexpr Geometry make_geometry() {
   return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
                   reinterpret_cast<const void *>(
-                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE>)};
+                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO>)};
 }
 
 // Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
@@ -426,33 +476,35 @@ constexpr Geometry make_geometry() {
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
 //                tokens against one row per lane), 16 lanes per row, 4 waves,
 //                a four-token prefetch ring.
-template <bool CAPTURE>
+template <bool CAPTURE, typename IO>
 Geometry pick(uint32_t d_k, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
   switch (d_k) {
     case 32:
-      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE>()
-                       : make_geometry<32, 4, 2, 4, 4, CAPTURE>();
+      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE, IO>()
+                       : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO>();
     case 64:
-      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE>()
-                       : make_geometry<64, 4, 2, 4, 4, CAPTURE>();
+      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO>()
+                       : make_geometry<64, 4, 2, 4, 4, CAPTURE, IO>();
     case 128:
-      return one_token ? make_geometry<128, 8, 1, 4, 1, CAPTURE>()
-                       : make_geometry<128, 8, 2, 4, 4, CAPTURE>();
+      return one_token ? make_geometry<128, 8, 1, 4, 1, CAPTURE, IO>()
+                       : make_geometry<128, 8, 2, 4, 4, CAPTURE, IO>();
     default:
       return Geometry{0, 0, nullptr};
   }
 }
 
-Geometry pick_geometry(uint32_t d_k, uint32_t n_tokens, bool capture) {
-  return capture ? pick<true>(d_k, n_tokens) : pick<false>(d_k, n_tokens);
+Geometry pick_geometry(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16) {
+  if (bf16)
+    return capture ? pick<true, __bf16>(d_k, n_tokens) : pick<false, __bf16>(d_k, n_tokens);
+  return capture ? pick<true, float>(d_k, n_tokens) : pick<false, float>(d_k, n_tokens);
 }
 
 }  // namespace
 
 uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
                      uint32_t n_seqs, uint32_t n_tokens, bool capture) {
-  const Geometry geo = pick_geometry(d_k, n_tokens, capture);
+  const Geometry geo = pick_geometry(d_k, n_tokens, capture, false);
   if (geo.kernel == nullptr) return 0;
   const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
   return row_blocks * n_v_heads * n_seqs;
@@ -460,7 +512,7 @@ uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
 
 hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   const bool capture = f.capture != nullptr;
-  const Geometry geo = pick_geometry(f.d_k, f.n_tokens, capture);
+  const Geometry geo = pick_geometry(f.d_k, f.n_tokens, capture, f.bf16);
   if (geo.kernel == nullptr) return hipErrorInvalidValue;
   const uint32_t row_blocks =
       (f.d_v + geo.rows_per_block - 1) / geo.rows_per_block;

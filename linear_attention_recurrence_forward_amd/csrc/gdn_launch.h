@@ -8,12 +8,16 @@
 namespace gdn {
 
 // Validated arguments of one forward call. Pointers are device memory in the
-// innermost-first layouts of include/gdn.h; capture may be null.
+// innermost-first layouts of include/gdn.h; capture may be null. q, k, v and
+// output hold f32, or bf16 when bf16 is set.
 struct ForwardArgs {
-  const float *q, *k, *v, *g, *beta, *state_in;
-  float *output, *state_out, *capture;
+  const void *q, *k, *v;
+  const float *g, *beta, *state_in;
+  void *output;
+  float *state_out, *capture;
   uint32_t d_k, d_v, n_k_heads, n_v_heads, n_tokens, n_seqs;
   float q_scale;
+  bool bf16;
 };
 
 // Number of workgroups the chosen launch geometry needs (for the host-side

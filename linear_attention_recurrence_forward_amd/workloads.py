@@ -71,16 +71,16 @@ class Workload:
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
 
-    def algorithmic_bytes(self) -> int:
+    def algorithmic_bytes(self, io_bytes: int = 4) -> int:
         """Bytes the step must move once: state read and written, q and k read
         once per k-head, v, g, beta read and output written once, capture
-        written once when present."""
+        written once when present. io_bytes is the element size of q, k, v and
+        output (4 for f32, 2 for bf16); everything else is f32."""
         S, T = self.n_seqs, self.n_tokens
         state = self.d_k * self.d_v * self.n_v_heads * S
-        per_token = (2 * self.d_k * self.n_k_heads + 2 * self.d_v * self.n_v_heads
-                     + 2 * self.n_v_heads)
+        io = 2 * self.d_k * self.n_k_heads + 2 * self.d_v * self.n_v_heads
         cap = T * state if self.capture else 0
-        return 4 * (2 * state + T * S * per_token + cap)
+        return 4 * (2 * state + T * S * 2 * self.n_v_heads + cap) + io_bytes * T * S * io
 
     def state_bytes(self) -> int:
         return 4 * 2 * self.d_k * self.d_v * self.n_v_heads * self.n_seqs

@@ -5,6 +5,8 @@ CPU-baseline leg use it. The product path (the HIP library and its binding)
 never imports it.
 """
 
-from .gdn_oracle import HEAD_MAP_DIV, HEAD_MAP_MOD, build, reference, rollback
+from .gdn_oracle import (HEAD_MAP_DIV, HEAD_MAP_MOD, build, reference, reference_bf16,
+                         rollback, to_bf16)
 
-__all__ = ["HEAD_MAP_DIV", "HEAD_MAP_MOD", "build", "reference", "rollback"]
+__all__ = ["HEAD_MAP_DIV", "HEAD_MAP_MOD", "build", "reference", "reference_bf16",
+           "rollback", "to_bf16"]

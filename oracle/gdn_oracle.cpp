@@ -159,6 +159,27 @@ int run(const float *q, const float *k, const float *v, const float *g,
   return 0;
 }
 
+// bfloat16 is the top half of an IEEE binary32 value (sign, 8 exponent bits,
+// 7 fraction bits). Widening is exact; narrowing rounds to nearest, ties to
+// even on the 16 dropped bits; NaN stays NaN (quiet, sign kept).
+float bf16_to_f32(uint16_t h) {
+  const uint32_t bits = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+uint16_t f32_to_bf16(float f) {
+  uint32_t bits;
+  std::memcpy(&bits, &f, sizeof bits);
+  if ((bits & 0x7FFFFFFFu) > 0x7F800000u)  // NaN
+    return (uint16_t)((bits >> 16) | 0x0040u);
+  const uint32_t dropped = bits & 0xFFFFu;
+  uint32_t kept = bits >> 16;
+  if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1;
+  return (uint16_t)kept;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +200,39 @@ int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
                            double *state_capture) {
   return run<double>(q, k, v, g, beta, state_in, p, head_map, output,
                      state_out, state_capture);
+}
+
+// bf16 inputs and output (the "future add" of mlx-native 0.4.0
+// src/ops/gated_delta_net.rs, module doc "Dtype / precision"): q, k, v are
+// widened exactly, the recurrence runs in f32 as above, and each output is
+// rounded to the nearest bf16. State and capture stay f32.
+int oracle_gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *g,
+                            const float *beta, const float *state_in,
+                            const oracle_gdn_shape *p, int head_map,
+                            uint16_t *output, float *state_out,
+                            float *state_capture) {
+  if (p == nullptr || q == nullptr || k == nullptr || v == nullptr ||
+      output == nullptr)
+    return 1;
+  const uint64_t nqk = (uint64_t)p->d_k * p->n_k_heads * p->n_tokens * p->n_seqs;
+  const uint64_t nv = (uint64_t)p->d_v * p->n_v_heads * p->n_tokens * p->n_seqs;
+  std::vector<float> qf(nqk), kf(nqk), vf(nv), of(nv);
+  for (uint64_t e = 0; e < nqk; ++e) {
+    qf[e] = bf16_to_f32(q[e]);
+    kf[e] = bf16_to_f32(k[e]);
+  }
+  for (uint64_t e = 0; e < nv; ++e) vf[e] = bf16_to_f32(v[e]);
+  const int rc = run<float>(qf.data(), kf.data(), vf.data(), g, beta, state_in,
+                            p, head_map, of.data(), state_out, state_capture);
+  if (rc != 0) return rc;
+  for (uint64_t e = 0; e < nv; ++e) output[e] = f32_to_bf16(of[e]);
+  return 0;
+}
+
+// The oracle's f32 -> bf16 rounding on its own, for the pins.
+void oracle_f32_to_bf16(const float *in, uint16_t *out, uint64_t n) {
+  for (uint64_t e = 0; e < n; ++e) out[e] = f32_to_bf16(in[e]);
 }
 
 // Accepted-prefix rollback (mlx-native 0.21.1,

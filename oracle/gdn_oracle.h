@@ -45,6 +45,19 @@ int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
                            int head_map, double *output, double *state_out,
                            double *state_capture);
 
+/* bf16 q, k, v and output (raw 16-bit patterns); g, beta, state and capture
+ * f32. Inputs widened exactly, f32 recurrence, output rounded to nearest-even
+ * bf16 (NaN kept as a quiet NaN). */
+int oracle_gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *g,
+                            const float *beta, const float *state_in,
+                            const oracle_gdn_shape *p, int head_map,
+                            uint16_t *output, float *state_out,
+                            float *state_capture);
+
+/* The oracle's f32 -> bf16 rounding alone (round to nearest, ties to even). */
+void oracle_f32_to_bf16(const float *in, uint16_t *out, uint64_t n);
+
 /* Accepted-prefix rollback: state[s] = state_capture[s, accepted[s]] for every
  * sequence whose accepted[s] < n_tokens (others untouched). Uses d_k, d_v,
  * n_v_heads, n_tokens, n_seqs of p. */

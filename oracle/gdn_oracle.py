@@ -70,6 +70,16 @@ def _load(path: str | None = None):
                 fn.argtypes = [fp] * 6 + [ctypes.POINTER(_Shape), ctypes.c_int,
                                           rp, rp, rp]
                 fn.restype = ctypes.c_int
+            if hasattr(lib, "oracle_gdn_forward_bf16"):
+                u16 = ctypes.POINTER(ctypes.c_uint16)
+                fn = lib.oracle_gdn_forward_bf16
+                fn.argtypes = [u16, u16, u16] + [ctypes.POINTER(ctypes.c_float)] * 3 + [
+                    ctypes.POINTER(_Shape), ctypes.c_int, u16,
+                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]
+                fn.restype = ctypes.c_int
+                lib.oracle_f32_to_bf16.argtypes = [ctypes.POINTER(ctypes.c_float), u16,
+                                                   ctypes.c_uint64]
+                lib.oracle_f32_to_bf16.restype = None
             if hasattr(lib, "oracle_gdn_rollback"):
                 fn = lib.oracle_gdn_rollback
                 fn.argtypes = [ctypes.POINTER(ctypes.c_float),
@@ -146,3 +156,38 @@ def rollback(state_capture, accepted, state, *, library: str | None = None):
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return out
+
+
+def to_bf16(x, *, library: str | None = None):
+    """The oracle's f32 -> bf16 rounding: uint16 bit patterns of x's elements."""
+    a = _f32(x)
+    out = np.empty(a.shape, np.uint16)
+    _load(library).oracle_f32_to_bf16(_ptr(a, ctypes.c_float),
+                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                      a.size)
+    return out
+
+
+def reference_bf16(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
+                   head_map: int = HEAD_MAP_MOD, capture: bool = False,
+                   library: str | None = None):
+    """bf16 variant: q, k, v are uint16 bf16 bit patterns (shapes as in
+    reference); returns (output as uint16 bf16 bits, state_out f32[, capture])."""
+    q16, k16, v16 = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v))
+    g, beta, state_in = (_f32(a) for a in (g, beta, state_in))
+    S, T, Hk, Dk = q16.shape
+    Hv, Dv = v16.shape[2], v16.shape[3]
+    out = np.empty((S, T, Hv, Dv), np.uint16)
+    st = np.empty((S, Hv, Dv, Dk), np.float32)
+    cap = np.empty((S, T, Hv, Dv, Dk), np.float32) if capture else None
+    shape = _Shape(Dk, Dv, Hk, Hv, T, S, q_scale_bits & 0xFFFFFFFF)
+    u16 = ctypes.POINTER(ctypes.c_uint16)
+    fp = ctypes.c_float
+    rc = _load(library).oracle_gdn_forward_bf16(
+        q16.ctypes.data_as(u16), k16.ctypes.data_as(u16), v16.ctypes.data_as(u16),
+        _ptr(g, fp), _ptr(beta, fp), _ptr(state_in, fp), ctypes.byref(shape), head_map,
+        out.ctypes.data_as(u16), _ptr(st, fp),
+        _ptr(cap, fp) if cap is not None else ctypes.POINTER(fp)())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return (out, st, cap) if capture else (out, st)

@@ -350,6 +350,59 @@ def pin_rollback(ref, rollback=None):
                  "rollback to the last token == state_out")
 
 
+def golden_bf16_rounding(ref, to_bf16=None):
+    """The oracle's f32 -> bf16 rounding against the hand-worked table
+    (tests/golden/bf16_rounding.json)."""
+    import oracle
+    to_bf16 = to_bf16 or oracle.to_bf16
+    with open(os.path.join(GOLDEN, "bf16_rounding.json")) as f:
+        fx = json.load(f)
+    vals = np.array([np.uint32(int(c["f32_bits"], 16)).view(np.float32) if "f32_bits" in c
+                     else np.float32(float(c["f32"])) for c in fx["cases"]], np.float32)
+    want = np.array([int(c["bf16"], 16) for c in fx["cases"]], np.uint16)
+    got = to_bf16(vals)
+    for c, g_, w_ in zip(fx["cases"], got, want):
+        assert g_ == w_, (f"bf16 rounding of {c.get('f32', c.get('f32_bits'))}: "
+                          f"{g_:#06x} != {w_:#06x} ({c['why']})")
+
+
+def bf16_bits_exact(x):
+    """uint16 patterns of float values that bf16 holds exactly (small integers)."""
+    return (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pin_bf16(ref, ref_bf16=None):
+    """bf16 inputs and output: the head-map and linear-attention probes are
+    exact in bf16 too (small integers), and on random inputs the state is the
+    f32 path's state on the widened inputs, bit for bit."""
+    import oracle
+    ref_bf16 = ref_bf16 or oracle.reference_bf16
+    S, T, Hk, Hv, Dk, Dv = 1, 6, 2, 4, 32, 8
+    rng = np.random.default_rng(12)
+    k = np.zeros((S, T, Hk, Dk), np.float32)
+    for t in range(T):
+        k[:, t, :, t] = 1.0
+    q = rng.integers(-4, 5, size=(S, T, Hk, Dk)).astype(np.float32)
+    v = rng.integers(-4, 5, size=(S, T, Hv, Dv)).astype(np.float32)
+    z = np.zeros((S, T, Hv), np.float32)
+    s0 = np.zeros((S, Hv, Dv, Dk), np.float32)
+    out16, st = ref_bf16(bf16_bits_exact(q), bf16_bits_exact(k), bf16_bits_exact(v),
+                         z, z + 1, s0)
+    out32, st32 = ref(q=q, k=k, v=v, g=z, beta=z + 1, state_in=s0)
+    assert_equal(st, st32, "bf16 probe state")
+    assert_equal(out16, bf16_bits_exact(out32), "bf16 probe output (small integers)")
+    x = gqa_inputs(113)
+    q16, k16, v16 = (bf16_bits_exact(x[n]) for n in ("q", "k", "v"))
+    wide = {n: (a.astype(np.uint32) << 16).view(np.float32)
+            for n, a in (("q", q16), ("k", k16), ("v", v16))}
+    o16, s16 = ref_bf16(q16, k16, v16, x["g"], x["beta"], x["state_in"])
+    o32, s32 = ref(**dict(x, **wide))
+    assert_equal(s16, s32, "bf16 path state == f32 path state on widened inputs")
+    lo = (o16.astype(np.uint32) << 16).view(np.float32)
+    # |fl_bf16(y) - y| <= half a bf16 step: 2^-8 relative to |y|
+    assert_within(lo, o32, 2.0 ** -8 * np.abs(o32) + 1e-30, "bf16 output rounding")
+
+
 def golden_hand_worked(ref):
     """Hand-derived dyadic example (tests/golden/hand_worked_d2.json), bit-exact."""
     with open(os.path.join(GOLDEN, "hand_worked_d2.json")) as f:
@@ -367,4 +420,5 @@ def golden_hand_worked(ref):
 
 ALL_PINS = [pin_identity, pin_zeroing, pin_delta_rule, pin_chaining, pin_capture,
             pin_q_scale, pin_head_map, pin_linear_attention, pin_pure_decay,
-            pin_matrix_form, pin_rollback, golden_hand_worked]
+            pin_matrix_form, pin_rollback, pin_bf16, golden_bf16_rounding,
+            golden_hand_worked]

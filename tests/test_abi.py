@@ -209,3 +209,29 @@ def test_rollback_validation(lib):
     # state inside the capture buffer, or over the index array
     assert rb(fp(cap), up(acc), fp(cap + 4 * c["state_capture"] - 64)) == "GDN_ERR_ALIASING"
     assert rb(fp(cap), up(st + 16), fp(st)) == "GDN_ERR_ALIASING"
+
+
+def test_forward_bf16_alignment(lib):
+    """bf16 q and k need 8-byte alignment, v and output 2-byte."""
+    p = gdn.make_params(**OK)
+    a = layout(p)
+    vp = lambda n, off=0: ctypes.c_void_p(a[n] + off)  # noqa: E731
+
+    def call16(**off):
+        return _binding.STATUS[lib.gdn_forward_bf16(
+            vp("q", off.get("q", 0)), vp("k", off.get("k", 0)), vp("v", off.get("v", 0)),
+            fake(a["g"]), fake(a["beta"]), fake(a["state_in"]),
+            vp("output", off.get("output", 0)), fake(a["state_out"]),
+            fake(a["state_capture"]), ctypes.byref(p), None)]
+
+    assert call16(q=4) == "GDN_ERR_MISALIGNED"
+    assert call16(k=2) == "GDN_ERR_MISALIGNED"
+    assert call16(v=1) == "GDN_ERR_MISALIGNED"
+    assert call16(output=1) == "GDN_ERR_MISALIGNED"
+    # bf16 output overlapping the bf16 v buffer's tail
+    c = p.counts()
+    b = dict(a, output=a["v"] + 2 * c["v"] - 2)
+    assert _binding.STATUS[lib.gdn_forward_bf16(
+        ctypes.c_void_p(b["q"]), ctypes.c_void_p(b["k"]), ctypes.c_void_p(b["v"]),
+        fake(b["g"]), fake(b["beta"]), fake(b["state_in"]), ctypes.c_void_p(b["output"]),
+        fake(b["state_out"]), None, ctypes.byref(p), None)] == "GDN_ERR_ALIASING"

@@ -309,6 +309,83 @@ def test_deterministic():
         assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
 
 
+# ------------------------------------------------------------------ bf16 I/O
+
+def bf16_inputs(x):
+    """Round q, k, v to bf16 with torch (independent of both paths): returns
+    (uint16 bit patterns, the same values widened to f32)."""
+    bits, wide = {}, {}
+    for n in ("q", "k", "v"):
+        t = torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16)
+        bits[n] = t.view(torch.int16).numpy().view(np.uint16).copy()
+        wide[n] = t.float().numpy()
+    return bits, wide
+
+
+def run_bf16(x, bits, *, q_scale_bits=0, capture=False):
+    d = {n: torch.from_numpy(bits[n].view(np.int16)).cuda().view(torch.bfloat16)
+         for n in ("q", "k", "v")}
+    for n in ("g", "beta", "state_in"):
+        d[n] = torch.from_numpy(np.ascontiguousarray(x[n])).cuda()
+    res = gdn.forward(*(d[n] for n in NAMES), q_scale_bits=q_scale_bits, capture=capture)
+    torch.cuda.synchronize()
+    out = res[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    return (out,) + tuple(r.cpu().numpy() for r in res[1:])
+
+
+def widen(bits16):
+    return (bits16.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_close(got16, exp16, what):
+    """Within one bf16 step (2^-7 relative) plus abs 1e-5: both sides round
+    f32 values that differ only by reduction order."""
+    e = widen(exp16).astype(np.float64)
+    assert_within(widen(got16), e, 2.0 ** -7 * np.abs(e) + 1e-5, what)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_bf16_workload_parity(name):
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    bits, wide = bf16_inputs(x)
+    bq = x["q_scale_bits"]
+    got = run_bf16(x, bits, q_scale_bits=bq, capture=w.capture)
+    exp = oracle.reference_bf16(bits["q"], bits["k"], bits["v"], x["g"], x["beta"],
+                                x["state_in"], q_scale_bits=bq, capture=w.capture)
+    bf16_close(got[0], exp[0], f"{name} bf16 output vs oracle")
+    close(got[1], exp[1], f"{name} bf16 state_out vs oracle")
+    if w.capture:
+        close(got[2], exp[2], f"{name} bf16 capture vs oracle")
+        assert_equal(got[2][:, -1], got[1], "capture[T-1] == state_out")
+    # Against the GPU's own f32 path on the widened inputs: same arithmetic,
+    # so the state agrees bit for bit and the output is its bf16 rounding.
+    f32 = run(dict(x, **wide), q_scale_bits=bq, capture=w.capture)
+    assert_equal(got[1], f32[1], f"{name} bf16 state == f32-path state")
+    want = torch.from_numpy(f32[0]).to(torch.bfloat16).view(torch.int16).numpy()
+    assert_equal(got[0], want.view(np.uint16), f"{name} bf16 output == rounded f32 output")
+
+
+def test_bf16_exact_probe():
+    """Orthogonal keys and small integers: exact in bf16 end to end."""
+    S, T, Hk, Hv, Dk, Dv = 2, 20, 2, 4, 128, 40
+    rng = np.random.default_rng(9)
+    k = np.zeros((S, T, Hk, Dk), np.float32)
+    for t in range(T):
+        k[:, t, :, t] = 1.0
+    x = dict(q=rng.integers(-3, 4, size=(S, T, Hk, Dk)).astype(np.float32), k=k,
+             v=rng.integers(-3, 4, size=(S, T, Hv, Dv)).astype(np.float32),
+             g=np.zeros((S, T, Hv), np.float32), beta=np.ones((S, T, Hv), np.float32),
+             state_in=np.zeros((S, Hv, Dv, Dk), np.float32))
+    bits, _ = bf16_inputs(x)
+    for capture in (False, True):
+        got = run_bf16(x, bits, capture=capture)
+        exp = oracle.reference_bf16(bits["q"], bits["k"], bits["v"], x["g"], x["beta"],
+                                    x["state_in"], capture=capture)
+        for g_, e_, what in zip(got, exp, ("output", "state", "capture")):
+            assert_equal(g_, e_, f"bf16 exact probe {what}")
+
+
 # ------------------------------------------------------------------ rollback
 
 @pytest.mark.parametrize("name", ["spec_verify", "tiny"])

@@ -16,7 +16,7 @@ import pytest
 import oracle
 from oracle import gdn_oracle
 
-from pins import ALL_PINS, pin_rollback
+from pins import ALL_PINS, golden_bf16_rounding, pin_bf16, pin_rollback
 
 SK = "sk = sk + row[j] * static_cast<real>(k[at_qk(s, t, kh, j)]);"
 DECAY = "row[j] = alpha * row[j];"
@@ -59,6 +59,13 @@ MUTANTS = {
                              "(s * p->n_tokens + accepted[s] + 1) * head_state")],
     "rollback_ignores_bound": [("if (accepted[s] >= p->n_tokens) continue;",
                                 "if (accepted[s] > p->n_tokens) continue;")],
+    "bf16_truncates": [("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1;",
+                        "")],
+    "bf16_ties_away": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
+    "bf16_nan_not_quieted": [("return (uint16_t)((bits >> 16) | 0x0040u);",
+                              "return (uint16_t)(bits >> 16);")],
+    "bf16_v_not_widened": [("for (uint64_t e = 0; e < nv; ++e) vf[e] = bf16_to_f32(v[e]);",
+                            "for (uint64_t e = 0; e < nv; ++e) vf[e] = (float)v[e];")],
     "state_in_ignored": [("X[i * Dk + j] = static_cast<real>(state_in[at_state(s, vh, i, j)]);",
                           "X[i * Dk + j] = 0;")],
 }
@@ -88,11 +95,14 @@ def build_mutant(name, edits, where):
 def test_mutant_is_caught(name, mutant_dir):
     lib = build_mutant(name, MUTANTS[name], str(mutant_dir))
     ref = functools.partial(oracle.reference, library=lib)
-    rb = functools.partial(oracle.rollback, library=lib)
+    extra = {pin_rollback: dict(rollback=functools.partial(oracle.rollback, library=lib)),
+             pin_bf16: dict(ref_bf16=functools.partial(oracle.reference_bf16, library=lib)),
+             golden_bf16_rounding: dict(to_bf16=functools.partial(oracle.to_bf16,
+                                                                  library=lib))}
     caught = []
     for pin in ALL_PINS:
         try:
-            pin(ref, rollback=rb) if pin is pin_rollback else pin(ref)
+            pin(ref, **extra.get(pin, {}))
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name!r} passes every pin"
