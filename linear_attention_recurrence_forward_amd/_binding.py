@@ -149,7 +149,15 @@ def _check_tensors(where: str, params: GdnParams, tensors: dict, io=torch.float3
             raise ValueError(f"{where}: {name} is on {t.device}, other arrays on {device}")
         if not t.is_contiguous():
             raise ValueError(f"{where}: {name} must be contiguous")
-        if t.numel() != counts[name]:
+        if name == "state_capture" and params.n_seqs == 1:
+            # One sequence: a larger (preallocated) capture buffer is accepted and
+            # only its first n_tokens slices are written; with several sequences
+            # the per-sequence stride depends on n_tokens, so the size must match
+            # (mlx-native 0.21.1, dispatch_gated_delta_net_decode_with_capture).
+            if t.numel() < counts[name]:
+                raise ValueError(f"{where}: {name} element count {t.numel()} < required "
+                                 f"{counts[name]}")
+        elif t.numel() != counts[name]:
             raise ValueError(f"{where}: {name} element count {t.numel()} != expected "
                              f"{counts[name]}")
     return device
@@ -182,7 +190,8 @@ def gdn_forward_capture(q, k, v, g, beta, state_in, output, state_out, state_cap
                         params: GdnParams, stream=None) -> None:
     """Enqueue one forward call that also writes the per-token state
     (C: gdn_forward_capture). state_capture must hold exactly
-    n_tokens * d_k * d_v * n_v_heads * n_seqs floats."""
+    n_tokens * d_k * d_v * n_v_heads * n_seqs floats, or at least that many
+    when n_seqs == 1 (only the first n_tokens slices are written)."""
     tensors = dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in, output=output,
                    state_out=state_out, state_capture=state_capture)
     lib = _load()

@@ -467,6 +467,27 @@ def test_graph_replay():
         _ = (d["q"] * 2).sum().item()  # unrelated eager work between replays
 
 
+def test_single_sequence_capture_into_larger_buffer():
+    """n_seqs == 1: a capture buffer preallocated for more tokens is accepted
+    and only the first n_tokens slices are written; n_seqs > 1 needs the exact
+    size."""
+    w = WORKLOADS["spec_verify"].with_(n_seqs=1)
+    x = make_inputs(w, seed=30)
+    d = dev(x)
+    T, Hv, Dv, Dk = w.n_tokens, w.n_v_heads, w.d_v, w.d_k
+    big = torch.full((1, T + 3, Hv, Dv, Dk), 9.0, device="cuda")
+    out, st, cap = gdn.forward(*(d[n] for n in NAMES), capture=True, state_capture=big)
+    torch.cuda.synchronize()
+    exp = ref(x, capture=True)
+    close(cap[:, :T].cpu().numpy(), exp[2], "capture slices in the larger buffer")
+    assert torch.all(big[:, T:] == 9.0), "slices past n_tokens untouched"
+    w2 = WORKLOADS["spec_verify"]
+    d2 = dev(make_inputs(w2))
+    big2 = torch.empty((w2.n_seqs, T + 1, Hv, Dv, Dk), device="cuda")
+    with pytest.raises(ValueError, match="state_capture element count"):
+        gdn.forward(*(d2[n] for n in NAMES), capture=True, state_capture=big2)
+
+
 def test_errors_on_device_tensors():
     w = WORKLOADS["tiny"]
     x = make_inputs(w)
