@@ -213,11 +213,34 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   static_assert(R <= L, "one output lane per row");
 
   // Workgroup -> (sequence s, value head vh, block of rows); all uniform.
-  const uint32_t bid = blockIdx.x;
-  const uint32_t rb = bid % a.row_blocks;
-  const uint32_t hs = bid / a.row_blocks;  // s * n_v_heads + vh
-  const uint32_t vh = hs % a.n_v_heads;
-  const uint32_t s = hs / a.n_v_heads;
+  // One-token calls take the plain order (s, vh, block). Multi-token calls
+  // read every token's k and q rows once per key head, so their workgroups are
+  // ordered (s, kh, g, block) with vh = kh + g * n_k_heads (the value heads of
+  // the modulo GQA map that share key head kh) and renumbered so that each of
+  // the 8 XCDs, which receive workgroups round-robin and each have their own
+  // L2, runs one contiguous range of that order: a key head's k/q rows are
+  // then fetched into one L2 instead of several.
+  uint32_t s, vh, rb;
+  if constexpr (NB == 1) {
+    rb = blockIdx.x % a.row_blocks;
+    const uint32_t head = blockIdx.x / a.row_blocks;  // s * n_v_heads + vh
+    vh = head % a.n_v_heads;
+    s = head / a.n_v_heads;
+  } else {
+    const uint32_t n = gridDim.x, xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
+    const uint32_t per = n / 8u, extra = n % 8u;
+    const uint32_t bid = xcd * per + (xcd < extra ? xcd : extra) + local;
+    const uint32_t groups = a.n_v_heads / a.n_k_heads;  // value heads per key head
+    rb = bid % a.row_blocks;
+    uint32_t rest = bid / a.row_blocks;  // (s * n_k_heads + kh) * groups + g
+    const uint32_t g = rest % groups;
+    rest /= groups;
+    const uint32_t khead = rest % a.n_k_heads;
+    s = rest / a.n_k_heads;
+    vh = khead + g * a.n_k_heads;
+  }
+  // s * n_v_heads + vh is below the grid size (host-checked < 2^24).
+  const uint32_t hs = s * a.n_v_heads + vh;
   const uint32_t kh = vh % a.n_k_heads;  // GQA map of the capture kernel
 
   const uint32_t lane = threadIdx.x & 63u;
@@ -426,11 +449,18 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     uint32_t t = 0;
     while (T - t >= NB) {
       if (t - base_t >= 64) rebase(t);
+      // A group starts on a multiple of NB, so a chunk boundary can only fall
+      // on its first token; alpha/beta of the group's NB tokens are read from
+      // LDS together, one wait per group.
+      next_chunk(t);
+      float2 abg[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) abg[u] = ab[(t & 63u) + u];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const uint32_t ahead = t + NB - 1;
         load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
-        run(t, buf[u]);
+        step(t, buf[u], abg[u].x, abg[u].y);
         ++t;
       }
     }
