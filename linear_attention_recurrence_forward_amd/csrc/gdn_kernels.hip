@@ -19,8 +19,14 @@
 //     wave covers whole 128-byte lines: fully coalesced dwordx4 traffic.
 //   * sk and y are sums over the L lanes of a row: butterfly DPP adds
 //     (quad_perm, row_half_mirror, row_mirror) and one ds_swizzle for L = 32.
-//     No LDS traffic, no barriers. Each butterfly step adds a value to its
-//     partner's, so every lane of the row ends with the same bits.
+//     No barriers. Each butterfly step adds a value to its partner's, so
+//     every lane of the row ends with the same bits. With two rows per lane
+//     the halves of a row group hold the rows in swapped order, so that one
+//     butterfly reduces both rows (see partner()).
+//   * In multi-token calls every row group of a wave needs the same k and q
+//     columns; the wave loads each token's k and q rows once and hands them
+//     out through a per-wave LDS slot, so the vector memory unit sees each
+//     byte once per wave instead of once per row group.
 //   * A workgroup covers rows of one (sequence, value head), so g and beta are
 //     uniform: 64 tokens' worth of alpha = exp(-g) and beta are computed once
 //     per wave (lane t holds token t0+t), parked in LDS and read per token.
@@ -33,8 +39,8 @@
 //     past the descriptor's size (loads return 0, stores are discarded).
 // Two launch geometries instantiate the same template: one for a single decode
 // token (HBM-bound on the state read and write; straight-line, no ring) and one
-// for multi-token calls (VALU- and latency-bound; two rows per lane share each
-// k/q register).
+// for multi-token calls (bound by the VALU and the vector memory unit together;
+// two rows per lane share each k/q register).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,6 +58,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm:[1,0,3,2]  lane ^ 1
 constexpr int kDppXor2 = 0x4E;        // quad_perm:[2,3,0,1]  lane ^ 2
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane -> 7 - lane (per 8)
 constexpr int kDppMirror = 0x140;     // row_mirror: lane -> 15 - lane (per 16)
+constexpr int kDppRor8 = 0x128;       // row_ror:8: lane -> lane ^ 8 (per 16)
 // ds_swizzle bit mode (offset bit 15 = 0): and_mask 0x1f, or_mask 0,
 // xor_mask 0x10 -> lane ^ 16 within each group of 32.
 constexpr int kSwizzleXor16 = 0x1F | (0x10 << 10);
@@ -79,6 +86,29 @@ __device__ __forceinline__ float group_sum(float x) {
         float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
                                            kSwizzleXor16));
   return x;
+}
+
+// Two rows per lane, paired. A row group of L lanes holds rows P and Q; the
+// low half of the group keeps row P in its first register set ("A") and row Q
+// in its second ("B"), the high half the other way round. Each lane pairs
+// with a partner in the other half, whose B cells are the same row as its own
+// A cells. Adding the partner's B partial to one's own A partial leaves a
+// partial of the lane's A row over both lanes' columns; a butterfly over the
+// L/2 lanes of the half then completes it. Both rows are reduced with
+// log2(L) adds per lane instead of 2*log2(L), and each half ends holding the
+// sum of its own A row.
+template <int L>
+__device__ __forceinline__ float partner(float x) {
+  static_assert(L == 4 || L == 8 || L == 16, "paired rows need 4, 8 or 16 lanes");
+  if constexpr (L == 4) return dpp<kDppXor2>(x);        // lane ^ 2
+  if constexpr (L == 8) return dpp<kDppHalfMirror>(x);  // lane -> 7 - lane
+  if constexpr (L == 16) return dpp<kDppRor8>(x);       // lane ^ 8
+}
+
+// Sum of the lane's A row given the A and B partials (paired layout).
+template <int L>
+__device__ __forceinline__ float pair_sum(float a, float b) {
+  return group_sum<L / 2>(a + partner<L>(b));
 }
 
 // ---------------------------------------------------------------- buffers
@@ -160,6 +190,10 @@ struct Io<float> {
                                                 float x) {
     ::gdn::store1(r, off, soff, x);
   }
+  // Four elements from LDS, starting at element e of a staged row.
+  static __device__ __forceinline__ f4 lds4(const char *row, uint32_t e) {
+    return *reinterpret_cast<const f4 *>(row + e * 4);
+  }
 };
 
 template <>
@@ -182,6 +216,45 @@ struct Io<__bf16> {
                                                 float x) {
     __builtin_amdgcn_raw_buffer_store_b16(
         __builtin_bit_cast(unsigned short, static_cast<__bf16>(x)), r, off, soff, 0);
+  }
+  static __device__ __forceinline__ f4 lds4(const char *row, uint32_t e) {
+    const u2 w = *reinterpret_cast<const u2 *>(row + e * 2);
+    return f4{__builtin_bit_cast(float, w.x << 16),
+              __builtin_bit_cast(float, w.x & 0xFFFF0000u),
+              __builtin_bit_cast(float, w.y << 16),
+              __builtin_bit_cast(float, w.y & 0xFFFF0000u)};
+  }
+};
+
+// Raw per-lane bytes of a staged row load (RB bytes per lane).
+template <int RB>
+struct Raw;
+template <>
+struct Raw<8> {
+  typedef u2 T;
+  static __device__ __forceinline__ T load(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  }
+};
+template <>
+struct Raw<4> {
+  typedef uint32_t T;
+  static __device__ __forceinline__ T load(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+  }
+};
+template <>
+struct Raw<2> {
+  typedef uint16_t T;
+  static __device__ __forceinline__ T load(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+  }
+};
+template <>
+struct Raw<1> {
+  typedef uint8_t T;
+  static __device__ __forceinline__ T load(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
   }
 };
 
@@ -211,6 +284,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   constexpr uint32_t IB = Io<IO>::bytes;       // bytes per q/k/v/output element
   static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
   static_assert(R <= L, "one output lane per row");
+  // R == 2 uses the paired layout (see partner()): register set 0 is the
+  // lane's A row, whose sums, v and output the lane handles; set 1 its B row.
+  constexpr bool PAIRED = R == 2;
+  constexpr int NY = PAIRED ? 1 : R;  // rows whose v and output a lane handles
 
   // Workgroup -> (sequence s, value head vh, block of rows); all uniform.
   // One-token calls take the plain order (s, vh, block). Multi-token calls
@@ -253,12 +330,15 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   const uint64_t Hv = a.n_v_heads, Hk = a.n_k_heads;
 
   // This lane's rows. Rows past D_v compute on a clamped (valid) row and
-  // store nothing; all lanes stay active for the cross-lane sums.
+  // store nothing; all lanes stay active for the cross-lane sums. The high
+  // half of a paired group holds the group's two rows in swapped order.
+  const bool high = PAIRED && sub >= L / 2;
   uint32_t row[R];
   bool ok[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t i = rb * ROWS + wave * ROWS_PER_WAVE + r * G + grp;
+    const uint32_t slot = high ? R - 1 - r : r;
+    const uint32_t i = rb * ROWS + wave * ROWS_PER_WAVE + slot * G + grp;
     ok[r] = i < Dv;
     row[r] = ok[r] ? i : Dv - 1;
   }
@@ -288,21 +368,23 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   uint32_t cell[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) cell[r] = row[r] * ROW_BYTES + col;
-  uint32_t vrow[R];
+  uint32_t vrow[NY];
 #pragma unroll
-  for (int r = 0; r < R; ++r) vrow[r] = row[r] * IB;
-  // Outputs are written L tokens at a time: lane sub of a row group keeps
-  // the row's output of token t0 + sub (t0 a multiple of L) in yk, and one
-  // store per row writes the L tokens. Stores share the in-order memory
-  // counter with the prefetch loads, so one store per token would hold back
-  // every later prefetch behind its write acknowledgement.
-  constexpr uint32_t TB = L;  // tokens per output batch (divides 64)
-  float yk[R];
-  uint32_t yoff[R];  // lane's output address: row r of token t0 + sub
+  for (int r = 0; r < NY; ++r) vrow[r] = row[r] * IB;
+  // Outputs are written TB tokens at a time, TB being the number of lanes
+  // that hold a row's sums (L, or L/2 when paired): lane j of them keeps the
+  // row's output of token t0 + j (t0 a multiple of TB) in yk, and one store
+  // per row writes the TB tokens. Stores share the in-order memory counter
+  // with the prefetch loads, so one store per token would hold back every
+  // later prefetch behind its write acknowledgement.
+  constexpr uint32_t TB = PAIRED ? L / 2 : L;  // divides 64
+  const uint32_t slot_t = sub % TB;            // token slot of this lane
+  float yk[NY];
+  uint32_t yoff[NY];  // lane's output address: row r of token t0 + slot_t
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < NY; ++r) {
     yk[r] = 0.f;
-    yoff[r] = vrow[r] + sub * (uint32_t)(Hv * Dv * IB);
+    yoff[r] = vrow[r] + slot_t * (uint32_t)(Hv * Dv * IB);
   }
 
   f4 st[R][NV];
@@ -311,9 +393,25 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
     for (int m = 0; m < NV; ++m) st[r][m] = load4(s_in, cell[r] + m * 16 * L);
 
+  // Multi-token calls stage k and q through LDS. All G row groups of a wave
+  // need the same k and q columns, so direct per-lane loads would pull every
+  // byte through the vector memory unit G times. Instead the wave reads each
+  // token's k and q rows once (RB bytes per lane), parks them in a per-wave
+  // LDS slot, and every lane reads its own columns from there.
+  constexpr bool STAGE = NB > 1;
+  constexpr uint32_t ROW_IO = DK * IB;  // bytes of one k (or q) row
+  constexpr int RB = ROW_IO / 64;       // staged bytes per lane
+  static_assert(!STAGE || RB == 1 || RB == 2 || RB == 4 || RB == 8, "staged row size");
+  typedef typename Raw<STAGE ? RB : 4>::T RawT;
+  __shared__ __attribute__((aligned(16))) char kq_lds[STAGE ? WAVES : 1][2 * ROW_IO];
+  char *const kq_row = kq_lds[STAGE ? wave : 0];  // k row, then q row
   struct Tok {
+    f4 k[STAGE ? 1 : NV], q[STAGE ? 1 : NV];  // direct loads (one-token calls)
+    RawT kr, qr;                              // staged bytes (multi-token)
+    float v[NY];
+  };
+  struct KQ {
     f4 k[NV], q[NV];
-    float v[R];
   };
   // k, q, v and output are read through descriptors based at token base_t
   // that reach to the end of this sequence; token t's row is at scalar byte
@@ -340,54 +438,99 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     const uint32_t v_off = uniform((t - base_t) * v_bytes);
     const rsrc_t k_rs = buffer(k_b, kq_ext), q_rs = buffer(q_b, kq_ext);
     const rsrc_t v_rs = buffer(v_b, v_ext);
+    if constexpr (STAGE) {
+      x.kr = Raw<RB>::load(k_rs, lane * RB, kq_off);
+      x.qr = Raw<RB>::load(q_rs, lane * RB, kq_off);
+    } else {
 #pragma unroll
-    for (int m = 0; m < NV; ++m) {
-      x.k[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, kq_off);
-      x.q[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, kq_off);
+      for (int m = 0; m < NV; ++m) {
+        x.k[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, kq_off);
+        x.q[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, kq_off);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) x.v[r] = Io<IO>::load1(v_rs, vrow[r], v_off);
+    for (int r = 0; r < NY; ++r) x.v[r] = Io<IO>::load1(v_rs, vrow[r], v_off);
+  };
+
+  // This lane's k and q columns of a token: from the staged LDS slot, or
+  // the direct loads. The slot is rewritten per token; LDS operations of a
+  // wave run in order, so the reads of one token complete before the next
+  // token's write.
+  auto columns = [&](const Tok &x) {
+    KQ c;
+    if constexpr (STAGE) {
+      reinterpret_cast<RawT *>(kq_row)[lane] = x.kr;
+      reinterpret_cast<RawT *>(kq_row + ROW_IO)[lane] = x.qr;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int m = 0; m < NV; ++m) {
+        c.k[m] = Io<IO>::lds4(kq_row, m * 4 * L + 4 * sub);
+        c.q[m] = Io<IO>::lds4(kq_row + ROW_IO, m * 4 * L + 4 * sub);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NV; ++m) {
+        c.k[m] = x.k[m];
+        c.q[m] = x.q[m];
+      }
+    }
+    return c;
   };
 
   auto step = [&](uint32_t t, const Tok &x, float alpha, float b) {
-    float d[R];
+    const KQ kq = columns(x);
+    float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float part = 0.f;
+      part[r] = 0.f;
 #pragma unroll
       for (int m = 0; m < NV; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           st[r][m][e] *= alpha;                          // decay first
-          part = __builtin_fmaf(st[r][m][e], x.k[m][e], part);
+          part[r] = __builtin_fmaf(st[r][m][e], kq.k[m][e], part[r]);
         }
-      const float sk = group_sum<L>(part);
-      d[r] = (x.v[r] - sk) * b;
     }
-    const bool mine = sub == (t & (TB - 1));
+    float d[R];
+    if constexpr (PAIRED) {
+      d[0] = (x.v[0] - pair_sum<L>(part[0], part[1])) * b;
+      d[1] = partner<L>(d[0]);  // the partner's A row is this lane's B row
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) d[r] = (x.v[r] - group_sum<L>(part[r])) * b;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float part = 0.f;
+      part[r] = 0.f;
 #pragma unroll
       for (int m = 0; m < NV; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          st[r][m][e] = __builtin_fmaf(d[r], x.k[m][e], st[r][m][e]);
-          part = __builtin_fmaf(st[r][m][e], x.q[m][e], part);
+          st[r][m][e] = __builtin_fmaf(d[r], kq.k[m][e], st[r][m][e]);
+          part[r] = __builtin_fmaf(st[r][m][e], kq.q[m][e], part[r]);
         }
-      const float y = group_sum<L>(part);
-      yk[r] = mine ? y * a.q_scale : yk[r];
+    }
+    const bool mine = slot_t == (t & (TB - 1));
+    if constexpr (PAIRED) {
+      const float y = pair_sum<L>(part[0], part[1]);
+      yk[0] = mine ? y : yk[0];
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float y = group_sum<L>(part[r]);
+        yk[r] = mine ? y : yk[r];
+      }
     }
     if ((t & (TB - 1)) == TB - 1 || t + 1 == T) {
-      // Lanes 0 .. t % TB of each row group hold tokens t0 .. t. base_t is a
-      // multiple of 64 and at most t, so t0 - base_t >= 0.
+      // Token slots 0 .. t % TB hold tokens t0 .. t. base_t is a multiple of
+      // 64 and at most t, so t0 - base_t >= 0. q_scale is applied here.
       const uint32_t t0 = t & ~(TB - 1);
       const rsrc_t o_rs = buffer(o_b, v_ext);
       const uint32_t soff = uniform((t0 - base_t) * v_bytes);
-      if (sub <= (t & (TB - 1)))
+      if (slot_t <= (t & (TB - 1)))
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (ok[r]) Io<IO>::store1(o_rs, yoff[r], soff, yk[r]);
+        for (int r = 0; r < NY; ++r)
+          if (ok[r]) Io<IO>::store1(o_rs, yoff[r], soff, yk[r] * a.q_scale);
     }
     if constexpr (CAPTURE) {
       const rsrc_t ct = buffer(c_tok + t * cap_step, head_bytes);

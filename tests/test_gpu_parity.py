@@ -149,6 +149,35 @@ def test_shapes(shape, capture):
             assert_equal(got[2][:, -1], got[1], "capture[T-1] == state_out")
 
 
+def test_decay_extremes():
+    """Decay factors far from the usual range, mixed into one run: g = 60
+    (alpha ~ 1e-26, the state all but wiped), g = -1 (alpha = e, growth), and
+    three tokens of g = -16 (alpha ~ 9e6) on a zero state with beta = 0, which
+    must stay exactly zero. Every element within tolerance of the f64 shadow
+    and finite."""
+    w = Workload("extremes", 0, 128, 64, 2, 4, 200, 2)
+    x = make_inputs(w, seed=21)
+    rng = np.random.default_rng(21)
+    g, beta, state = x["g"].copy(), x["beta"].copy(), x["state_in"].copy()
+    S, T, Hv = g.shape
+    for s_ in range(S):
+        picks = rng.permutation(np.arange(4, T))[:20]
+        g[s_, picks[:10]] = 60.0
+        g[s_, picks[10:]] = -1.0
+    state[0, 0] = 0.0
+    beta[0, 0:4, 0] = 0.0
+    g[0, 1:4, 0] = -16.0
+    g[1, 8:12, 1] = 60.0
+    x = dict(x, g=g, beta=beta, state_in=state)
+    got = run(x)
+    exp = ref(x, precision="f64")
+    for g_, e, what in zip(got, exp, ("output", "state_out")):
+        assert np.all(np.isfinite(g_)), what
+        close(g_, e, f"extremes {what} vs f64 shadow")
+    assert_equal(got[0][0, 0:4, 0], np.zeros_like(got[0][0, 0:4, 0]),
+                 "zero state, beta = 0: zero outputs through the growth tokens")
+
+
 def test_long_run_drift():
     """A long run (T = 2048) stays within tolerance of the oracle and the f64
     shadow: no drift from the exp or the reduction order."""
