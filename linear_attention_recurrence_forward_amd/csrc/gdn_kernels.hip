@@ -477,8 +477,21 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     return c;
   };
 
-  auto step = [&](uint32_t t, const Tok &x, float alpha, float b) {
+  // One token. With decay set (c = 1, b = beta): the cells are multiplied by
+  // alpha, then sk, delta = (v - sk) * beta, the rank-1 write and y, as the
+  // recurrence is written. Lazy tokens (decay clear; multi-token calls only)
+  // keep the state divided by c, the product of the alphas of the ring
+  // group's tokens after its first, up to this one, and leave the cells
+  // undecayed: sk = c * (cells . k), the write adds delta / c along k
+  // (b = beta / c), y = c * (cells . q). The same recurrence reassociated,
+  // one multiply per cell and token fewer. decay is wave-uniform.
+  auto step = [&](uint32_t t, const Tok &x, bool decay, float alpha, float b, float c) {
     const KQ kq = columns(x);
+    if (decay)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < NV; ++m) st[r][m] *= alpha;
     float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -487,17 +500,16 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       for (int m = 0; m < NV; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          st[r][m][e] *= alpha;                          // decay first
           part[r] = __builtin_fmaf(st[r][m][e], kq.k[m][e], part[r]);
         }
     }
     float d[R];
     if constexpr (PAIRED) {
-      d[0] = (x.v[0] - pair_sum<L>(part[0], part[1])) * b;
+      d[0] = __builtin_fmaf(-c, pair_sum<L>(part[0], part[1]), x.v[0]) * b;
       d[1] = partner<L>(d[0]);  // the partner's A row is this lane's B row
     } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) d[r] = (x.v[r] - group_sum<L>(part[r])) * b;
+      for (int r = 0; r < R; ++r) d[r] = __builtin_fmaf(-c, group_sum<L>(part[r]), x.v[r]) * b;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -512,12 +524,12 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     }
     const bool mine = slot_t == (t & (TB - 1));
     if constexpr (PAIRED) {
-      const float y = pair_sum<L>(part[0], part[1]);
+      const float y = c * pair_sum<L>(part[0], part[1]);
       yk[0] = mine ? y : yk[0];
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float y = group_sum<L>(part[r]);
+        const float y = c * group_sum<L>(part[r]);
         yk[r] = mine ? y : yk[r];
       }
     }
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     Tok x;
     load_token(0, x);
     const rsrc_t gb = buffer(g_tok, 4), bb = buffer(b_tok, 4);
-    step(0, x, expf(-load1(gb, 0)), load1(bb, 0));
+    step(0, x, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
   } else {
     // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
     // t0 + j (clamped to the last token; lanes past the end are never read).
@@ -561,21 +573,56 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     // per-wave LDS slot: computed once per chunk (one exp per lane), read per
     // token as one broadcast ds_read_b64. The raw g/beta of the next chunk
     // are requested a chunk ahead into registers that nothing else reads.
-    __shared__ float2 ab_lds[WAVES][64];
-    float2 *ab = ab_lds[wave];
+    // Per-token factors of the current 64-token chunk live in a small
+    // per-wave LDS slot, computed once per chunk (lane j: token t0 + j) and
+    // read per token as broadcasts: {alpha = exp(-g), b, c, beta}. In a ring
+    // group that runs lazily, c is the product of the alphas of the group's
+    // tokens 1 .. u (1 at u = 0) and b = beta / c. A group runs eagerly
+    // (every token decays; c = 1, b = beta) if any of its c or beta / c
+    // would leave [2^-64, 2^64] or is not finite (strong decay or growth,
+    // special values), and always when the state is captured. The raw
+    // g/beta of the next chunk are requested a chunk ahead into registers
+    // that nothing else reads.
+    __shared__ float4 ab_lds[WAVES][64];
+    float4 *ab = ab_lds[wave];
     float g_raw, b_raw;
     load_chunk(0, g_raw, b_raw);
+    // Bit j set: token t0 + j belongs to an eager group (wave-uniform).
+    uint64_t eager_mask = ~0ull;
     auto next_chunk = [&](uint32_t t) {
       if ((t & 63u) == 0) {
-        ab[lane] = make_float2(expf(-g_raw), b_raw);
+        const float al = expf(-g_raw), be = b_raw;
+        if constexpr (CAPTURE) {
+          ab[lane] = make_float4(al, be, 1.f, be);
+        } else {
+          ab[lane].x = al;
+          __builtin_amdgcn_wave_barrier();
+          const uint32_t q0 = lane & ~(NB - 1u), u = lane & (NB - 1u);
+          float c = 1.f;
+#pragma unroll
+          for (uint32_t i = 1; i < NB; ++i) {
+            const float ai = ab[q0 + i].x;
+            c = i <= u ? c * ai : c;
+          }
+          const float bc = be / c;
+          const bool lazy_ok = c >= 0x1p-64f && c <= 0x1p64f &&
+                               __builtin_fabsf(bc) <= 0x1p64f;
+          const uint64_t bad = __builtin_amdgcn_ballot_w64(!lazy_ok);
+          eager_mask =
+              (uint64_t)uniform((uint32_t)(bad >> 32)) << 32 | uniform((uint32_t)bad);
+          const bool eager = (eager_mask >> q0) & ((1ull << NB) - 1u);
+          ab[lane] = eager ? make_float4(al, be, 1.f, be) : make_float4(al, bc, c, be);
+        }
+        // After the last use of this chunk's raw values, so that the requests
+        // can land in the same registers without a copy (and a wait).
         if (T - t > 64) load_chunk(t + 64, g_raw, b_raw);
         __builtin_amdgcn_wave_barrier();
       }
     };
     auto run = [&](uint32_t t, const Tok &x) {
       next_chunk(t);
-      const float2 a_b = ab[t & 63u];
-      step(t, x, a_b.x, a_b.y);
+      const float4 f = ab[t & 63u];
+      step(t, x, true, f.x, f.w, 1.f);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -590,23 +637,36 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
     uint32_t t = 0;
+    // The cells hold the state divided by kappa: the c of the previous
+    // group's last token when that group ran lazily, else 1. A group's first
+    // token decays by kappa * alpha, which makes the cells the state again
+    // (c = 1) before the group's lazy tokens.
+    float kappa = 1.f;
     while (T - t >= NB) {
       if (t - base_t >= 64) rebase(t);
       // A group starts on a multiple of NB, so a chunk boundary can only fall
-      // on its first token; alpha/beta of the group's NB tokens are read from
-      // LDS together, one wait per group.
+      // on its first token; the factors of the group's NB tokens are read
+      // from LDS together, one wait per group.
       next_chunk(t);
-      float2 abg[NB];
+      float4 f[NB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) abg[u] = ab[(t & 63u) + u];
+      for (int u = 0; u < NB; ++u) f[u] = ab[(t & 63u) + u];
+      const bool eager =
+          CAPTURE || ((uint32_t)(eager_mask >> (t & 63u)) & ((1u << NB) - 1u)) != 0;
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const uint32_t ahead = t + NB - 1;
         load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
-        step(t, buf[u], abg[u].x, abg[u].y);
+        step(t, buf[u], u == 0 || eager, u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z);
         ++t;
       }
+      kappa = f[NB - 1].z;  // 1 after an eager group
     }
+    // Back to the plain state for the remaining tokens and the final store.
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < NV; ++m) st[r][m] *= kappa;
     // Fewer than NB tokens remain, all already requested.
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
@@ -647,11 +707,15 @@ constexpr Geometry make_geometry() {
 //                measured within a few percent of each other.
 //   two or more: two rows per lane (each k/q register feeds two rows, which
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
-//                tokens against one row per lane), 16 lanes per row, 4 waves,
-//                a four-token prefetch ring. Best or within 2% of the best
-//                measured variant from 2 tokens up (2 to 512), so one token is
-//                the only short-run case. At D_k = 64, 8 lanes per row (8
-//                cells each): 512-token prefill 145 -> 135 us against 16.
+//                tokens against one row per lane), 16 lanes per row, 4 waves.
+//                Without capture an eight-token prefetch ring and lazy group
+//                (512-token prefill 221 -> 206 us against four tokens without
+//                the lazy form); with capture, which runs eagerly and is bound
+//                by its writes, a four-token ring. The two-row geometry was
+//                best or within 2% of the best measured variant from 2 tokens
+//                up (2 to 512), so one token is the only short-run case. At
+//                D_k = 64, 8 lanes per row (8 cells each): 512-token prefill
+//                145 -> 135 us against 16.
 template <bool CAPTURE, typename IO>
 Geometry pick(uint32_t d_k, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
@@ -664,7 +728,7 @@ Geometry pick(uint32_t d_k, uint32_t n_tokens) {
                        : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO>();
     case 128:
       return one_token ? make_geometry<128, 8, 1, 4, 1, CAPTURE, IO>()
-                       : make_geometry<128, 8, 2, 4, 4, CAPTURE, IO>();
+                       : make_geometry<128, 8, 2, 4, CAPTURE ? 4 : 8, CAPTURE, IO>();
     default:
       return Geometry{0, 0, nullptr};
   }
