@@ -190,10 +190,6 @@ struct Io<float> {
                                                 float x) {
     ::gdn::store1(r, off, soff, x);
   }
-  // Four elements from LDS, starting at element e of a staged row.
-  static __device__ __forceinline__ f4 lds4(const char *row, uint32_t e) {
-    return *reinterpret_cast<const f4 *>(row + e * 4);
-  }
 };
 
 template <>
@@ -216,13 +212,6 @@ struct Io<__bf16> {
                                                 float x) {
     __builtin_amdgcn_raw_buffer_store_b16(
         __builtin_bit_cast(unsigned short, static_cast<__bf16>(x)), r, off, soff, 0);
-  }
-  static __device__ __forceinline__ f4 lds4(const char *row, uint32_t e) {
-    const u2 w = *reinterpret_cast<const u2 *>(row + e * 2);
-    return f4{__builtin_bit_cast(float, w.x << 16),
-              __builtin_bit_cast(float, w.x & 0xFFFF0000u),
-              __builtin_bit_cast(float, w.y << 16),
-              __builtin_bit_cast(float, w.y & 0xFFFF0000u)};
   }
 };
 
@@ -250,13 +239,20 @@ struct Raw<2> {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
   }
 };
-template <>
-struct Raw<1> {
-  typedef uint8_t T;
-  static __device__ __forceinline__ T load(rsrc_t r, uint32_t off, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
+// Store EPL staged elements (raw bits of IO type) as f32 at dst.
+template <typename IO, uint32_t EPL, typename R>
+__device__ __forceinline__ void widen_store(float *dst, R raw) {
+  if constexpr (sizeof(IO) == 4) {
+    *reinterpret_cast<R *>(dst) = raw;  // f32: the bits are the values
+  } else if constexpr (EPL == 2) {
+    const uint32_t w = raw;  // two bf16
+    *reinterpret_cast<float2 *>(dst) = make_float2(__builtin_bit_cast(float, w << 16),
+                                                   __builtin_bit_cast(float, w & 0xFFFF0000u));
+  } else {
+    static_assert(EPL == 1, "one or two elements per lane");
+    *dst = __builtin_bit_cast(float, (uint32_t)raw << 16);
   }
-};
+}
 
 struct KernelArgs {
   const void *q, *k, *v;  // IO type
@@ -398,13 +394,18 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // byte through the vector memory unit G times. Instead the wave reads each
   // token's k and q rows once (RB bytes per lane), parks them in a per-wave
   // LDS slot, and every lane reads its own columns from there.
+  // Lane j loads elements EPL*j .. EPL*j+EPL-1 of each row (lanes past the
+  // row repeat its last part and write nothing) and stores them widened to
+  // f32, so the column reads need no conversion.
   constexpr bool STAGE = NB > 1;
-  constexpr uint32_t ROW_IO = DK * IB;  // bytes of one k (or q) row
-  constexpr int RB = ROW_IO / 64;       // staged bytes per lane
-  static_assert(!STAGE || RB == 1 || RB == 2 || RB == 4 || RB == 8, "staged row size");
+  constexpr uint32_t EPL = DK >= 64 ? DK / 64 : 1;  // elements per lane
+  constexpr uint32_t SLANES = DK / EPL;              // lanes holding a part
+  constexpr int RB = EPL * IB;                       // staged bytes per lane
+  static_assert(!STAGE || RB == 2 || RB == 4 || RB == 8, "staged row size");
   typedef typename Raw<STAGE ? RB : 4>::T RawT;
-  __shared__ __attribute__((aligned(16))) char kq_lds[STAGE ? WAVES : 1][2 * ROW_IO];
-  char *const kq_row = kq_lds[STAGE ? wave : 0];  // k row, then q row
+  __shared__ __attribute__((aligned(16))) float kq_lds[STAGE ? WAVES : 1][2 * DK];
+  float *const kq_row = kq_lds[STAGE ? wave : 0];  // k row, then q row (f32)
+  const uint32_t slane = lane < SLANES ? lane : SLANES - 1;
   struct Tok {
     f4 k[STAGE ? 1 : NV], q[STAGE ? 1 : NV];  // direct loads (one-token calls)
     RawT kr, qr;                              // staged bytes (multi-token)
@@ -439,8 +440,8 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     const rsrc_t k_rs = buffer(k_b, kq_ext), q_rs = buffer(q_b, kq_ext);
     const rsrc_t v_rs = buffer(v_b, v_ext);
     if constexpr (STAGE) {
-      x.kr = Raw<RB>::load(k_rs, lane * RB, kq_off);
-      x.qr = Raw<RB>::load(q_rs, lane * RB, kq_off);
+      x.kr = Raw<RB>::load(k_rs, slane * RB, kq_off);
+      x.qr = Raw<RB>::load(q_rs, slane * RB, kq_off);
     } else {
 #pragma unroll
       for (int m = 0; m < NV; ++m) {
@@ -459,13 +460,15 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   auto columns = [&](const Tok &x) {
     KQ c;
     if constexpr (STAGE) {
-      reinterpret_cast<RawT *>(kq_row)[lane] = x.kr;
-      reinterpret_cast<RawT *>(kq_row + ROW_IO)[lane] = x.qr;
+      if (SLANES == 64 || lane < SLANES) {
+        widen_store<IO, EPL>(kq_row + EPL * lane, x.kr);
+        widen_store<IO, EPL>(kq_row + DK + EPL * lane, x.qr);
+      }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int m = 0; m < NV; ++m) {
-        c.k[m] = Io<IO>::lds4(kq_row, m * 4 * L + 4 * sub);
-        c.q[m] = Io<IO>::lds4(kq_row + ROW_IO, m * 4 * L + 4 * sub);
+        c.k[m] = *reinterpret_cast<const f4 *>(kq_row + m * 4 * L + 4 * sub);
+        c.q[m] = *reinterpret_cast<const f4 *>(kq_row + DK + m * 4 * L + 4 * sub);
       }
     } else {
 #pragma unroll
