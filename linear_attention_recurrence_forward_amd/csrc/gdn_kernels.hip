@@ -158,6 +158,13 @@ __device__ __forceinline__ float load1(rsrc_t r, uint32_t off, uint32_t soff = 0
                             __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
 }
 
+// The state is read once per call: a streaming (non-temporal) load keeps it
+// from displacing the k/q rows that other value heads reread.
+__device__ __forceinline__ f4 load4_stream(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(
+      f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+}
+
 __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, uint32_t soff, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), r,
                                         off, soff, 0);
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < NV; ++m) st[r][m] = load4(s_in, cell[r] + m * 16 * L);
+    for (int m = 0; m < NV; ++m) st[r][m] = load4_stream(s_in, cell[r] + m * 16 * L);
 
   // Multi-token calls stage k and q through LDS. All G row groups of a wave
   // need the same k and q columns, so direct per-lane loads would pull every
@@ -704,10 +711,11 @@ constexpr Geometry make_geometry() {
 // Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
 // HBM-resident inputs; D_k = 128 workloads of one-token decode, 64-sequence
 // batched decode, 4-token capture and 512-token prefill):
-//   one token  : C = D_k/16 cells per lane (16 lanes per row), one row per
-//                lane, 4 waves, straight-line code. Pure streaming of the state;
-//                all C and wave counts from 4 to 16 cells and 1 to 4 waves
-//                measured within a few percent of each other.
+//   one token  : 16 lanes per row, 4 waves, straight-line code; pure
+//                streaming of the state, read with non-temporal loads (single
+//                decode 3.58 -> 3.23 us, 64-sequence decode 48.3 -> 43.0 us).
+//                At D_k = 128 two rows per lane (paired): 3.23 -> 3.13 us;
+//                other cell counts and wave counts measured no better.
 //   two or more: two rows per lane (each k/q register feeds two rows, which
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
 //                tokens against one row per lane), 16 lanes per row, 4 waves.
@@ -730,7 +738,7 @@ Geometry pick(uint32_t d_k, uint32_t n_tokens) {
       return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO>()
                        : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO>();
     case 128:
-      return one_token ? make_geometry<128, 8, 1, 4, 1, CAPTURE, IO>()
+      return one_token ? make_geometry<128, 8, 2, 4, 1, CAPTURE, IO>()
                        : make_geometry<128, 8, 2, 4, CAPTURE ? 4 : 8, CAPTURE, IO>();
     default:
       return Geometry{0, 0, nullptr};
