@@ -721,8 +721,9 @@ constexpr Geometry make_geometry() {
 //                tokens against one row per lane), 16 lanes per row, 4 waves.
 //                Without capture an eight-token prefetch ring and lazy group
 //                (512-token prefill 221 -> 206 us against four tokens without
-//                the lazy form); with capture, which runs eagerly and is bound
-//                by its writes, a four-token ring. The two-row geometry was
+//                the lazy form). With capture, which runs eagerly and is bound
+//                by its writes, one row per lane (twice the waves) and a
+//                four-token ring: 4-token verify 5.88 -> 5.64 us. The two-row geometry was
 //                best or within 2% of the best measured variant from 2 tokens
 //                up (2 to 512), so one token is the only short-run case. At
 //                D_k = 64, 8 lanes per row (8 cells each): 512-token prefill
@@ -738,8 +739,9 @@ Geometry pick(uint32_t d_k, uint32_t n_tokens) {
       return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO>()
                        : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO>();
     case 128:
-      return one_token ? make_geometry<128, 8, 2, 4, 1, CAPTURE, IO>()
-                       : make_geometry<128, 8, 2, 4, CAPTURE ? 4 : 8, CAPTURE, IO>();
+      if (one_token) return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO>();
+      if constexpr (CAPTURE) return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO>();
+      return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO>();
     default:
       return Geometry{0, 0, nullptr};
   }

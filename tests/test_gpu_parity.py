@@ -425,8 +425,10 @@ def test_bf16_exact_probe():
 @pytest.mark.parametrize("name", ["spec_verify", "tiny"])
 def test_rollback(name):
     """Accepted-prefix rollback on the GPU: bit-exact against the oracle's copy
-    of the GPU capture; equal to the GPU state after the accepted prefix (bit for
-    bit from two tokens on, same geometry); out-of-range indexes keep the state."""
+    of the GPU capture; equal to the state of a capture call cut to the accepted
+    prefix (bit for bit from two tokens on: one kernel, the same arithmetic) and
+    to a plain cut call within tolerance (plain calls have their own geometry);
+    out-of-range indexes keep the state."""
     w = WORKLOADS[name]
     x = make_inputs(w)
     d = dev(x)
@@ -456,9 +458,12 @@ def test_rollback(name):
                 assert np.array_equal(got[s_], st_np[s_]), "last token == state_out"
             elif a_ >= 1:
                 cut = {n: x[n][s_:s_ + 1, :a_ + 1] for n in ("q", "k", "v", "g", "beta")}
-                _, s_cut = run(dict(cut, state_in=x["state_in"][s_:s_ + 1],
-                                    q_scale_bits=x["q_scale_bits"]))
-                assert_equal(got[s_], s_cut[0], f"rollback to {a_} == {a_ + 1}-token state")
+                cut = dict(cut, state_in=x["state_in"][s_:s_ + 1],
+                           q_scale_bits=x["q_scale_bits"])
+                _, s_cap, _ = run(cut, capture=True)
+                assert_equal(got[s_], s_cap[0], f"rollback to {a_} == {a_ + 1}-token state")
+                _, s_plain = run(cut)
+                close(got[s_], s_plain[0], f"rollback to {a_} vs a plain {a_ + 1}-token call")
 
 
 # ------------------------------------------------------------------ plumbing
