@@ -55,6 +55,8 @@ def parse_args(argv=None):
     ap.add_argument("--launch", default="graph", choices=("graph", "direct"))
     ap.add_argument("--io", default="f32", choices=("f32", "bf16"),
                     help="element type of q, k, v and output (state stays f32)")
+    ap.add_argument("--normalize-k", action="store_true",
+                    help="L2-normalise every key row in the kernel (gdn_forward_ex)")
     ap.add_argument("--layers", type=int, default=0,
                     help="input sets to cycle through (0: enough for 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -257,8 +259,9 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     rollback = args.workload == "rollback"
-    if args.io == "bf16" and args.workload == "rollback":
-        print("bench.py: --io bf16 applies to forward workloads", file=sys.stderr)
+    if (args.io == "bf16" or args.normalize_k) and args.workload == "rollback":
+        print("bench.py: --io bf16 and --normalize-k apply to forward workloads",
+              file=sys.stderr)
         return 2
     bf16 = args.io == "bf16"
     w, kernel_name, alg_bytes, description = workload_info(args.workload, args.io)
@@ -297,6 +300,11 @@ def main(argv=None):
         d = sets[i % layers]
         if rollback:
             gdn.gdn_rollback(d["capture"], d["accepted"], d["state_in"], params, stream)
+        elif args.normalize_k:
+            gdn.gdn_forward_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                               d["output"], d["state_in"], d["capture"], params,
+                               gdn.OPT_NORMALIZE_K | (gdn.OPT_BF16_IO if bf16 else 0),
+                               stream)
         elif bf16:
             gdn.gdn_forward_bf16(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
                                  d["output"], d["state_in"], d["capture"], params, stream)
@@ -363,7 +371,7 @@ def main(argv=None):
         achieved = alg_bytes / kernel_s / 1e9
         roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                         frac=achieved / HBM_PEAK_GBPS)
-    roofline["traffic"] = (None if bf16 else
+    roofline["traffic"] = (None if bf16 or args.normalize_k else
                            traffic_from_profiles(args.workload, digest, kernel_name))
     roofline["kernel"] = kernel_name
     roofline["kernel_us"] = kernel_s * 1e6
@@ -385,7 +393,8 @@ def main(argv=None):
             "workload": description,
             "d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads, "n_v_heads": w.n_v_heads,
             "n_tokens": w.n_tokens, "n_seqs": w.n_seqs, "q_scale_bits": bits,
-            "capture": w.capture, "launch": args.launch, "resident_sets": layers,
+            "capture": w.capture, "normalize_k": args.normalize_k,
+            "launch": args.launch, "resident_sets": layers,
             "algorithmic_bytes_per_step": alg_bytes,
             "flops_per_step": 0 if rollback else w.flops(),
         },
@@ -394,7 +403,7 @@ def main(argv=None):
         "roofline": roofline,
         "kernel_digest": digest,
     }
-    if not args.no_cpu_baseline and not bf16:
+    if not args.no_cpu_baseline and not bf16 and not args.normalize_k:
         line["cpu_baseline"] = (cpu_baseline_rollback(w, args.cpu_seconds) if rollback
                                 else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)

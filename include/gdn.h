@@ -83,8 +83,13 @@ typedef enum gdn_status {
   GDN_ERR_MISALIGNED = 8,       /* an array breaks the alignment rule above   */
   GDN_ERR_ALIASING = 9,         /* an output overlaps another array (other
                                    than state_out == state_in exactly)        */
-  GDN_ERR_LAUNCH = 10           /* the HIP runtime refused the launch         */
+  GDN_ERR_LAUNCH = 10,          /* the HIP runtime refused the launch         */
+  GDN_ERR_OPTION = 11           /* an unknown bit is set in the options word  */
 } gdn_status;
+
+/* Option bits of gdn_forward_ex. */
+#define GDN_OPT_BF16_IO 1u     /* q, k, v and output are bf16 (as gdn_forward_bf16) */
+#define GDN_OPT_NORMALIZE_K 2u /* L2-normalise every key row in the kernel       */
 
 /* Validate a params block (the checks on dims, extents, GQA ratio, D_k,
  * reserved words and sizes; mlx-native 0.21.1 validate / validate_params_buf).
@@ -123,6 +128,23 @@ gdn_status gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
                             uint16_t *output, float *state_out,
                             float *state_capture, const gdn_params *p,
                             void *stream);
+
+/* gdn_forward_capture / gdn_forward_bf16 with an options word.
+ * GDN_OPT_BF16_IO: q, k, v and output hold bf16 (uint16_t) elements, with the
+ * conventions of gdn_forward_bf16; otherwise f32.
+ * GDN_OPT_NORMALIZE_K: every key row k[s,t,kh,:] is used as
+ *     k / sqrt(sum_j k_j^2 + 1e-6)
+ * (the in-kernel form of the L2 normalisation that models apply to keys
+ * before this step; not a step of the pages' kernels, which take k as given).
+ * The caller's k array is not modified. Sums are taken in f32 in a
+ * reduction order of the library's choosing.
+ * state_capture may be NULL. Unknown option bits: GDN_ERR_OPTION, checked
+ * before anything else after params. */
+gdn_status gdn_forward_ex(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *state_in, void *output,
+                          float *state_out, float *state_capture,
+                          const gdn_params *p, uint32_t options, void *stream);
 
 /* Accepted-prefix rollback for speculative decoding (mlx-native 0.21.1,
  * dispatch_gated_delta_net_decode_with_capture doc: on a partial reject the

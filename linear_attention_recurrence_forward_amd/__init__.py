@@ -11,7 +11,7 @@ torch or a GPU.
 _BINDING_NAMES = (
     "EXPORTS", "GdnError", "GdnParams", "STATUS", "STATUS_CODE", "f32_bits", "forward",
     "gdn_check_params", "gdn_forward", "gdn_forward_bf16", "gdn_forward_capture",
-    "gdn_rollback",
+    "gdn_forward_ex", "gdn_rollback", "OPT_BF16_IO", "OPT_NORMALIZE_K",
     "gdn_status_string",
     "library_path", "make_params", "params_for",
 )

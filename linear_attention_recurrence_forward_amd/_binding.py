@@ -27,12 +27,15 @@ STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_ZERO_DIM",
     3: "GDN_ERR_ZERO_EXTENT", 4: "GDN_ERR_GQA_RATIO", 5: "GDN_ERR_UNSUPPORTED_DK",
     6: "GDN_ERR_RESERVED_NONZERO", 7: "GDN_ERR_SIZE_OVERFLOW", 8: "GDN_ERR_MISALIGNED",
-    9: "GDN_ERR_ALIASING", 10: "GDN_ERR_LAUNCH",
+    9: "GDN_ERR_ALIASING", 10: "GDN_ERR_LAUNCH", 11: "GDN_ERR_OPTION",
 }
+# Option bits of gdn_forward_ex.
+OPT_BF16_IO = 1
+OPT_NORMALIZE_K = 2
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTS = ("gdn_check_params", "gdn_forward", "gdn_forward_bf16", "gdn_forward_capture",
-           "gdn_rollback", "gdn_status_string")
+           "gdn_forward_ex", "gdn_rollback", "gdn_status_string")
 IO_ARRAYS = ("q", "k", "v", "output")  # the arrays gdn_forward_bf16 takes in bf16
 
 
@@ -88,6 +91,9 @@ def _load():
             vp = ctypes.c_void_p
             lib.gdn_forward_bf16.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, p, vp]
             lib.gdn_forward_bf16.restype = ctypes.c_int
+            lib.gdn_forward_ex.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, p,
+                                           ctypes.c_uint32, vp]
+            lib.gdn_forward_ex.restype = ctypes.c_int
             lib.gdn_rollback.argtypes = [fp, ctypes.POINTER(ctypes.c_uint32), fp, p,
                                          ctypes.c_void_p]
             lib.gdn_rollback.restype = ctypes.c_int
@@ -228,6 +234,32 @@ def gdn_forward_bf16(q, k, v, g, beta, state_in, output, state_out, state_captur
         raise GdnError(st, "gdn_forward_bf16")
 
 
+def gdn_forward_ex(q, k, v, g, beta, state_in, output, state_out, state_capture,
+                   params: GdnParams, options: int, stream=None) -> None:
+    """Enqueue one forward call with an options word (C: gdn_forward_ex):
+    OPT_BF16_IO (q, k, v, output in bf16) and OPT_NORMALIZE_K (every key row
+    used as k / sqrt(sum k^2 + 1e-6)). state_capture may be None."""
+    tensors = dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in, output=output,
+                   state_out=state_out)
+    if state_capture is not None:
+        tensors["state_capture"] = state_capture
+    lib = _load()
+    st = lib.gdn_check_params(ctypes.byref(params))
+    if st != 0:
+        raise GdnError(st, "gdn_forward_ex")
+    if options & ~(OPT_BF16_IO | OPT_NORMALIZE_K):
+        raise GdnError(STATUS_CODE["GDN_ERR_OPTION"], "gdn_forward_ex")
+    io = torch.bfloat16 if options & OPT_BF16_IO else torch.float32
+    device = _check_tensors("gdn_forward_ex", params, tensors, io=io)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = lib.gdn_forward_ex(ptr(q), ptr(k), ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                            ptr(output), _ptr(state_out),
+                            _ptr(state_capture) if state_capture is not None else None,
+                            ctypes.byref(params), options, _stream_handle(device, stream))
+    if st != 0:
+        raise GdnError(st, "gdn_forward_ex")
+
+
 def gdn_rollback(state_capture, accepted, state, params: GdnParams, stream=None) -> None:
     """Enqueue the accepted-prefix rollback (C: gdn_rollback): for each
     sequence s with accepted[s] < n_tokens, state[s] = state_capture[s,
@@ -254,12 +286,15 @@ def gdn_rollback(state_capture, accepted, state, params: GdnParams, stream=None)
 
 
 def forward(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0, capture: bool = False,
-            output=None, state_out=None, state_capture=None, stream=None):
+            normalize_k: bool = False, output=None, state_out=None, state_capture=None,
+            stream=None):
     """Convenience wrapper on torch-shaped tensors:
     q, k (S, T, H_k, D_k); v (S, T, H_v, D_v); g, beta (S, T, H_v);
     state_in (S, H_v, D_v, D_k). q, k, v in f32, or all three in bf16 (then the
-    output is bf16 too; the state is f32 either way). Allocates missing outputs
-    and returns (output, state_out) or (output, state_out, state_capture)."""
+    output is bf16 too; the state is f32 either way). normalize_k: use every
+    key row as k / sqrt(sum k^2 + 1e-6) (gdn_forward_ex). Allocates missing
+    outputs and returns (output, state_out) or (output, state_out,
+    state_capture)."""
     params = params_for(q, v, q_scale_bits)
     S, T, Hv, Dv = v.shape
     Dk = q.shape[3]
@@ -272,6 +307,11 @@ def forward(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0, capture: bool 
     if capture and state_capture is None:
         state_capture = torch.empty((S, T, Hv, Dv, Dk), dtype=torch.float32,
                                     device=q.device)
+    if normalize_k:
+        gdn_forward_ex(q, k, v, g, beta, state_in, output, state_out,
+                       state_capture if capture else None, params,
+                       OPT_NORMALIZE_K | (OPT_BF16_IO if bf16 else 0), stream)
+        return (output, state_out, state_capture) if capture else (output, state_out)
     if bf16:
         gdn_forward_bf16(q, k, v, g, beta, state_in, output, state_out,
                          state_capture if capture else None, params, stream)

@@ -59,7 +59,7 @@ bool aligned(const void *p, uintptr_t n) {
 gdn_status forward(const void *q, const void *k, const void *v, const float *g,
                    const float *beta, const float *state_in, void *output,
                    float *state_out, float *capture, const gdn_params *p,
-                   void *stream, uint32_t io_bytes) {
+                   void *stream, uint32_t io_bytes, bool normalize_k = false) {
   gdn_status st = gdn_check_params(p);
   if (st != GDN_OK) return st;
   if (!q || !k || !v || !g || !beta || !state_in || !output || !state_out)
@@ -113,6 +113,7 @@ gdn_status forward(const void *q, const void *k, const void *v, const float *g,
   a.n_seqs = p->n_seqs;
   a.q_scale = q_scale;
   a.bf16 = io_bytes == 2;
+  a.normalize_k = normalize_k;
   if (gdn::enqueue_forward(a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GDN_ERR_LAUNCH;
   return GDN_OK;
@@ -199,6 +200,19 @@ gdn_status gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
                  p, stream, 2);
 }
 
+gdn_status gdn_forward_ex(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *state_in, void *output,
+                          float *state_out, float *state_capture,
+                          const gdn_params *p, uint32_t options, void *stream) {
+  if (p == nullptr) return GDN_ERR_NULL_POINTER;
+  if ((options & ~(GDN_OPT_BF16_IO | GDN_OPT_NORMALIZE_K)) != 0u)
+    return GDN_ERR_OPTION;
+  return forward(q, k, v, g, beta, state_in, output, state_out, state_capture,
+                 p, stream, (options & GDN_OPT_BF16_IO) ? 2 : 4,
+                 (options & GDN_OPT_NORMALIZE_K) != 0u);
+}
+
 const char *gdn_status_string(gdn_status s) {
   switch (s) {
     case GDN_OK: return "success";
@@ -212,6 +226,7 @@ const char *gdn_status_string(gdn_status s) {
     case GDN_ERR_MISALIGNED: return "an array breaks the alignment rule (f32: q, k, state, capture 16 bytes; bf16: q, k 8 bytes; every array its element size)";
     case GDN_ERR_ALIASING: return "an output array overlaps another array (only state_out == state_in is allowed)";
     case GDN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case GDN_ERR_OPTION: return "an unknown bit is set in the options word";
   }
   return "unknown gdn_status";
 }

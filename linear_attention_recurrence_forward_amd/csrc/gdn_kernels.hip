@@ -246,19 +246,36 @@ struct Raw<2> {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
   }
 };
-// Store EPL staged elements (raw bits of IO type) as f32 at dst.
+// The EPL staged elements (raw bits of IO type) as f32 values.
 template <typename IO, uint32_t EPL, typename R>
-__device__ __forceinline__ void widen_store(float *dst, R raw) {
+__device__ __forceinline__ void widen(R raw, float (&out)[EPL]) {
+  static_assert(EPL == 1 || EPL == 2, "one or two elements per lane");
   if constexpr (sizeof(IO) == 4) {
-    *reinterpret_cast<R *>(dst) = raw;  // f32: the bits are the values
+    if constexpr (EPL == 2) {
+      // Element reads as values (raw[i]): bit-casting a vector member access
+      // (raw.y) has been seen to read element 0 with this compiler.
+      out[0] = __builtin_bit_cast(float, (uint32_t)raw[0]);
+      out[1] = __builtin_bit_cast(float, (uint32_t)raw[1]);
+    } else {
+      out[0] = __builtin_bit_cast(float, (uint32_t)raw);
+    }
   } else if constexpr (EPL == 2) {
     const uint32_t w = raw;  // two bf16
-    *reinterpret_cast<float2 *>(dst) = make_float2(__builtin_bit_cast(float, w << 16),
-                                                   __builtin_bit_cast(float, w & 0xFFFF0000u));
+    out[0] = __builtin_bit_cast(float, w << 16);
+    out[1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
   } else {
-    static_assert(EPL == 1, "one or two elements per lane");
-    *dst = __builtin_bit_cast(float, (uint32_t)raw << 16);
+    out[0] = __builtin_bit_cast(float, (uint32_t)raw << 16);
   }
+}
+
+// Sum over all 64 lanes of a wave, as a wave-uniform value: DPP sums within
+// each 16-lane row, then the four row sums read out lane by lane.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  auto lane_value = [&](int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  };
+  return (lane_value(0) + lane_value(16)) + (lane_value(32) + lane_value(48));
 }
 
 struct KernelArgs {
@@ -271,12 +288,16 @@ struct KernelArgs {
   float q_scale;
 };
 
+// Epsilon of the key-normalisation option (binary32 value of 1e-6).
+constexpr float kNormEps = 1e-6f;
+
 // DK: key dim. C: cells per lane per row. R: rows per lane. WAVES: waves per
 // workgroup. NB: token buffers in the prefetch ring (token t + NB - 1 is
 // requested while token t computes); NB = 1 selects the one-token path, used
 // only for n_tokens == 1. CAPTURE: also write the per-token state. IO: element
-// type of q, k, v and output (float or __bf16).
-template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO>
+// type of q, k, v and output (float or __bf16). NORMK: use every key row as
+// k / sqrt(sum k^2 + kNormEps).
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, bool NORMK>
 __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   constexpr int L = DK / C;      // lanes sharing one state row
   constexpr int G = 64 / L;      // row groups per wave
@@ -420,6 +441,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   };
   struct KQ {
     f4 k[NV], q[NV];
+    float inv;  // NORMK: 1 / sqrt(sum k^2 + kNormEps) of the token's key row
   };
   // k, q, v and output are read through descriptors based at token base_t
   // that reach to the end of this sequence; token t's row is at scalar byte
@@ -466,10 +488,27 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // token's write.
   auto columns = [&](const Tok &x) {
     KQ c;
+    c.inv = 1.f;
     if constexpr (STAGE) {
+      float kw[EPL], qw[EPL];
+      widen<IO, EPL>(x.kr, kw);
+      widen<IO, EPL>(x.qr, qw);
+      if constexpr (NORMK) {
+        // The wave holds the whole key row: its sum of squares over all lanes
+        // (lanes past the row repeat its last part and count zero). The keys
+        // stay unscaled; step() folds the factor into sk and delta, so this
+        // reduction overlaps the LDS round trip instead of preceding it.
+        float ss = 0.f;
+#pragma unroll
+        for (uint32_t e = 0; e < EPL; ++e) ss = __builtin_fmaf(kw[e], kw[e], ss);
+        c.inv = __builtin_amdgcn_rsqf(wave_sum(lane < SLANES ? ss : 0.f) + kNormEps);
+      }
       if (SLANES == 64 || lane < SLANES) {
-        widen_store<IO, EPL>(kq_row + EPL * lane, x.kr);
-        widen_store<IO, EPL>(kq_row + DK + EPL * lane, x.qr);
+#pragma unroll
+        for (uint32_t e = 0; e < EPL; ++e) {
+          kq_row[EPL * lane + e] = kw[e];
+          kq_row[DK + EPL * lane + e] = qw[e];
+        }
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -482,6 +521,14 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       for (int m = 0; m < NV; ++m) {
         c.k[m] = x.k[m];
         c.q[m] = x.q[m];
+      }
+      if constexpr (NORMK) {  // the L lanes of a row group hold the key row
+        float ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < NV; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(c.k[m][e], c.k[m][e], ss);
+        c.inv = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
       }
     }
     return c;
@@ -497,6 +544,13 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // one multiply per cell and token fewer. decay is wave-uniform.
   auto step = [&](uint32_t t, const Tok &x, bool decay, float alpha, float b, float c) {
     const KQ kq = columns(x);
+    // Normalised keys (NORMK): sk = c * inv * (cells . k) and the write adds
+    // delta * inv along the raw k, the same as using k * inv throughout.
+    float cs = c, bs = b;
+    if constexpr (NORMK) {
+      cs = c * kq.inv;
+      bs = b * kq.inv;
+    }
     if (decay)
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -515,11 +569,11 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     }
     float d[R];
     if constexpr (PAIRED) {
-      d[0] = __builtin_fmaf(-c, pair_sum<L>(part[0], part[1]), x.v[0]) * b;
+      d[0] = __builtin_fmaf(-cs, pair_sum<L>(part[0], part[1]), x.v[0]) * bs;
       d[1] = partner<L>(d[0]);  // the partner's A row is this lane's B row
     } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) d[r] = __builtin_fmaf(-c, group_sum<L>(part[r]), x.v[r]) * b;
+      for (int r = 0; r < R; ++r) d[r] = __builtin_fmaf(-cs, group_sum<L>(part[r]), x.v[r]) * bs;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -701,11 +755,11 @@ struct Geometry {
   const void *kernel;
 };
 
-template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO>
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, bool NORMK>
 constexpr Geometry make_geometry() {
   return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
                   reinterpret_cast<const void *>(
-                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO>)};
+                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO, NORMK>)};
 }
 
 // Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
@@ -728,36 +782,45 @@ constexpr Geometry make_geometry() {
 //                up (2 to 512), so one token is the only short-run case. At
 //                D_k = 64, 8 lanes per row (8 cells each): 512-token prefill
 //                145 -> 135 us against 16.
-template <bool CAPTURE, typename IO>
+template <bool CAPTURE, typename IO, bool NORMK>
 Geometry pick(uint32_t d_k, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
   switch (d_k) {
     case 32:
-      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE, IO>()
-                       : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO>();
+      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE, IO, NORMK>()
+                       : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NORMK>();
     case 64:
-      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO>()
-                       : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO>();
+      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO, NORMK>()
+                       : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO, NORMK>();
     case 128:
-      if (one_token) return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO>();
-      if constexpr (CAPTURE) return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO>();
-      return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO>();
+      if (one_token) return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO, NORMK>();
+      if constexpr (CAPTURE) return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NORMK>();
+      return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NORMK>();
     default:
       return Geometry{0, 0, nullptr};
   }
 }
 
-Geometry pick_geometry(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16) {
+template <bool NORMK>
+Geometry pick_io(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16) {
   if (bf16)
-    return capture ? pick<true, __bf16>(d_k, n_tokens) : pick<false, __bf16>(d_k, n_tokens);
-  return capture ? pick<true, float>(d_k, n_tokens) : pick<false, float>(d_k, n_tokens);
+    return capture ? pick<true, __bf16, NORMK>(d_k, n_tokens)
+                   : pick<false, __bf16, NORMK>(d_k, n_tokens);
+  return capture ? pick<true, float, NORMK>(d_k, n_tokens)
+                 : pick<false, float, NORMK>(d_k, n_tokens);
+}
+
+Geometry pick_geometry(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16,
+                       bool normalize_k) {
+  return normalize_k ? pick_io<true>(d_k, n_tokens, capture, bf16)
+                     : pick_io<false>(d_k, n_tokens, capture, bf16);
 }
 
 }  // namespace
 
 uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
                      uint32_t n_seqs, uint32_t n_tokens, bool capture) {
-  const Geometry geo = pick_geometry(d_k, n_tokens, capture, false);
+  const Geometry geo = pick_geometry(d_k, n_tokens, capture, false, false);
   if (geo.kernel == nullptr) return 0;
   const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
   return row_blocks * n_v_heads * n_seqs;
@@ -765,7 +828,7 @@ uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
 
 hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   const bool capture = f.capture != nullptr;
-  const Geometry geo = pick_geometry(f.d_k, f.n_tokens, capture, f.bf16);
+  const Geometry geo = pick_geometry(f.d_k, f.n_tokens, capture, f.bf16, f.normalize_k);
   if (geo.kernel == nullptr) return hipErrorInvalidValue;
   const uint32_t row_blocks =
       (f.d_v + geo.rows_per_block - 1) / geo.rows_per_block;

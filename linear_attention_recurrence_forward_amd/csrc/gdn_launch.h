@@ -18,6 +18,7 @@ struct ForwardArgs {
   uint32_t d_k, d_v, n_k_heads, n_v_heads, n_tokens, n_seqs;
   float q_scale;
   bool bf16;
+  bool normalize_k;  // use k / sqrt(sum k^2 + 1e-6) per key row
 };
 
 // Number of workgroups the chosen launch geometry needs (for the host-side

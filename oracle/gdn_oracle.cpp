@@ -73,8 +73,10 @@ float scale_from_bits(uint32_t bits) {
   return f;
 }
 
-template <typename real>
-int run(const float *q, const float *k, const float *v, const float *g,
+// kreal: element type of the key array the recurrence reads (the caller's f32
+// keys, or keys normalised in the oracle's own precision).
+template <typename real, typename kreal>
+int run(const float *q, const kreal *k, const float *v, const float *g,
         const float *beta, const float *state_in, const oracle_gdn_shape *p,
         int head_map, real *output, real *state_out, real *capture) {
   if (p == nullptr || q == nullptr || k == nullptr || v == nullptr ||
@@ -159,6 +161,47 @@ int run(const float *q, const float *k, const float *v, const float *g,
   return 0;
 }
 
+// Key normalisation option (in the benchmark configurations' input recipe,
+// not on the pages): every key row k[s,t,kh,:] is replaced by
+//   k / sqrt(sum_j k_j^2 + eps),  eps = 1e-6 (the binary32 value),
+// the plain L2 normalisation with an epsilon that keeps an all-zero row at
+// zero. Computed in the oracle's precision, sum over j in increasing order.
+constexpr float kNormEps = 1e-6f;
+
+template <typename real>
+std::vector<real> normalized_keys(const float *k, const oracle_gdn_shape *p) {
+  const uint64_t Dk = p->d_k;
+  const uint64_t rows = (uint64_t)p->n_seqs * p->n_tokens * p->n_k_heads;
+  std::vector<real> out(rows * Dk);
+  for (uint64_t r = 0; r < rows; ++r) {
+    const float *kr = k + r * Dk;
+    real ss = 0;
+    for (uint64_t j = 0; j < Dk; ++j)
+      ss = ss + static_cast<real>(kr[j]) * static_cast<real>(kr[j]);
+    const real inv = real(1) / std::sqrt(ss + static_cast<real>(kNormEps));
+    for (uint64_t j = 0; j < Dk; ++j) out[r * Dk + j] = static_cast<real>(kr[j]) * inv;
+  }
+  return out;
+}
+
+// Option bits of the _ex entry points.
+constexpr uint32_t kOptNormalizeK = 2u;
+
+template <typename real>
+int run_ex(const float *q, const float *k, const float *v, const float *g,
+           const float *beta, const float *state_in, const oracle_gdn_shape *p,
+           int head_map, uint32_t options, real *output, real *state_out,
+           real *capture) {
+  if ((options & ~kOptNormalizeK) != 0u) return 5;
+  if (!(options & kOptNormalizeK))
+    return run<real, float>(q, k, v, g, beta, state_in, p, head_map, output,
+                            state_out, capture);
+  if (p == nullptr || k == nullptr) return 1;
+  const std::vector<real> kn = normalized_keys<real>(k, p);
+  return run<real, real>(q, kn.data(), v, g, beta, state_in, p, head_map,
+                         output, state_out, capture);
+}
+
 // bfloat16 is the top half of an IEEE binary32 value (sign, 8 exponent bits,
 // 7 fraction bits). Widening is exact; narrowing rounds to nearest, ties to
 // even on the 16 dropped bits; NaN stays NaN (quiet, sign kept).
@@ -189,8 +232,8 @@ int oracle_gdn_forward_f32(const float *q, const float *k, const float *v,
                            const float *state_in, const oracle_gdn_shape *p,
                            int head_map, float *output, float *state_out,
                            float *state_capture) {
-  return run<float>(q, k, v, g, beta, state_in, p, head_map, output, state_out,
-                    state_capture);
+  return run<float, float>(q, k, v, g, beta, state_in, p, head_map, output,
+                           state_out, state_capture);
 }
 
 int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
@@ -198,20 +241,40 @@ int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
                            const float *state_in, const oracle_gdn_shape *p,
                            int head_map, double *output, double *state_out,
                            double *state_capture) {
-  return run<double>(q, k, v, g, beta, state_in, p, head_map, output,
-                     state_out, state_capture);
+  return run<double, float>(q, k, v, g, beta, state_in, p, head_map, output,
+                            state_out, state_capture);
+}
+
+// As the two above, with option bits: 2 = normalise every key row first
+// (normalized_keys). Other bits are an error (5).
+int oracle_gdn_forward_ex_f32(const float *q, const float *k, const float *v,
+                              const float *g, const float *beta,
+                              const float *state_in, const oracle_gdn_shape *p,
+                              int head_map, uint32_t options, float *output,
+                              float *state_out, float *state_capture) {
+  return run_ex<float>(q, k, v, g, beta, state_in, p, head_map, options, output,
+                       state_out, state_capture);
+}
+
+int oracle_gdn_forward_ex_f64(const float *q, const float *k, const float *v,
+                              const float *g, const float *beta,
+                              const float *state_in, const oracle_gdn_shape *p,
+                              int head_map, uint32_t options, double *output,
+                              double *state_out, double *state_capture) {
+  return run_ex<double>(q, k, v, g, beta, state_in, p, head_map, options,
+                        output, state_out, state_capture);
 }
 
 // bf16 inputs and output (the "future add" of mlx-native 0.4.0
 // src/ops/gated_delta_net.rs, module doc "Dtype / precision"): q, k, v are
 // widened exactly, the recurrence runs in f32 as above, and each output is
 // rounded to the nearest bf16. State and capture stay f32.
-int oracle_gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
-                            const uint16_t *v, const float *g,
-                            const float *beta, const float *state_in,
-                            const oracle_gdn_shape *p, int head_map,
-                            uint16_t *output, float *state_out,
-                            float *state_capture) {
+int oracle_gdn_forward_ex_bf16(const uint16_t *q, const uint16_t *k,
+                               const uint16_t *v, const float *g,
+                               const float *beta, const float *state_in,
+                               const oracle_gdn_shape *p, int head_map,
+                               uint32_t options, uint16_t *output,
+                               float *state_out, float *state_capture) {
   if (p == nullptr || q == nullptr || k == nullptr || v == nullptr ||
       output == nullptr)
     return 1;
@@ -223,11 +286,22 @@ int oracle_gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
     kf[e] = bf16_to_f32(k[e]);
   }
   for (uint64_t e = 0; e < nv; ++e) vf[e] = bf16_to_f32(v[e]);
-  const int rc = run<float>(qf.data(), kf.data(), vf.data(), g, beta, state_in,
-                            p, head_map, of.data(), state_out, state_capture);
+  const int rc = run_ex<float>(qf.data(), kf.data(), vf.data(), g, beta,
+                               state_in, p, head_map, options, of.data(),
+                               state_out, state_capture);
   if (rc != 0) return rc;
   for (uint64_t e = 0; e < nv; ++e) output[e] = f32_to_bf16(of[e]);
   return 0;
+}
+
+int oracle_gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *g,
+                            const float *beta, const float *state_in,
+                            const oracle_gdn_shape *p, int head_map,
+                            uint16_t *output, float *state_out,
+                            float *state_capture) {
+  return oracle_gdn_forward_ex_bf16(q, k, v, g, beta, state_in, p, head_map, 0u,
+                                    output, state_out, state_capture);
 }
 
 // The oracle's f32 -> bf16 rounding on its own, for the pins.

@@ -58,6 +58,26 @@ int oracle_gdn_forward_bf16(const uint16_t *q, const uint16_t *k,
 /* The oracle's f32 -> bf16 rounding alone (round to nearest, ties to even). */
 void oracle_f32_to_bf16(const float *in, uint16_t *out, uint64_t n);
 
+/* As oracle_gdn_forward_f32 / _f64 / _bf16 with option bits: 2 = normalise
+ * every key row k[s,t,kh,:] to k / sqrt(sum k^2 + 1e-6) before the recurrence
+ * (in the oracle's precision). Any other bit returns 5. */
+int oracle_gdn_forward_ex_f32(const float *q, const float *k, const float *v,
+                              const float *g, const float *beta,
+                              const float *state_in, const oracle_gdn_shape *p,
+                              int head_map, uint32_t options, float *output,
+                              float *state_out, float *state_capture);
+int oracle_gdn_forward_ex_f64(const float *q, const float *k, const float *v,
+                              const float *g, const float *beta,
+                              const float *state_in, const oracle_gdn_shape *p,
+                              int head_map, uint32_t options, double *output,
+                              double *state_out, double *state_capture);
+int oracle_gdn_forward_ex_bf16(const uint16_t *q, const uint16_t *k,
+                               const uint16_t *v, const float *g,
+                               const float *beta, const float *state_in,
+                               const oracle_gdn_shape *p, int head_map,
+                               uint32_t options, uint16_t *output,
+                               float *state_out, float *state_capture);
+
 /* Accepted-prefix rollback: state[s] = state_capture[s, accepted[s]] for every
  * sequence whose accepted[s] < n_tokens (others untouched). Uses d_k, d_v,
  * n_v_heads, n_tokens, n_seqs of p. */

@@ -70,6 +70,22 @@ def _load(path: str | None = None):
                 fn.argtypes = [fp] * 6 + [ctypes.POINTER(_Shape), ctypes.c_int,
                                           rp, rp, rp]
                 fn.restype = ctypes.c_int
+            for name, real in (("oracle_gdn_forward_ex_f32", ctypes.c_float),
+                               ("oracle_gdn_forward_ex_f64", ctypes.c_double)):
+                if hasattr(lib, name):
+                    fn = getattr(lib, name)
+                    fp = ctypes.POINTER(ctypes.c_float)
+                    rp = ctypes.POINTER(real)
+                    fn.argtypes = [fp] * 6 + [ctypes.POINTER(_Shape), ctypes.c_int,
+                                              ctypes.c_uint32, rp, rp, rp]
+                    fn.restype = ctypes.c_int
+            if hasattr(lib, "oracle_gdn_forward_ex_bf16"):
+                u16 = ctypes.POINTER(ctypes.c_uint16)
+                fn = lib.oracle_gdn_forward_ex_bf16
+                fn.argtypes = [u16, u16, u16] + [ctypes.POINTER(ctypes.c_float)] * 3 + [
+                    ctypes.POINTER(_Shape), ctypes.c_int, ctypes.c_uint32, u16,
+                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]
+                fn.restype = ctypes.c_int
             if hasattr(lib, "oracle_gdn_forward_bf16"):
                 u16 = ctypes.POINTER(ctypes.c_uint16)
                 fn = lib.oracle_gdn_forward_bf16
@@ -98,13 +114,19 @@ def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
+# Option bit of the oracle's _ex entry points: normalise every key row.
+OPT_NORMALIZE_K = 2
+
+
 def reference(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
               head_map: int = HEAD_MAP_MOD, capture: bool = False,
-              precision: str = "f32", library: str | None = None):
+              precision: str = "f32", normalize_k: bool = False,
+              library: str | None = None):
     """Run the oracle. Returns (output, state_out) or (output, state_out, capture).
 
     Shapes are taken from the arrays: q is (S, T, H_k, D_k), v is (S, T, H_v, D_v).
     precision="f32" is the oracle proper; "f64" is the binary64 shadow.
+    normalize_k replaces every key row by k / sqrt(sum k^2 + 1e-6) first.
     library selects another build of gdn_oracle.cpp (the planted-mistake
     tests use this); None means the regular build.
     """
@@ -127,11 +149,16 @@ def reference(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
     cap = np.empty((S, T, Hv, Dv, Dk), dtype=dtype) if capture else None
     shape = _Shape(Dk, Dv, Hk, Hv, T, S, q_scale_bits & 0xFFFFFFFF)
     fp = ctypes.c_float
-    rc = getattr(_load(library), fname)(
-        _ptr(q, fp), _ptr(k, fp), _ptr(v, fp), _ptr(g, fp), _ptr(beta, fp),
-        _ptr(state_in, fp), ctypes.byref(shape), head_map,
-        _ptr(out, real), _ptr(st, real),
-        _ptr(cap, real) if cap is not None else ctypes.POINTER(real)())
+    lib = _load(library)
+    common = (_ptr(q, fp), _ptr(k, fp), _ptr(v, fp), _ptr(g, fp), _ptr(beta, fp),
+              _ptr(state_in, fp), ctypes.byref(shape), head_map)
+    outs = (_ptr(out, real), _ptr(st, real),
+            _ptr(cap, real) if cap is not None else ctypes.POINTER(real)())
+    if normalize_k:
+        fname = fname.replace("oracle_gdn_forward_", "oracle_gdn_forward_ex_")
+        rc = getattr(lib, fname)(*common, OPT_NORMALIZE_K, *outs)
+    else:
+        rc = getattr(lib, fname)(*common, *outs)
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return (out, st, cap) if capture else (out, st)
@@ -170,7 +197,7 @@ def to_bf16(x, *, library: str | None = None):
 
 def reference_bf16(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
                    head_map: int = HEAD_MAP_MOD, capture: bool = False,
-                   library: str | None = None):
+                   normalize_k: bool = False, library: str | None = None):
     """bf16 variant: q, k, v are uint16 bf16 bit patterns (shapes as in
     reference); returns (output as uint16 bf16 bits, state_out f32[, capture])."""
     q16, k16, v16 = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v))
@@ -183,9 +210,10 @@ def reference_bf16(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
     shape = _Shape(Dk, Dv, Hk, Hv, T, S, q_scale_bits & 0xFFFFFFFF)
     u16 = ctypes.POINTER(ctypes.c_uint16)
     fp = ctypes.c_float
-    rc = _load(library).oracle_gdn_forward_bf16(
+    rc = _load(library).oracle_gdn_forward_ex_bf16(
         q16.ctypes.data_as(u16), k16.ctypes.data_as(u16), v16.ctypes.data_as(u16),
         _ptr(g, fp), _ptr(beta, fp), _ptr(state_in, fp), ctypes.byref(shape), head_map,
+        OPT_NORMALIZE_K if normalize_k else 0,
         out.ctypes.data_as(u16), _ptr(st, fp),
         _ptr(cap, fp) if cap is not None else ctypes.POINTER(fp)())
     if rc != 0:

@@ -403,6 +403,53 @@ def pin_bf16(ref, ref_bf16=None):
     assert_within(lo, o32, 2.0 ** -8 * np.abs(o32) + 1e-30, "bf16 output rounding")
 
 
+NORM_EPS = 1e-6  # epsilon of the key-normalisation option (binary32 value)
+
+
+def pin_normalize_k(ref):
+    """Key-normalisation option (in the benchmark configurations' input recipe,
+    not on the pages): each key row becomes k / sqrt(sum k^2 + eps).
+    (a) One-hot keys a*e_j with beta = 1, g = 0 and a zero state write
+        v_i * a / sqrt(a^2 + eps) into column j (closed form, f64; a = 3 and
+        a = 1e-4, where eps dominates), and nothing elsewhere.
+    (b) An all-zero key row stays zero: the call equals the plain call exactly.
+    (c) Random unnormalised keys: the option equals a plain call on keys
+        normalised by numpy in f64, within the f32 tolerance."""
+    S, T, Hk, Hv, Dk, Dv = 1, 1, 1, 1, 32, 4
+    v = np.arange(1, Dv + 1, dtype=np.float32).reshape(S, T, Hv, Dv)
+    zeros_s = np.zeros((S, T, Hv), np.float32)
+    state0 = np.zeros((S, Hv, Dv, Dk), np.float32)
+    for a, j0 in ((3.0, 5), (1e-4, 17)):
+        k = np.zeros((S, T, Hk, Dk), np.float32)
+        k[0, 0, 0, j0] = a
+        q = np.zeros_like(k)
+        q[0, 0, 0, j0] = 1.0
+        out, st = ref(q, k, v, zeros_s, zeros_s + 1, state0, normalize_k=True)
+        a32 = np.float64(np.float32(a))
+        khat = a32 / np.sqrt(a32 * a32 + np.float64(np.float32(NORM_EPS)))
+        expect = np.zeros((S, Hv, Dv, Dk))
+        expect[0, 0, :, j0] = v[0, 0, 0].astype(np.float64) * khat
+        assert_within(st, expect, 8 * U32 * np.abs(expect), f"normalised one-hot key a={a}")
+        assert_within(out[0, 0, 0], expect[0, 0, :, j0], 8 * U32 * np.abs(expect[0, 0, :, j0]),
+                      f"normalised one-hot output a={a}")
+    x = gqa_inputs(121, S=2, T=3)
+    x["k"][:] = 0.0
+    a = ref(**x, normalize_k=True)
+    b = ref(**x)
+    for u, w_, what in zip(a, b, ("output", "state")):
+        assert np.all(np.isfinite(u)), f"zero key row, {what}"
+        assert_equal(u, w_, f"zero key row, {what}")
+    x = gqa_inputs(122, S=2, T=4)
+    x["k"] = (x["k"] * np.float32(3.0) + np.float32(0.25)).astype(np.float32)
+    k64 = x["k"].astype(np.float64)
+    kn = (k64 / np.sqrt((k64 * k64).sum(-1, keepdims=True) + np.float32(NORM_EPS))
+          ).astype(np.float32)
+    got = ref(**x, normalize_k=True)
+    exp = ref(**dict(x, k=kn))
+    for u, w_, what in zip(got, exp, ("output", "state")):
+        assert_within(u, w_, 1e-5 + 1e-4 * np.abs(w_), f"normalised keys vs numpy, {what}")
+
+
 def golden_hand_worked(ref):
     """Hand-derived dyadic example (tests/golden/hand_worked_d2.json), bit-exact."""
     with open(os.path.join(GOLDEN, "hand_worked_d2.json")) as f:
@@ -421,4 +468,4 @@ def golden_hand_worked(ref):
 ALL_PINS = [pin_identity, pin_zeroing, pin_delta_rule, pin_chaining, pin_capture,
             pin_q_scale, pin_head_map, pin_linear_attention, pin_pure_decay,
             pin_matrix_form, pin_rollback, pin_bf16, golden_bf16_rounding,
-            golden_hand_worked]
+            pin_normalize_k, golden_hand_worked]

@@ -235,3 +235,27 @@ def test_forward_bf16_alignment(lib):
         ctypes.c_void_p(b["q"]), ctypes.c_void_p(b["k"]), ctypes.c_void_p(b["v"]),
         fake(b["g"]), fake(b["beta"]), fake(b["state_in"]), ctypes.c_void_p(b["output"]),
         fake(b["state_out"]), None, ctypes.byref(p), None)] == "GDN_ERR_ALIASING"
+
+
+def test_forward_ex_options(lib):
+    """gdn_forward_ex: unknown option bits are refused first (after params);
+    the known bits select the f32/bf16 rules of the other entry points."""
+    p = gdn.make_params(**OK)
+    a = layout(p)
+    vp = lambda n, off=0: ctypes.c_void_p(a[n] + off)  # noqa: E731
+
+    def ex(options, params=p, **off):
+        return _binding.STATUS[lib.gdn_forward_ex(
+            vp("q", off.get("q", 0)), vp("k", off.get("k", 0)), vp("v"), fake(a["g"]),
+            fake(a["beta"]), fake(a["state_in"]), vp("output"), fake(a["state_out"]),
+            None, ctypes.byref(params) if params is not None else None, options, None)]
+
+    assert ex(0, params=None) == "GDN_ERR_NULL_POINTER"
+    for bad in (4, 8, 1 << 31, 0xFFFFFFFF):
+        assert ex(bad) == "GDN_ERR_OPTION"
+        assert ex(bad | _binding.OPT_NORMALIZE_K) == "GDN_ERR_OPTION"
+    assert ex(_binding.OPT_NORMALIZE_K, params=gdn.make_params(**{**OK, "d_k": 48})) == \
+        "GDN_ERR_UNSUPPORTED_DK"
+    # f32 rule (16-byte q) without the bf16 bit, 8-byte with it
+    assert ex(_binding.OPT_NORMALIZE_K, q=8) == "GDN_ERR_MISALIGNED"
+    assert ex(_binding.OPT_NORMALIZE_K | _binding.OPT_BF16_IO, k=4) == "GDN_ERR_MISALIGNED"

@@ -41,11 +41,12 @@ def dev(x):
     return {n: torch.from_numpy(np.ascontiguousarray(x[n])).cuda() for n in NAMES}
 
 
-def run(x, *, q_scale_bits=None, capture=False, in_place=False, stream=None):
+def run(x, *, q_scale_bits=None, capture=False, in_place=False, stream=None,
+        normalize_k=False):
     """Run the HIP path on numpy inputs; returns numpy results."""
     bits = x.get("q_scale_bits", 0) if q_scale_bits is None else q_scale_bits
     d = dev(x)
-    kw = dict(q_scale_bits=bits, capture=capture, stream=stream)
+    kw = dict(q_scale_bits=bits, capture=capture, stream=stream, normalize_k=normalize_k)
     if in_place:
         kw["state_out"] = d["state_in"]
     res = gdn.forward(*(d[n] for n in NAMES), **kw)
@@ -55,10 +56,10 @@ def run(x, *, q_scale_bits=None, capture=False, in_place=False, stream=None):
     return tuple(r.cpu().numpy() for r in res)
 
 
-def ref(x, *, q_scale_bits=None, capture=False, precision="f32"):
+def ref(x, *, q_scale_bits=None, capture=False, precision="f32", normalize_k=False):
     bits = x.get("q_scale_bits", 0) if q_scale_bits is None else q_scale_bits
     return oracle.reference(**{n: x[n] for n in NAMES}, q_scale_bits=bits,
-                            capture=capture, precision=precision)
+                            capture=capture, precision=precision, normalize_k=normalize_k)
 
 
 def close(gpu, expected, what):
@@ -356,12 +357,13 @@ def bf16_inputs(x):
     return bits, wide
 
 
-def run_bf16(x, bits, *, q_scale_bits=0, capture=False):
+def run_bf16(x, bits, *, q_scale_bits=0, capture=False, normalize_k=False):
     d = {n: torch.from_numpy(bits[n].view(np.int16)).cuda().view(torch.bfloat16)
          for n in ("q", "k", "v")}
     for n in ("g", "beta", "state_in"):
         d[n] = torch.from_numpy(np.ascontiguousarray(x[n])).cuda()
-    res = gdn.forward(*(d[n] for n in NAMES), q_scale_bits=q_scale_bits, capture=capture)
+    res = gdn.forward(*(d[n] for n in NAMES), q_scale_bits=q_scale_bits, capture=capture,
+                      normalize_k=normalize_k)
     torch.cuda.synchronize()
     out = res[0].view(torch.int16).cpu().numpy().view(np.uint16)
     return (out,) + tuple(r.cpu().numpy() for r in res[1:])
@@ -464,6 +466,68 @@ def test_rollback(name):
                 assert_equal(got[s_], s_cap[0], f"rollback to {a_} == {a_ + 1}-token state")
                 _, s_plain = run(cut)
                 close(got[s_], s_plain[0], f"rollback to {a_} vs a plain {a_ + 1}-token call")
+
+
+# ------------------------------------------------------------------ key normalisation
+
+NORM_SHAPES = [
+    # d_k, d_v, n_k, n_v, T, S
+    (32, 32, 1, 2, 1, 2),
+    (32, 20, 2, 4, 9, 2),
+    (64, 48, 2, 4, 1, 2),
+    (64, 33, 1, 3, 70, 1),
+    (128, 128, 4, 8, 1, 2),
+    (128, 64, 2, 6, 65, 2),
+]
+
+
+def raw_keys(x, seed):
+    """Unnormalised keys of varied norms (the generator normalises them)."""
+    rng = np.random.default_rng(seed)
+    scale = rng.uniform(0.05, 8.0, size=x["k"].shape[:-1] + (1,))
+    k = rng.standard_normal(x["k"].shape) * scale + 0.1
+    k[0, 0, 0, :] = 0.0  # one all-zero row: stays zero
+    return dict(x, k=k.astype(np.float32))
+
+
+@pytest.mark.parametrize("capture", [False, True], ids=["plain", "capture"])
+@pytest.mark.parametrize("shape", NORM_SHAPES, ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
+def test_normalize_k(shape, capture):
+    """In-kernel key normalisation (gdn_forward_ex) against the oracle with the
+    same option, f32 and bf16, one-token and multi-token geometries."""
+    dk, dv, hk, hv, t, s_ = shape
+    w = Workload("normk", 0, dk, dv, hk, hv, t, s_)
+    x = raw_keys(make_inputs(w, seed=30 + t), seed=31 + t)
+    got = run(x, capture=capture, normalize_k=True)
+    exp = ref(x, capture=capture, normalize_k=True)
+    for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
+        assert np.all(np.isfinite(g_)), what
+        close(g_, e, f"{shape} normalised keys {what}")
+    bits, wide = bf16_inputs(x)
+    got16 = run_bf16(x, bits, capture=capture, normalize_k=True)
+    exp16 = oracle.reference_bf16(bits["q"], bits["k"], bits["v"], x["g"], x["beta"],
+                                  x["state_in"], capture=capture, normalize_k=True)
+    bf16_close(got16[0], exp16[0], f"{shape} bf16 normalised keys output")
+    close(got16[1], exp16[1], f"{shape} bf16 normalised keys state_out")
+
+
+def test_normalize_k_workloads():
+    """The option on the benchmark workloads (keys already unit-norm, so the
+    result is the plain call's within tolerance) and on raw keys."""
+    for name in ("decode", "prefill"):
+        w = WORKLOADS[name]
+        x = make_inputs(w)
+        if name == "prefill":
+            x = {n: (v[:1] if isinstance(v, np.ndarray) else v) for n, v in x.items()}
+        got = run(x, normalize_k=True)
+        plain = run(x)
+        for g_, p_, what in zip(got, plain, ("output", "state_out")):
+            close(g_, p_, f"{name}: unit-norm keys, option vs plain {what}")
+        xr = raw_keys(x, seed=40)
+        got = run(xr, normalize_k=True)
+        exp = ref(xr, normalize_k=True)
+        for g_, e, what in zip(got, exp, ("output", "state_out")):
+            close(g_, e, f"{name}: raw keys {what}")
 
 
 # ------------------------------------------------------------------ plumbing

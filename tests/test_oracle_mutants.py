@@ -68,6 +68,13 @@ MUTANTS = {
                             "for (uint64_t e = 0; e < nv; ++e) vf[e] = (float)v[e];")],
     "state_in_ignored": [("X[i * Dk + j] = static_cast<real>(state_in[at_state(s, vh, i, j)]);",
                           "X[i * Dk + j] = 0;")],
+    # Key normalisation option.
+    "normk_no_eps": [("std::sqrt(ss + static_cast<real>(kNormEps))", "std::sqrt(ss)")],
+    "normk_no_sqrt": [("real(1) / std::sqrt(ss + static_cast<real>(kNormEps))",
+                       "real(1) / (ss + static_cast<real>(kNormEps))")],
+    "normk_sum_abs": [("ss = ss + static_cast<real>(kr[j]) * static_cast<real>(kr[j]);",
+                       "ss = ss + std::fabs(static_cast<real>(kr[j]));")],
+    "normk_ignored": [("  if (!(options & kOptNormalizeK))\n", "  if (true)\n")],
 }
 
 
