@@ -542,8 +542,8 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // undecayed: sk = c * (cells . k), the write adds delta / c along k
   // (b = beta / c), y = c * (cells . q). The same recurrence reassociated,
   // one multiply per cell and token fewer. decay is wave-uniform.
-  auto step = [&](uint32_t t, const Tok &x, bool decay, float alpha, float b, float c) {
-    const KQ kq = columns(x);
+  auto step = [&](uint32_t t, const KQ &kq, const Tok &x, bool decay, float alpha, float b,
+                  float c) {
     // Normalised keys (NORMK): sk = c * inv * (cells . k) and the write adds
     // delta * inv along the raw k, the same as using k * inv throughout.
     float cs = c, bs = b;
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     Tok x;
     load_token(0, x);
     const rsrc_t gb = buffer(g_tok, 4), bb = buffer(b_tok, 4);
-    step(0, x, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
+    step(0, columns(x), x, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
   } else {
     // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
     // t0 + j (clamped to the last token; lanes past the end are never read).
@@ -683,10 +683,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         __builtin_amdgcn_wave_barrier();
       }
     };
-    auto run = [&](uint32_t t, const Tok &x) {
+    auto run = [&](uint32_t t, const KQ &kq, const Tok &x) {
       next_chunk(t);
       const float4 f = ab[t & 63u];
-      step(t, x, true, f.x, f.w, 1.f);
+      step(t, kq, x, true, f.x, f.w, 1.f);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -701,6 +701,14 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
     uint32_t t = 0;
+    // Columns of the current token. Without capture each step stages the next
+    // token's k and q rows through LDS before computing its own, so the LDS
+    // round trip runs under the current token's arithmetic (512-token prefill
+    // -2%); capture calls, bound by their writes, stage each token in its own
+    // step (4-token verify +2% the other way).
+    constexpr bool AHEAD = !CAPTURE;
+    KQ kq;
+    if constexpr (AHEAD) kq = columns(buf[0]);
     // The cells hold the state divided by kappa: the c of the previous
     // group's last token when that group ran lazily, else 1. A group's first
     // token decays by kappa * alpha, which makes the cells the state again
@@ -721,7 +729,12 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       for (int u = 0; u < NB; ++u) {
         const uint32_t ahead = t + NB - 1;
         load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
-        step(t, buf[u], u == 0 || eager, u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z);
+        // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
+        // last token when t is the last one.
+        const KQ nxt = columns(buf[AHEAD ? (u + 1) % NB : u]);
+        step(t, AHEAD ? kq : nxt, buf[u], u == 0 || eager,
+             u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z);
+        kq = nxt;
         ++t;
       }
       kappa = f[NB - 1].z;  // 1 after an eager group
@@ -735,7 +748,14 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
       if (t < T) {
-        run(t, buf[u]);
+        if constexpr (AHEAD) {
+          KQ nxt = kq;
+          if (t + 1 < T) nxt = columns(buf[u + 1]);
+          run(t, kq, buf[u]);
+          kq = nxt;
+        } else {
+          run(t, columns(buf[u]), buf[u]);
+        }
         ++t;
       }
   }
