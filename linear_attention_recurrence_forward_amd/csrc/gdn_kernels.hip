@@ -18,9 +18,9 @@
 //     a row touch 4L consecutive floats, so each load/store instruction of a
 //     wave covers whole 128-byte lines: fully coalesced dwordx4 traffic.
 //   * sk and y are sums over the L lanes of a row: butterfly DPP adds
-//     (quad_perm, row_half_mirror, row_mirror) and one ds_swizzle for L = 32.
-//     No barriers. Each butterfly step adds a value to its partner's, so
-//     every lane of the row ends with the same bits. With two rows per lane
+//     (quad_perm, row_half_mirror, row_mirror; a ds_swizzle for 32-lane
+//     groups). No barriers. Each butterfly step adds a value to its partner's,
+//     so every lane of the row ends with the same bits. With two rows per lane
 //     the halves of a row group hold the rows in swapped order, so that one
 //     butterfly reduces both rows (see partner()).
 //   * In multi-token calls every row group of a wave needs the same k and q
@@ -28,15 +28,19 @@
 //     out through a per-wave LDS slot, so the vector memory unit sees each
 //     byte once per wave instead of once per row group.
 //   * A workgroup covers rows of one (sequence, value head), so g and beta are
-//     uniform: 64 tokens' worth of alpha = exp(-g) and beta are computed once
-//     per wave (lane t holds token t0+t), parked in LDS and read per token.
+//     uniform: the per-token factors of 64 tokens are computed once per wave
+//     (lane j holds token t0+j), parked in LDS and read per ring group.
+//   * Multi-token calls without capture carry the state divided by a running
+//     product of alphas inside each ring group (the lazy form of step()): one
+//     multiply per cell and token fewer, the same recurrence reassociated.
 //   * Token t+NB-1's k, q and v are requested while token t computes (a ring
 //     of NB register sets).
 //   * Every access goes through a buffer resource (a 128-bit scalar
 //     descriptor: base address and size in bytes) plus a 32-bit per-lane byte
-//     offset that is fixed for the whole loop. Per-token bases advance with
-//     scalar arithmetic only, and the hardware range check drops any access
-//     past the descriptor's size (loads return 0, stores are discarded).
+//     offset that is fixed for the whole loop; per-token bases advance with
+//     scalar arithmetic only. Every offset is computed in range; the
+//     descriptor size is a bound, not a mechanism the code relies on.
+//   * Optionally (NORMK) every key row is used L2-normalised.
 // Two launch geometries instantiate the same template: one for a single decode
 // token (HBM-bound on the state read and write; straight-line, no ring) and one
 // for multi-token calls (bound by the VALU and the vector memory unit together;
@@ -117,7 +121,8 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family.
 constexpr int kBufferWord3 = 0x00020000;
-// Cache-policy bit of buffer stores for non-temporal (streaming) writes.
+// Cache-policy bit of buffer loads and stores for non-temporal (streaming)
+// accesses.
 constexpr int kNonTemporal = 2;
 
 // Descriptor over `bytes` bytes from `base` (bytes < 2^32).
@@ -368,9 +373,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   }
 
   // Wave-uniform bases of this (s, vh): token-0 addresses and per-token
-  // strides, in elements. Descriptors per token cover exactly one token's
-  // row of k/q (D_k floats), v/output (D_v floats) or capture (D_v x D_k).
-  // The host guarantees d_v * d_k * 4 < 2^32.
+  // strides, in elements. The k/q/v descriptors start at a token's row and
+  // reach the end of the sequence (see rebase); state and capture descriptors
+  // cover one head (D_v x D_k floats; the host guarantees d_v * d_k * 4 <
+  // 2^32).
   const uint64_t tok0 = (uint64_t)s * T;                   // first token of s
   const char *k_tok = static_cast<const char *>(a.k) + ((tok0 * Hk + kh) * DK) * IB;
   const char *q_tok = static_cast<const char *>(a.q) + ((tok0 * Hk + kh) * DK) * IB;
