@@ -820,8 +820,10 @@ Geometry pick(uint32_t d_k, uint32_t n_tokens) {
                        : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO, NORMK>();
     case 128:
       if (one_token) return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO, NORMK>();
-      if constexpr (CAPTURE) return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NORMK>();
-      return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NORMK>();
+      if constexpr (CAPTURE)
+        return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NORMK>();
+      else
+        return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NORMK>();
     default:
       return Geometry{0, 0, nullptr};
   }
