@@ -78,10 +78,12 @@ def kernel_digest() -> str:
     return build.source_digest()
 
 
-def traffic_from_profiles(workload: str, digest: str, kernel: str = KERNEL_NAME):
+def traffic_from_profiles(workload: str, digest: str, kernel: str = KERNEL_NAME,
+                          profiles: str | None = None):
     """HBM bytes per launch measured with rocprofv3 counters for this exact
     kernel build (None when absent or taken on another build)."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
+    profiles = profiles or os.path.join(ROOT, "profiles")
+    path = os.path.join(profiles, f"{kernel}_{workload}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -113,7 +115,8 @@ def workload_info(name: str, io: str = "f32"):
     return w, KERNEL_NAME, w.algorithmic_bytes(), w.description
 
 
-def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict) -> str:
+def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict,
+                      out_dir: str | None = None) -> str:
     """Summaries under profiles/ from rocprofv3 CSV output (see --summarize-rocprof):
     the kernel-trace statistics of every kernel, and the HBM bytes per launch of
     gdn_recurrent from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
@@ -165,15 +168,15 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict) -
                      f"{d['factor']:.4f} | {b:,.0f} |")
     lines += ["", f"Total HBM traffic per launch: {fetch + write:,.0f} B; algorithmic: "
               f"{alg:,} B (ratio {(fetch + write) / alg:.3f}).", ""]
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    md = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    md = os.path.join(out_dir, f"{kernel}_{workload}.md")
     with open(md, "w") as f:
         f.write("\n".join(lines))
     rec = dict(kernel=kernel, workload=workload, kernel_digest=digest,
                hbm_bytes_per_launch=fetch + write, fetch_bytes=fetch, write_bytes=write,
                algorithmic_bytes=alg, counters=per, calibration_copy_mib=calib_mib)
-    with open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json"),
-              "w") as f:
+    with open(os.path.join(out_dir, f"{kernel}_{workload}_hbm_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     return md
 

@@ -1,0 +1,127 @@
+"""bench.py's host logic (no GPU): the one-GPU rule, the algorithmic work of
+each workload written out from its definition, and the rocprofv3 summary
+arithmetic on synthetic counter files."""
+
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from linear_attention_recurrence_forward_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stderr
+    assert res.stdout == ""
+
+
+# Bytes each workload must move once, written out term by term: state read and
+# written, q and k once per key head, v and output once, g and beta once,
+# capture once (elements x bytes).
+def expected_bytes(d_k, d_v, hk, hv, t, s, capture=False, io=4):
+    state = d_k * d_v * hv * s
+    return (4 * 2 * state + io * t * s * (d_k * hk) * 2 + io * t * s * (d_v * hv) * 2
+            + 4 * t * s * hv * 2 + (4 * t * state if capture else 0))
+
+
+@pytest.mark.parametrize("name,shape,capture,total", [
+    ("decode", (128, 128, 16, 48, 1, 1), False, 6_357_376),
+    ("batched_decode", (128, 128, 16, 32, 1, 64), False, 271_597_568),
+    ("spec_verify", (128, 128, 8, 8, 4, 8), True, 25_692_160),
+    ("prefill", (128, 128, 16, 48, 512, 4), False, 160_169_984),
+])
+def test_algorithmic_bytes(bench, name, shape, capture, total):
+    w, kernel, alg, _ = bench.workload_info(name)
+    assert (w.d_k, w.d_v, w.n_k_heads, w.n_v_heads, w.n_tokens, w.n_seqs) == shape
+    assert alg == expected_bytes(*shape, capture=capture) == total
+    assert kernel == "gdn_recurrent"
+    _, _, alg16, _ = bench.workload_info(name, "bf16")
+    assert alg16 == expected_bytes(*shape, capture=capture, io=2)
+
+
+def test_rollback_bytes(bench):
+    w, kernel, alg, _ = bench.workload_info("rollback")
+    state = w.d_k * w.d_v * w.n_v_heads * w.n_seqs
+    assert kernel == "gdn_rollback_kernel"
+    assert alg == 4 * 2 * state + 4 * w.n_seqs  # slice read, state written, indexes
+
+
+def test_flops():
+    w = WORKLOADS["prefill"]
+    # one multiply and three multiply-adds per state cell per token
+    assert w.flops() == 7 * 128 * 128 * 48 * 512 * 4 == 11_274_289_152
+
+
+def write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write(",".join(header) + "\n")
+        for r in rows:
+            f.write(",".join(f'"{v}"' for v in r) + "\n")
+
+
+def test_summarize_rocprof(bench, tmp_path):
+    """Counters scaled by what they read for the calibration copy: FETCH_SIZE
+    reads half (factor 2), WRITE_SIZE all (factor 1) in this fixture."""
+    src, out = tmp_path / "prof", tmp_path / "profiles"
+    wl, digest = "decode", "abc123"
+    for log in (f"kt_{wl}.log", f"pmc_FETCH_SIZE_{wl}.log", f"pmc_WRITE_SIZE_{wl}.log"):
+        os.makedirs(src, exist_ok=True)
+        with open(src / log, "w") as f:
+            f.write("noise\n" + json.dumps({"kernel_digest": digest}) + "\n")
+    write_csv(str(src / f"kt_{wl}" / "run_kernel_stats.csv"),
+              ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+              [["void gdn::gdn_recurrent<128>", 220, 3650.0, 2800.0, 7000.0, 30.0],
+               ["__amd_rocclr_copyBuffer", 10, 3000.0, 2000.0, 9000.0, 70.0]])
+    calib_mib = 1024
+    for ctr, copy_kib, ours in (("FETCH_SIZE", 524288.0, [1600.0, 1700.0]),
+                                ("WRITE_SIZE", 1048576.0, [3000.0, 3000.0])):
+        write_csv(str(src / f"pmc_{ctr}_{wl}" / "run_counter_collection.csv"),
+                  ["Kernel_Name", "Counter_Value"],
+                  [["__amd_rocclr_copyBuffer", 10.0], ["__amd_rocclr_copyBuffer", copy_kib]]
+                  + [["void gdn::gdn_recurrent<128>", v] for v in ours])
+    md = bench.summarize_rocprof(str(src), wl, calib_mib,
+                                 dict(kt="kt-cmd", fetch="fetch-cmd", write="write-cmd"),
+                                 out_dir=str(out))
+    with open(out / f"gdn_recurrent_{wl}_hbm_traffic.json") as f:
+        rec = json.load(f)
+    fetch = 1650.0 * 2 * 1024
+    write = 3000.0 * 1 * 1024
+    assert rec["kernel_digest"] == digest
+    assert rec["fetch_bytes"] == pytest.approx(fetch)
+    assert rec["write_bytes"] == pytest.approx(write)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(fetch + write)
+    text = open(md).read()
+    assert "kt-cmd" in text and "fetch-cmd" in text and "write-cmd" in text
+    assert f"ratio {(fetch + write) / 6_357_376:.3f}" in text
+    assert bench.traffic_from_profiles(wl, digest, profiles=str(out)) == \
+        pytest.approx(fetch + write)
+    assert bench.traffic_from_profiles(wl, "other-build", profiles=str(out)) is None
+    assert bench.traffic_from_profiles("prefill", digest, profiles=str(out)) is None
+
+
+def test_summarize_rocprof_refuses_mixed_builds(bench, tmp_path):
+    src = tmp_path / "prof"
+    os.makedirs(src)
+    for i, log in enumerate(("kt_decode.log", "pmc_FETCH_SIZE_decode.log",
+                             "pmc_WRITE_SIZE_decode.log")):
+        with open(src / log, "w") as f:
+            f.write(json.dumps({"kernel_digest": f"build{i % 2}"}) + "\n")
+    with pytest.raises(SystemExit, match="disagree"):
+        bench.summarize_rocprof(str(src), "decode", 1024, {}, out_dir=str(tmp_path / "o"))
