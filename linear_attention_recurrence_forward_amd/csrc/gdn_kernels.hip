@@ -422,6 +422,19 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < NV; ++m) st[r][m] = load4_stream(s_in, cell[r] + m * 16 * L);
+  // Register element e of a cell vector holds column (e + ROT) % 4 of its four
+  // columns. The k/q column vectors arrive in aligned register quads, as the
+  // state does, so with ROT = 0 every multiply-add would read cell and key (or
+  // query) element e from the same VGPR bank, and a quarter of them a third
+  // operand from that bank too, which costs the VALU a second cycle. ROT = 1
+  // puts them in different banks (multi-token calls without capture; capture
+  // stores the cells every token and keeps ROT = 0).
+  constexpr int ROT = (NB > 1 && !CAPTURE) ? 1 : 0;
+  if constexpr (ROT == 1)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < NV; ++m) st[r][m] = st[r][m].yzwx;
 
   // Multi-token calls stage k and q through LDS. All G row groups of a wave
   // need the same k and q columns, so direct per-lane loads would pull every
@@ -570,7 +583,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       for (int m = 0; m < NV; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          part[r] = __builtin_fmaf(st[r][m][e], kq.k[m][e], part[r]);
+          part[r] = __builtin_fmaf(st[r][m][e], kq.k[m][(e + ROT) % 4], part[r]);
         }
     }
     float d[R];
@@ -588,8 +601,8 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       for (int m = 0; m < NV; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          st[r][m][e] = __builtin_fmaf(d[r], kq.k[m][e], st[r][m][e]);
-          part[r] = __builtin_fmaf(st[r][m][e], kq.q[m][e], part[r]);
+          st[r][m][e] = __builtin_fmaf(d[r], kq.k[m][(e + ROT) % 4], st[r][m][e]);
+          part[r] = __builtin_fmaf(st[r][m][e], kq.q[m][(e + ROT) % 4], part[r]);
         }
     }
     const bool mine = slot_t == (t & (TB - 1));
@@ -770,7 +783,8 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   for (int r = 0; r < R; ++r)
     if (ok[r])
 #pragma unroll
-      for (int m = 0; m < NV; ++m) store4_stream(s_out, cell[r] + m * 16 * L, st[r][m]);
+      for (int m = 0; m < NV; ++m)
+        store4_stream(s_out, cell[r] + m * 16 * L, ROT == 1 ? st[r][m].wxyz : st[r][m]);
 }
 
 // ---------------------------------------------------------------- geometry
