@@ -109,10 +109,39 @@ __device__ __forceinline__ float partner(float x) {
   if constexpr (L == 16) return dpp<kDppRor8>(x);       // lane ^ 8
 }
 
+// Partial of the lane's A row over its own and its partner's columns, given
+// the A and B partials (paired layout).
+template <int L>
+__device__ __forceinline__ float pair_part(float a, float b) {
+  return a + partner<L>(b);
+}
+
 // Sum of the lane's A row given the A and B partials (paired layout).
 template <int L>
 __device__ __forceinline__ float pair_sum(float a, float b) {
-  return group_sum<L / 2>(a + partner<L>(b));
+  return group_sum<L / 2>(pair_part<L>(a, b));
+}
+
+// Reduce-scatter over H aligned lanes (H = 2, 4 or 8): on entry w[i] holds
+// the lane's partial of item i (i < H); on return w[0] of lane h (the lane's
+// index within its H lanes) holds item h summed over the H lanes. Each level
+// halves the items a lane keeps: with span S, a lane keeps the items whose
+// bit S equals its own bit S and sends the others to a lane with the
+// opposite bit (S = 4: lane -> 7 - lane, S = 2: lane ^ 2, S = 1: lane ^ 1),
+// so H - 1 cross-lane adds reduce all H items instead of H * log2(H).
+template <int S, int H>
+__device__ __forceinline__ void scatter_sum(float (&w)[H], uint32_t h) {
+  static_assert(S == 1 || S == 2 || S == 4, "span of 1, 2 or 4 lanes");
+  const bool hi = (h & S) != 0;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const float keep = hi ? w[S + i] : w[i];
+    const float send = hi ? w[i] : w[S + i];
+    if constexpr (S == 4) w[i] = keep + dpp<kDppHalfMirror>(send);
+    if constexpr (S == 2) w[i] = keep + dpp<kDppXor2>(send);
+    if constexpr (S == 1) w[i] = keep + dpp<kDppXor1>(send);
+  }
+  if constexpr (S > 1) scatter_sum<S / 2>(w, h);
 }
 
 // ---------------------------------------------------------------- buffers
@@ -409,6 +438,16 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // later prefetch behind its write acknowledgement.
   constexpr uint32_t TB = PAIRED ? L / 2 : L;  // divides 64
   const uint32_t slot_t = sub % TB;            // token slot of this lane
+  // Paired multi-token calls defer the sums: token slot j keeps the lane's
+  // pair-level partial of y (yp[j]), and one reduce-scatter over the TB lanes
+  // of each half per TB tokens leaves token t0 + j's output in lane j. The
+  // per-token butterfly (log2(TB) dependent cross-lane adds) leaves the
+  // token's instruction stream.
+  constexpr bool DEFER = PAIRED && NB > 1;
+  static_assert(!DEFER || NB % TB == 0, "ring groups hold whole output batches");
+  float yp[DEFER ? TB : 1];
+#pragma unroll
+  for (uint32_t j = 0; j < (DEFER ? TB : 1); ++j) yp[j] = 0.f;
   float yk[NY];
   uint32_t yoff[NY];  // lane's output address: row r of token t0 + slot_t
 #pragma unroll
@@ -561,8 +600,12 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // undecayed: sk = c * (cells . k), the write adds delta / c along k
   // (b = beta / c), y = c * (cells . q). The same recurrence reassociated,
   // one multiply per cell and token fewer. decay is wave-uniform.
-  auto step = [&](uint32_t t, const KQ &kq, const Tok &x, bool decay, float alpha, float b,
-                  float c) {
+  // j: the token's output slot t % TB when ring groups hold whole output
+  // batches (NB % TB == 0), a constant after unrolling. may_end: t may be the
+  // last token (in a ring group only the last token can be, and it then ends
+  // an output batch anyway).
+  auto step = [&](uint32_t t, uint32_t j, bool may_end, const KQ &kq, const Tok &x, bool decay,
+                  float alpha, float b, float c) {
     // Normalised keys (NORMK): sk = c * inv * (cells . k) and the write adds
     // delta * inv along the raw k, the same as using k * inv throughout.
     float cs = c, bs = b;
@@ -606,7 +649,15 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         }
     }
     const bool mine = slot_t == (t & (TB - 1));
-    if constexpr (PAIRED) {
+    if constexpr (DEFER) {
+      // Only the flush reads the partial; the empty asm keeps the compiler
+      // from sinking the token's dot product there, which would hold every
+      // token's cells live until the end of the batch.
+      float y = c * pair_part<L>(part[0], part[1]);
+      asm volatile("" : "+v"(y));
+#pragma unroll
+      for (uint32_t i = 0; i < TB; ++i) yp[i] = i == j ? y : yp[i];
+    } else if constexpr (PAIRED) {
       const float y = c * pair_sum<L>(part[0], part[1]);
       yk[0] = mine ? y : yk[0];
     } else {
@@ -616,12 +667,22 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         yk[r] = mine ? y : yk[r];
       }
     }
-    if ((t & (TB - 1)) == TB - 1 || t + 1 == T) {
+    // Ring groups that hold whole batches end one only at a known token.
+    const bool flush = NB % TB == 0 ? j == TB - 1 || (may_end && t + 1 == T)
+                                    : (t & (TB - 1)) == TB - 1 || t + 1 == T;
+    if (flush) {
       // Token slots 0 .. t % TB hold tokens t0 .. t. base_t is a multiple of
       // 64 and at most t, so t0 - base_t >= 0. q_scale is applied here.
       const uint32_t t0 = t & ~(TB - 1);
       const rsrc_t o_rs = buffer(o_b, v_ext);
       const uint32_t soff = uniform((t0 - base_t) * v_bytes);
+      if constexpr (DEFER) {
+        float w[TB];
+#pragma unroll
+        for (uint32_t i = 0; i < TB; ++i) w[i] = yp[i];
+        scatter_sum<TB / 2>(w, slot_t);
+        yk[0] = w[0];
+      }
       if (slot_t <= (t & (TB - 1)))
 #pragma unroll
         for (int r = 0; r < NY; ++r)
@@ -642,7 +703,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     Tok x;
     load_token(0, x);
     const rsrc_t gb = buffer(g_tok, 4), bb = buffer(b_tok, 4);
-    step(0, columns(x), x, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
+    step(0, 0, true, columns(x), x, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
   } else {
     // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
     // t0 + j (clamped to the last token; lanes past the end are never read).
@@ -702,10 +763,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         __builtin_amdgcn_wave_barrier();
       }
     };
-    auto run = [&](uint32_t t, const KQ &kq, const Tok &x) {
+    auto run = [&](uint32_t t, uint32_t j, const KQ &kq, const Tok &x) {
       next_chunk(t);
       const float4 f = ab[t & 63u];
-      step(t, kq, x, true, f.x, f.w, 1.f);
+      step(t, j, true, kq, x, true, f.x, f.w, 1.f);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -751,7 +812,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
         // last token when t is the last one.
         const KQ nxt = columns(buf[AHEAD ? (u + 1) % NB : u]);
-        step(t, AHEAD ? kq : nxt, buf[u], u == 0 || eager,
+        step(t, u % TB, false, AHEAD ? kq : nxt, buf[u], u == 0 || eager,
              u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z);
         kq = nxt;
         ++t;
@@ -770,10 +831,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         if constexpr (AHEAD) {
           KQ nxt = kq;
           if (t + 1 < T) nxt = columns(buf[u + 1]);
-          run(t, kq, buf[u]);
+          run(t, u % TB, kq, buf[u]);
           kq = nxt;
         } else {
-          run(t, columns(buf[u]), buf[u]);
+          run(t, u % TB, columns(buf[u]), buf[u]);
         }
         ++t;
       }
