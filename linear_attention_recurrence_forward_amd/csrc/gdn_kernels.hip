@@ -495,7 +495,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   struct Tok {
     f4 k[STAGE ? 1 : NV], q[STAGE ? 1 : NV];  // direct loads (one-token calls)
     RawT kr, qr;                              // staged bytes (multi-token)
-    float v[NY];
+    float v[STAGE ? 1 : NY];                  // one-token calls; see load_vgroup
   };
   struct KQ {
     f4 k[NV], q[NV];
@@ -523,21 +523,51 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 
   auto load_token = [&](uint32_t t, Tok &x) {
     const uint32_t kq_off = uniform((t - base_t) * kq_bytes);
-    const uint32_t v_off = uniform((t - base_t) * v_bytes);
     const rsrc_t k_rs = buffer(k_b, kq_ext), q_rs = buffer(q_b, kq_ext);
-    const rsrc_t v_rs = buffer(v_b, v_ext);
     if constexpr (STAGE) {
       x.kr = Raw<RB>::load(k_rs, slane * RB, kq_off);
       x.qr = Raw<RB>::load(q_rs, slane * RB, kq_off);
     } else {
+      const uint32_t v_off = uniform((t - base_t) * v_bytes);
+      const rsrc_t v_rs = buffer(v_b, v_ext);
 #pragma unroll
       for (int m = 0; m < NV; ++m) {
         x.k[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, kq_off);
         x.q[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, kq_off);
       }
-    }
 #pragma unroll
-    for (int r = 0; r < NY; ++r) x.v[r] = Io<IO>::load1(v_rs, vrow[r], v_off);
+      for (int r = 0; r < NY; ++r) x.v[r] = Io<IO>::load1(v_rs, vrow[r], v_off);
+    }
+  };
+
+  // Multi-token calls read v once per ring group: the wave's ROWS_PER_WAVE
+  // rows (consecutive) times the group's NB tokens are at most 64 values, so
+  // lane j requests token t0 + j / ROWS_PER_WAVE of row j % ROWS_PER_WAVE
+  // (clamped to the last token and row), parks it in a per-wave LDS slot laid
+  // out row by row, and every lane reads its rows' NB values back. One
+  // vector-memory request per group instead of one per token.
+  constexpr uint32_t VT = ROWS_PER_WAVE * NB;
+  static_assert(!STAGE || VT <= 64, "one value per lane per ring group");
+  __shared__ __attribute__((aligned(16))) float v_lds[STAGE ? WAVES : 1][STAGE ? VT : 1];
+  float *const vslot = v_lds[STAGE ? wave : 0];
+  const uint32_t vl = lane < VT ? lane : VT - 1;
+  const uint32_t vl_row = rb * ROWS + wave * ROWS_PER_WAVE + vl % ROWS_PER_WAVE;
+  const uint32_t vl_off = (vl_row < Dv ? vl_row : Dv - 1) * IB;
+  const uint32_t vl_tok = vl / ROWS_PER_WAVE;
+  auto load_vgroup = [&](uint32_t t0) {
+    const uint32_t tk = t0 + vl_tok < T ? t0 + vl_tok : T - 1;  // >= base_t
+    return Io<IO>::load1(buffer(v_b, v_ext), vl_off + (tk - base_t) * v_bytes, 0);
+  };
+  // Park a group's raw v and return this lane's rows' NB values.
+  auto park_vgroup = [&](float raw, float (&vg)[NY][STAGE ? NB : 1]) {
+    if (lane < VT) vslot[(vl % ROWS_PER_WAVE) * NB + vl_tok] = raw;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < NY; ++r) {
+      const uint32_t slot = PAIRED ? (high ? 1u : 0u) : (uint32_t)r;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) vg[r][u] = vslot[(slot * G + grp) * NB + u];
+    }
   };
 
   // This lane's k and q columns of a token: from the staged LDS slot, or
@@ -604,8 +634,8 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
   // batches (NB % TB == 0), a constant after unrolling. may_end: t may be the
   // last token (in a ring group only the last token can be, and it then ends
   // an output batch anyway).
-  auto step = [&](uint32_t t, uint32_t j, bool may_end, const KQ &kq, const Tok &x, bool decay,
-                  float alpha, float b, float c) {
+  auto step = [&](uint32_t t, uint32_t j, bool may_end, const KQ &kq, const float (&v)[NY],
+                  uint32_t decay, float alpha, float b, float c) {
     // Normalised keys (NORMK): sk = c * inv * (cells . k) and the write adds
     // delta * inv along the raw k, the same as using k * inv throughout.
     float cs = c, bs = b;
@@ -613,7 +643,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       cs = c * kq.inv;
       bs = b * kq.inv;
     }
-    if (decay)
+    if (decay != 0)
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -631,11 +661,11 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     }
     float d[R];
     if constexpr (PAIRED) {
-      d[0] = __builtin_fmaf(-cs, pair_sum<L>(part[0], part[1]), x.v[0]) * bs;
+      d[0] = __builtin_fmaf(-cs, pair_sum<L>(part[0], part[1]), v[0]) * bs;
       d[1] = partner<L>(d[0]);  // the partner's A row is this lane's B row
     } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) d[r] = __builtin_fmaf(-cs, group_sum<L>(part[r]), x.v[r]) * bs;
+      for (int r = 0; r < R; ++r) d[r] = __builtin_fmaf(-cs, group_sum<L>(part[r]), v[r]) * bs;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -703,7 +733,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     Tok x;
     load_token(0, x);
     const rsrc_t gb = buffer(g_tok, 4), bb = buffer(b_tok, 4);
-    step(0, 0, true, columns(x), x, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
+    step(0, 0, true, columns(x), x.v, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
   } else {
     // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
     // t0 + j (clamped to the last token; lanes past the end are never read).
@@ -763,10 +793,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         __builtin_amdgcn_wave_barrier();
       }
     };
-    auto run = [&](uint32_t t, uint32_t j, const KQ &kq, const Tok &x) {
+    auto run = [&](uint32_t t, uint32_t j, const KQ &kq, const float (&v)[NY]) {
       next_chunk(t);
       const float4 f = ab[t & 63u];
-      step(t, j, true, kq, x, true, f.x, f.w, 1.f);
+      step(t, j, true, kq, v, true, f.x, f.w, 1.f);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -777,9 +807,13 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     // (they are never used): every request is unconditional, because a
     // request that some paths skip makes the compiler's memory-counter
     // bookkeeping wait for all outstanding loads, the prefetches included.
+    // v of the group starting at t, requested before the ring so that the
+    // first group's wait for it leaves the ring's requests in flight.
+    float v_raw = load_vgroup(0);
     Tok buf[NB];
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
+    float vg[NY][NB];
     uint32_t t = 0;
     // Columns of the current token. Without capture each step stages the next
     // token's k and q rows through LDS before computing its own, so the LDS
@@ -803,16 +837,24 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       float4 f[NB];
 #pragma unroll
       for (int u = 0; u < NB; ++u) f[u] = ab[(t & 63u) + u];
-      const bool eager =
-          CAPTURE || ((uint32_t)(eager_mask >> (t & 63u)) & ((1u << NB) - 1u)) != 0;
+      // Nonzero: the group runs eagerly. An integer, not a bool: a bool live
+      // across the group's token branches is kept as a lane mask and turned
+      // into a VGPR and back for every branch.
+      const uint32_t eager =
+          CAPTURE ? 1u : uniform((uint32_t)(eager_mask >> (t & 63u)) & ((1u << NB) - 1u));
+      park_vgroup(v_raw, vg);
+      v_raw = load_vgroup(t + NB);
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
+        float vu[NY];
+#pragma unroll
+        for (int r = 0; r < NY; ++r) vu[r] = vg[r][u];
         const uint32_t ahead = t + NB - 1;
         load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
         // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
         // last token when t is the last one.
         const KQ nxt = columns(buf[AHEAD ? (u + 1) % NB : u]);
-        step(t, u % TB, false, AHEAD ? kq : nxt, buf[u], u == 0 || eager,
+        step(t, u % TB, false, AHEAD ? kq : nxt, vu, u == 0 ? 1u : eager,
              u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z);
         kq = nxt;
         ++t;
@@ -825,16 +867,20 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
       for (int m = 0; m < NV; ++m) st[r][m] *= kappa;
     // Fewer than NB tokens remain, all already requested.
+    if (t < T) park_vgroup(v_raw, vg);
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
       if (t < T) {
+        float vu[NY];
+#pragma unroll
+        for (int r = 0; r < NY; ++r) vu[r] = vg[r][u];
         if constexpr (AHEAD) {
           KQ nxt = kq;
           if (t + 1 < T) nxt = columns(buf[u + 1]);
-          run(t, u % TB, kq, buf[u]);
+          run(t, u % TB, kq, vu);
           kq = nxt;
         } else {
-          run(t, u % TB, columns(buf[u]), buf[u]);
+          run(t, u % TB, columns(buf[u]), vu);
         }
         ++t;
       }
