@@ -130,6 +130,11 @@ SHAPES = [
     (128, 17, 3, 3, 130, 1),
     (128, 128, 16, 48, 1, 2),
     (128, 256, 1, 2, 129, 1),
+    # one ring group exactly; 64 + 8 tokens with rows that split a wave's
+    # rows unevenly; a 64-token chunk plus one D_k = 64 group
+    (128, 128, 2, 4, 8, 1),
+    (128, 40, 1, 2, 72, 2),
+    (64, 64, 1, 2, 68, 1),
 ]
 
 
