@@ -329,10 +329,16 @@ constexpr float kNormEps = 1e-6f;
 // workgroup. NB: token buffers in the prefetch ring (token t + NB - 1 is
 // requested while token t computes); NB = 1 selects the one-token path, used
 // only for n_tokens == 1. CAPTURE: also write the per-token state. IO: element
-// type of q, k, v and output (float or __bf16). NORMK: use every key row as
-// k / sqrt(sum k^2 + kNormEps).
-template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, bool NORMK>
-__global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
+// type of q, k, v and output (float or __bf16). NK: 0, or use every key row
+// as k / sqrt(sum k^2 + kNormEps), its factor computed per token (1) or a ring
+// group ahead (2, multi-token calls; see GNORM).
+// Kernels with group-ahead factors ask for 3 waves per SIMD: the prefetch of
+// the next group's key rows would otherwise take the D_k = 128 instance one
+// register past the 168 that 3 waves allow (the compiler then spills two
+// values outside the token loop instead).
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
+__global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_recurrent(KernelArgs a) {
+  constexpr bool NORMK = NK != 0;
   constexpr int L = DK / C;      // lanes sharing one state row
   constexpr int G = 64 / L;      // row groups per wave
   constexpr int NV = C / 4;      // float4 vectors per lane per row
@@ -570,6 +576,61 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     }
   };
 
+  // Key normalisation in multi-token calls: the factors 1 / sqrt(sum k^2 +
+  // kNormEps) of a ring group's NB key rows are computed one group ahead.
+  // LPT = 64 / NB lanes share a token's row, each summing the squares of EPT
+  // consecutive elements; a butterfly over the LPT lanes and one reciprocal
+  // square root give the token's factor, parked in a per-wave LDS slot and
+  // read back as broadcasts when the group starts. One butterfly and one
+  // square root per group instead of a wave-wide sum per token. A lane's
+  // slice is requested in KP parts (two when it holds 8 or more elements, at
+  // the group's start and middle) to bound the registers in flight.
+  constexpr bool GNORM = NK == 2 && STAGE;
+  constexpr uint32_t LPT = STAGE ? 64 / NB : 16;
+  constexpr uint32_t EPT = DK / LPT;
+  static_assert(!GNORM || EPT == 2 || EPT % 4 == 0, "key row split");
+  constexpr uint32_t KP = EPT >= 8 ? 2 : 1;          // parts per slice
+  constexpr uint32_t KV = EPT >= 4 ? EPT / 4 / KP : 1;  // float4 per part
+  __shared__ __attribute__((aligned(16))) float inv_lds[GNORM ? WAVES : 1][GNORM ? NB : 1];
+  float *const inv_slot = inv_lds[GNORM ? wave : 0];
+  struct KRow {
+    f4 x[KV];
+    float y[2];
+  };
+  auto load_krow = [&](uint32_t t0, uint32_t part, KRow &kr) {
+    const uint32_t tk = t0 + lane / LPT < T ? t0 + lane / LPT : T - 1;  // >= base_t
+    const uint32_t off = (tk - base_t) * kq_bytes + ((lane % LPT) * EPT + part * (EPT / KP)) * IB;
+    const rsrc_t rs = buffer(k_b, kq_ext);
+    if constexpr (EPT >= 4) {
+#pragma unroll
+      for (uint32_t i = 0; i < KV; ++i) kr.x[i] = Io<IO>::load4(rs, off + i * 4 * IB, 0);
+    } else {
+#pragma unroll
+      for (uint32_t i = 0; i < 2; ++i) kr.y[i] = Io<IO>::load1(rs, off + i * IB, 0);
+    }
+  };
+  auto add_krow = [&](const KRow &kr, float ss) {
+    if constexpr (EPT >= 4) {
+#pragma unroll
+      for (uint32_t i = 0; i < KV; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kr.x[i][e], kr.x[i][e], ss);
+    } else {
+#pragma unroll
+      for (uint32_t i = 0; i < 2; ++i) ss = __builtin_fmaf(kr.y[i], kr.y[i], ss);
+    }
+    return ss;
+  };
+  auto park_krow = [&](float ss) {
+    ss = group_sum<LPT>(ss);
+    if (lane % LPT == 0) inv_slot[lane / LPT] = __builtin_amdgcn_rsqf(ss + kNormEps);
+  };
+  auto read_krow = [&](float (&inv)[GNORM ? NB : 1]) {
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (uint32_t u = 0; u < (GNORM ? NB : 1); ++u) inv[u] = inv_slot[u];
+  };
+
   // This lane's k and q columns of a token: from the staged LDS slot, or
   // the direct loads. The slot is rewritten per token; LDS operations of a
   // wave run in order, so the reads of one token complete before the next
@@ -581,7 +642,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
       float kw[EPL], qw[EPL];
       widen<IO, EPL>(x.kr, kw);
       widen<IO, EPL>(x.qr, qw);
-      if constexpr (NORMK) {
+      if constexpr (NORMK && !GNORM) {
         // The wave holds the whole key row: its sum of squares over all lanes
         // (lanes past the row repeat its last part and count zero). The keys
         // stay unscaled; step() folds the factor into sk and delta, so this
@@ -823,6 +884,17 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
     constexpr bool AHEAD = !CAPTURE;
     KQ kq;
     if constexpr (AHEAD) kq = columns(buf[0]);
+    KRow kn;
+    float kss = 0.f;  // sum of squares of the parts already received
+    float invg[GNORM ? NB : 1];
+    if constexpr (GNORM) {
+#pragma unroll
+      for (uint32_t p = 0; p < KP; ++p) {
+        load_krow(0, p, kn);
+        kss = add_krow(kn, kss);
+      }
+      park_krow(kss);
+    }
     // The cells hold the state divided by kappa: the c of the previous
     // group's last token when that group ran lazily, else 1. A group's first
     // token decays by kappa * alpha, which makes the cells the state again
@@ -844,17 +916,31 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
           CAPTURE ? 1u : uniform((uint32_t)(eager_mask >> (t & 63u)) & ((1u << NB) - 1u));
       park_vgroup(v_raw, vg);
       v_raw = load_vgroup(t + NB);
+      if constexpr (GNORM) {
+        read_krow(invg);
+        load_krow(t + NB, 0, kn);
+      }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         float vu[NY];
 #pragma unroll
         for (int r = 0; r < NY; ++r) vu[r] = vg[r][u];
+        // The next group's factors, parked after this group's were read.
+        if constexpr (GNORM) {
+          if (KP == 2 && u == NB / 2) {
+            kss = add_krow(kn, 0.f);
+            load_krow(t - u + NB, 1, kn);
+          }
+          if (u == NB - 1) park_krow(add_krow(kn, KP == 2 ? kss : 0.f));
+        }
         const uint32_t ahead = t + NB - 1;
         load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
         // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
         // last token when t is the last one.
         const KQ nxt = columns(buf[AHEAD ? (u + 1) % NB : u]);
-        step(t, u % TB, false, AHEAD ? kq : nxt, vu, u == 0 ? 1u : eager,
+        KQ cur = AHEAD ? kq : nxt;
+        if constexpr (GNORM) cur.inv = invg[u];
+        step(t, u % TB, false, cur, vu, u == 0 ? 1u : eager,
              u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z);
         kq = nxt;
         ++t;
@@ -867,7 +953,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
 #pragma unroll
       for (int m = 0; m < NV; ++m) st[r][m] *= kappa;
     // Fewer than NB tokens remain, all already requested.
-    if (t < T) park_vgroup(v_raw, vg);
+    if (t < T) {
+      park_vgroup(v_raw, vg);
+      if constexpr (GNORM) read_krow(invg);
+    }
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
       if (t < T) {
@@ -877,10 +966,14 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(KernelArgs a) {
         if constexpr (AHEAD) {
           KQ nxt = kq;
           if (t + 1 < T) nxt = columns(buf[u + 1]);
-          run(t, u % TB, kq, vu);
+          KQ cur = kq;
+          if constexpr (GNORM) cur.inv = invg[u];
+          run(t, u % TB, cur, vu);
           kq = nxt;
         } else {
-          run(t, u % TB, columns(buf[u]), vu);
+          KQ cur = columns(buf[u]);
+          if constexpr (GNORM) cur.inv = invg[u];
+          run(t, u % TB, cur, vu);
         }
         ++t;
       }
@@ -902,11 +995,11 @@ struct Geometry {
   const void *kernel;
 };
 
-template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, bool NORMK>
+template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
 constexpr Geometry make_geometry() {
   return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
                   reinterpret_cast<const void *>(
-                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO, NORMK>)};
+                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO, NK>)};
 }
 
 // Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
@@ -929,40 +1022,47 @@ constexpr Geometry make_geometry() {
 //                up (2 to 512), so one token is the only short-run case. At
 //                D_k = 64, 8 lanes per row (8 cells each): 512-token prefill
 //                145 -> 135 us against 16.
-template <bool CAPTURE, typename IO, bool NORMK>
+template <bool CAPTURE, typename IO, int NK>
 Geometry pick(uint32_t d_k, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
+  constexpr int NK1 = NK == 2 ? 1 : NK;  // one-token calls have no ring group
   switch (d_k) {
     case 32:
-      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE, IO, NORMK>()
-                       : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NORMK>();
+      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE, IO, NK1>()
+                       : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NK>();
     case 64:
-      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO, NORMK>()
-                       : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO, NORMK>();
+      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO, NK1>()
+                       : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO, NK>();
     case 128:
-      if (one_token) return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO, NORMK>();
+      if (one_token) return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO, NK1>();
       if constexpr (CAPTURE)
-        return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NORMK>();
+        return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NK>();
       else
-        return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NORMK>();
+        return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NK>();
     default:
       return Geometry{0, 0, nullptr};
   }
 }
 
-template <bool NORMK>
+template <int NK>
 Geometry pick_io(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16) {
   if (bf16)
-    return capture ? pick<true, __bf16, NORMK>(d_k, n_tokens)
-                   : pick<false, __bf16, NORMK>(d_k, n_tokens);
-  return capture ? pick<true, float, NORMK>(d_k, n_tokens)
-                 : pick<false, float, NORMK>(d_k, n_tokens);
+    return capture ? pick<true, __bf16, NK>(d_k, n_tokens)
+                   : pick<false, __bf16, NK>(d_k, n_tokens);
+  return capture ? pick<true, float, NK>(d_k, n_tokens)
+                 : pick<false, float, NK>(d_k, n_tokens);
 }
+
+// Key normalisation takes the group-ahead factors from this many tokens on:
+// they save ~25 ns per token on the 512-token prefill but put one key-row
+// round trip before the first token (~0.3 us on a 4-token verify).
+constexpr uint32_t kGroupNormMinTokens = 16;
 
 Geometry pick_geometry(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16,
                        bool normalize_k) {
-  return normalize_k ? pick_io<true>(d_k, n_tokens, capture, bf16)
-                     : pick_io<false>(d_k, n_tokens, capture, bf16);
+  if (!normalize_k) return pick_io<0>(d_k, n_tokens, capture, bf16);
+  return n_tokens >= kGroupNormMinTokens ? pick_io<2>(d_k, n_tokens, capture, bf16)
+                                         : pick_io<1>(d_k, n_tokens, capture, bf16);
 }
 
 }  // namespace

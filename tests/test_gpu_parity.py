@@ -483,6 +483,10 @@ NORM_SHAPES = [
     (64, 33, 1, 3, 70, 1),
     (128, 128, 4, 8, 1, 2),
     (128, 64, 2, 6, 65, 2),
+    # group-ahead key factors from 16 tokens on: D_k = 32 (two elements per
+    # lane) and a call of exactly 16 tokens
+    (32, 24, 1, 2, 40, 1),
+    (128, 32, 1, 2, 16, 1),
 ]
 
 
