@@ -320,6 +320,16 @@ struct KernelArgs {
   uint32_t d_v, n_k_heads, n_v_heads, n_tokens;
   uint32_t row_blocks;  // workgroups per (sequence, value head)
   float q_scale;
+  // Descriptor sizes of the k/q and v rows of a whole sequence (the first
+  // rebase), the same for every workgroup.
+  uint32_t kq_ext0, v_ext0;
+  // ceil(2^40 / n_k_heads) when n_k_heads < 2^16 (then vh / n_k_heads is
+  // (vh * kh_magic) >> 40 for every vh < 2^24), else 0.
+  uint64_t kh_magic;
+  // One-token calls: first value head and sequence of this launch (the host
+  // splits the heads and sequences of a call into launches of at most 65535
+  // each, the limit of a grid's y and z dimensions).
+  uint32_t vh0, s0;
 };
 
 // Epsilon of the key-normalisation option (binary32 value of 1e-6).
@@ -361,12 +371,17 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   // the 8 XCDs, which receive workgroups round-robin and each have their own
   // L2, runs one contiguous range of that order: a key head's k/q rows are
   // then fetched into one L2 instead of several.
-  uint32_t s, vh, rb;
+  // One-token calls are latency-bound: a 3-D grid (row block, value head,
+  // sequence) and a multiply by a host-computed reciprocal keep integer
+  // divisions off the path to the first state load.
+  uint32_t s, vh, rb, kh;
   if constexpr (NB == 1) {
-    rb = blockIdx.x % a.row_blocks;
-    const uint32_t head = blockIdx.x / a.row_blocks;  // s * n_v_heads + vh
-    vh = head % a.n_v_heads;
-    s = head / a.n_v_heads;
+    rb = blockIdx.x;
+    vh = blockIdx.y + a.vh0;
+    s = blockIdx.z + a.s0;
+    kh = a.kh_magic != 0
+             ? vh - a.n_k_heads * (uint32_t)(((uint64_t)vh * a.kh_magic) >> 40)
+             : vh % a.n_k_heads;
   } else {
     const uint32_t n = gridDim.x, xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
     const uint32_t per = n / 8u, extra = n % 8u;
@@ -379,10 +394,10 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
     const uint32_t khead = rest % a.n_k_heads;
     s = rest / a.n_k_heads;
     vh = khead + g * a.n_k_heads;
+    kh = khead;  // vh % n_k_heads
   }
   // s * n_v_heads + vh is below the grid size (host-checked < 2^24).
   const uint32_t hs = s * a.n_v_heads + vh;
-  const uint32_t kh = vh % a.n_k_heads;  // GQA map of the capture kernel
 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -525,7 +540,14 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
     kq_ext = uniform(extent_bytes((rest * kq_step + DK) * IB));
     v_ext = uniform(extent_bytes((rest * v_step + Dv) * IB));
   };
-  rebase(0);
+  // Token 0: the bases themselves, sizes from the host.
+  base_t = 0;
+  k_b = uniform(k_tok);
+  q_b = uniform(q_tok);
+  v_b = uniform(v_tok);
+  o_b = uniform(o_tok);
+  kq_ext = a.kq_ext0;
+  v_ext = a.v_ext0;
 
   auto load_token = [&](uint32_t t, Tok &x) {
     const uint32_t kq_off = uniform((t - base_t) * kq_bytes);
@@ -1100,9 +1122,34 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   a.row_blocks = row_blocks;
   a.q_scale = f.q_scale;
 
+  const uint64_t kq_row = (uint64_t)f.n_k_heads * f.d_k, v_row = (uint64_t)f.n_v_heads * f.d_v;
+  const uint64_t io = f.bf16 ? 2 : 4, last = f.n_tokens - 1u;
+  const uint64_t kq_bytes = (last * kq_row + f.d_k) * io, v_bytes = (last * v_row + f.d_v) * io;
+  a.kq_ext0 = kq_bytes < 0xFFFFFFFFull ? (uint32_t)kq_bytes : 0xFFFFFFFFu;
+  a.v_ext0 = v_bytes < 0xFFFFFFFFull ? (uint32_t)v_bytes : 0xFFFFFFFFu;
+  a.kh_magic = f.n_k_heads < (1u << 16)
+                   ? ((1ull << 40) + f.n_k_heads - 1) / f.n_k_heads
+                   : 0;
+
   void *args[] = {&a};
-  return hipLaunchKernel(geo.kernel, dim3((uint32_t)blocks), dim3(geo.threads),
-                         args, 0, stream);
+  a.vh0 = a.s0 = 0;
+  if (f.n_tokens != 1)
+    return hipLaunchKernel(geo.kernel, dim3((uint32_t)blocks), dim3(geo.threads), args, 0,
+                           stream);
+  // One-token geometries take a 3-D grid (row block, value head, sequence),
+  // one launch per 65535 x 65535 tile of (heads, sequences).
+  constexpr uint32_t kMaxYZ = 65535;
+  for (uint32_t s0 = 0; s0 < f.n_seqs; s0 += kMaxYZ)
+    for (uint32_t vh0 = 0; vh0 < f.n_v_heads; vh0 += kMaxYZ) {
+      a.s0 = s0;
+      a.vh0 = vh0;
+      const uint32_t ny = f.n_v_heads - vh0 < kMaxYZ ? f.n_v_heads - vh0 : kMaxYZ;
+      const uint32_t nz = f.n_seqs - s0 < kMaxYZ ? f.n_seqs - s0 : kMaxYZ;
+      const hipError_t e =
+          hipLaunchKernel(geo.kernel, dim3(row_blocks, ny, nz), dim3(geo.threads), args, 0, stream);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
 }
 
 }  // namespace gdn

@@ -155,6 +155,23 @@ def test_shapes(shape, capture):
             assert_equal(got[2][:, -1], got[1], "capture[T-1] == state_out")
 
 
+@pytest.mark.parametrize("shape", [
+    (32, 1, 1, 1, 1, 70000),      # sequences past one launch's 65535
+    (32, 1, 1, 65540, 1, 1),      # value heads past 65535 (GQA ratio 65540)
+    (32, 1, 65540, 65540, 1, 1),  # key heads past 2^16: no reciprocal, plain modulo
+], ids=["seqs70000", "vheads65540", "kheads65540"])
+def test_one_token_large_grids(shape):
+    """One-token calls launch a 3-D grid (row block, value head, sequence) of
+    at most 65535 heads and sequences at a time and take vh mod n_k_heads
+    through a reciprocal below 2^16 key heads: calls past those limits."""
+    dk, dv, hk, hv, t, s = shape
+    x = make_inputs(Workload("grid", 0, dk, dv, hk, hv, t, s), seed=77)
+    got = run(x)
+    exp = ref(x)
+    for g_, e, what in zip(got, exp, ("output", "state_out")):
+        close(g_, e, f"{shape} {what}")
+
+
 def test_decay_extremes():
     """Decay factors far from the usual range, mixed into one run: g = 60
     (alpha ~ 1e-26, the state all but wiped), g = -1 (alpha = e, growth), and
