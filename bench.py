@@ -70,6 +70,10 @@ def parse_args(argv=None):
                          "(kt_<workload>/, pmc_FETCH_SIZE_<workload>/, "
                          "pmc_WRITE_SIZE_<workload>/ and the bench output of each run "
                          "in <same name>.log) and exit")
+    ap.add_argument("--summarize-valu-counters", metavar="DIR", default=None,
+                    help="write the prefill VALU/clock counter summary under profiles/ "
+                         "from the two rocprofv3 counter runs in DIR (sq1/, sq2/ and "
+                         "their bench output in sq1.log) and exit")
     return ap.parse_args(argv)
 
 
@@ -232,8 +236,97 @@ def cpu_baseline_rollback(w, budget_s: float):
                        f"{dt:.1f} s, single thread")
 
 
+VALU_PASSES = (
+    "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_ANY SQ_WAIT_INST_ANY SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_WAVES SQ_ACTIVE_INST_VALU2 SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_MUL_F32 "
+    "SQ_INSTS_VALU_ADD_F32 SQ_INSTS_VALU_FLOPS_FP32 SQ_INSTS_LDS SQ_BUSY_CU_CYCLES "
+    "GRBM_GUI_ACTIVE",
+)
+
+
+def summarize_valu_counters(src: str, out_dir: str | None = None) -> str:
+    """The prefill VALU and clock summary from two rocprofv3 counter runs of
+    the 512-token prefill (VALU_PASSES, one run each, in src/sq1 and src/sq2):
+    medians over the dispatches of gdn_recurrent, the clock under load from
+    GRBM_GUI_ACTIVE (summed over 8 XCDs), instructions per wave-token and the
+    VALU dual-issue share (SQ_ACTIVE_INST_VALU2 counts quad-cycles that issue
+    two VALU instructions)."""
+    import re
+    import statistics
+    w = WORKLOADS["prefill"]
+    med, dur, n = {}, [], 0
+    for p in ("sq1", "sq2"):
+        rows = {}
+        for r in _csv(os.path.join(src, p, "run_counter_collection.csv")):
+            if KERNEL_NAME not in r["Kernel_Name"]:
+                continue
+            d = rows.setdefault(r["Dispatch_Id"], {})
+            d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+        n = len(rows)
+        for k in {k for d in rows.values() for k in d}:
+            v = statistics.median(d[k] for d in rows.values())
+            if k == "dur":
+                dur.append(v)
+            else:
+                med[k] = v
+    with open(os.path.join(src, "sq1.log")) as f:
+        digest = re.findall(r'"kernel_digest": "([0-9a-f]+)"', f.read())[0]
+    d = statistics.median(dur)
+    waves, toks, simds = med["SQ_WAVES"], w.n_tokens, 1024
+    cyc = med["GRBM_GUI_ACTIVE"] / 8
+    qc = cyc / 4
+    valu = med["SQ_INSTS_VALU"] / simds
+    dual = med["SQ_ACTIVE_INST_VALU2"] / simds
+    single = valu - 2 * dual
+    per = lambda c: med[c] / waves / toks  # noqa: E731
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir>/{p} -o run -- python3 bench.py "
+           "--workload prefill --steps 10 --warmup 2 --no-cpu-baseline --launch direct")
+    lines = [
+        f"# {KERNEL_NAME}: prefill run, VALU and clock counters (D_k=D_v={w.d_k}, "
+        f"H_k={w.n_k_heads}, H_v={w.n_v_heads}, T={w.n_tokens}, S={w.n_seqs})", "",
+        f"kernel digest (sha256 of sources + flags) of the profiled build: `{digest}`", "",
+        "Two counter passes, each its own run (8 SQ counters and one GRBM counter per pass):",
+        "", "```", cmd.format(c=VALU_PASSES[0], p="sq1"), cmd.format(c=VALU_PASSES[1], p="sq2"),
+        "```", "", "Summary written by `python bench.py --summarize-valu-counters <dir>`.", "",
+        f"Medians over the {n} dispatches of each run (values are summed over the chip):", "",
+        "| counter | value |", "|---|---|",
+        f"| dispatch duration under the profiler | {d:.1f} µs |"]
+    for c in ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_FMA_F32",
+              "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_FLOPS_FP32",
+              "SQ_ACTIVE_INST_VALU2", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS"):
+        label = {"GRBM_GUI_ACTIVE": "GRBM_GUI_ACTIVE (8 XCDs)",
+                 "SQ_ACTIVE_INST_VALU2": "SQ_ACTIVE_INST_VALU2 (quad-cycles issuing two VALU "
+                                         "instructions)"}.get(c, c)
+        lines.append(f"| {label} | {med[c]:,.0f} |")
+    gflop = med["SQ_INSTS_VALU_FLOPS_FP32"] * 64 / 1e9
+    lines += [
+        "", f"Derived ({simds:,} SIMDs, {toks} tokens per wave):", "",
+        f"- Clock under load: {med['GRBM_GUI_ACTIVE']:,.0f} / 8 XCDs = {cyc / 1e3:.1f} k cycles in "
+        f"{d:.1f} µs = **{cyc / d / 1e3:.2f} GHz** (the 157.3 TFLOP/s peak assumes 2.4 GHz).",
+        f"- VALU instructions per wave-token: {per('SQ_INSTS_VALU'):.1f}, of which FP32 FMA "
+        f"{per('SQ_INSTS_VALU_FMA_F32'):.1f}, FP32 multiply {per('SQ_INSTS_VALU_MUL_F32'):.1f}, "
+        f"FP32 add {per('SQ_INSTS_VALU_ADD_F32'):.1f}.",
+        f"- Executed FP32 work: SQ_INSTS_VALU_FLOPS_FP32 x 64 lanes = {gflop:.2f} GFLOP per call "
+        f"(algorithmic: {w.flops() / 1e9:.2f} GFLOP, 7 flops per cell and token).",
+        f"- Issue per SIMD: {valu / 1e3:.1f} k VALU instructions in {qc / 1e3:.1f} k quad-cycles; "
+        f"{dual / 1e3:.1f} k quad-cycles issue two ({2 * dual / valu * 100:.0f}% of VALU "
+        f"instructions are dual-issued), {single / 1e3:.1f} k issue one, so a VALU issues in "
+        f"{(dual + single) / qc * 100:.0f}% of quad-cycles; all dual-issued would need "
+        f"{valu / 2 / 1e3:.1f} k.", ""]
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    path = os.path.join(out_dir, f"{KERNEL_NAME}_prefill_valu_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
 def main(argv=None):
     args = parse_args(argv)
+    if args.summarize_valu_counters:
+        print(summarize_valu_counters(args.summarize_valu_counters))
+        return 0
     if args.summarize_rocprof:
         cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt_{w} -o run "
                "-- python3 bench.py --workload {w} --steps 200 --warmup 20 --no-cpu-baseline")

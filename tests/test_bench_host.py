@@ -125,3 +125,47 @@ def test_summarize_rocprof_refuses_mixed_builds(bench, tmp_path):
             f.write(json.dumps({"kernel_digest": f"build{i % 2}"}) + "\n")
     with pytest.raises(SystemExit, match="disagree"):
         bench.summarize_rocprof(str(src), "decode", 1024, {}, out_dir=str(tmp_path / "o"))
+
+
+def test_summarize_valu_counters(bench, tmp_path):
+    """Clock, per-token instruction counts and dual-issue share from two
+    synthetic counter runs of the prefill workload."""
+    src, out = tmp_path / "pmc", tmp_path / "profiles"
+    os.makedirs(out)
+    waves, toks = 3072, 512
+    cycles = 400_000 * 8  # 2.0 GHz over 200 us, summed over 8 XCDs
+    valu = waves * toks * 64.0
+    dual = 1024 * 16_000.0  # quad-cycles issuing two, summed over 1024 SIMDs
+    counters = {
+        "sq1": dict(SQ_WAVES=waves, SQ_INSTS_VALU=valu, SQ_INSTS_SALU=1.0,
+                    SQ_INSTS_VMEM_RD=1.0, GRBM_GUI_ACTIVE=cycles),
+        "sq2": dict(SQ_WAVES=waves, SQ_ACTIVE_INST_VALU2=dual,
+                    SQ_INSTS_VALU_FMA_F32=waves * toks * 48.0,
+                    SQ_INSTS_VALU_MUL_F32=waves * toks * 4.0,
+                    SQ_INSTS_VALU_ADD_F32=waves * toks * 6.0,
+                    SQ_INSTS_VALU_FLOPS_FP32=11e9 / 64, SQ_INSTS_LDS=1.0,
+                    GRBM_GUI_ACTIVE=cycles),
+    }
+    for p, cs in counters.items():
+        rows = []
+        for disp in (1, 2, 3):
+            for name, v in cs.items():
+                rows.append([disp, "void gdn::gdn_recurrent<128>", name, v,
+                             1_000_000, 1_000_000 + 200_000])
+        rows.append([9, "__amd_rocclr_copyBuffer", "SQ_WAVES", 5.0, 0, 10])
+        write_csv(str(src / p / "run_counter_collection.csv"),
+                  ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                   "Start_Timestamp", "End_Timestamp"], rows)
+    with open(src / "sq1.log", "w") as f:
+        f.write("noise\n" + json.dumps({"kernel_digest": "feed"}) + "\n")
+    text = open(bench.summarize_valu_counters(str(src), out_dir=str(out))).read()
+    assert "`feed`" in text
+    assert "**2.00 GHz**" in text
+    assert "per wave-token: 64.0" in text and "FP32 FMA 48.0" in text
+    # 64 VALU per wave-token x 3 waves per SIMD x 512 tokens = 98.3 k per SIMD,
+    # 16 k quad-cycles issue two: 32.6% dual-issued
+    assert "98.3 k VALU instructions in 100.0 k quad-cycles" in text
+    assert "(33% of VALU instructions are dual-issued)" in text
+    assert "11.00 GFLOP per call" in text
+    for cmd in bench.VALU_PASSES:
+        assert cmd in text
