@@ -569,30 +569,46 @@ def test_side_stream():
     close(got[1], exp[1], "side stream state")
 
 
-def test_graph_replay():
+GRAPH_CASES = {
+    "decode": (WORKLOADS["decode"], {}),
+    "multi_token": (WORKLOADS["prefill"].with_(n_tokens=100, n_seqs=2), {}),
+    "multi_token_normk": (WORKLOADS["prefill"].with_(n_tokens=100, n_seqs=2),
+                          dict(normalize_k=True)),
+    "capture": (WORKLOADS["spec_verify"], dict(capture=True)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(GRAPH_CASES))
+def test_graph_replay(case):
     """Captured into a HIP graph and replayed several times (with eager work and
-    synchronisations between replays): every replay matches the eager call."""
-    w = WORKLOADS["decode"]
+    synchronisations between replays): every replay matches the eager call, for
+    the one-token, multi-token, key-normalised and capture kernels."""
+    w, opts = GRAPH_CASES[case]
     x = make_inputs(w)
     d = dev(x)
     out = torch.empty(x["v"].shape, device="cuda")
     st = torch.empty(x["state_in"].shape, device="cuda")
-    eager_out, eager_st = (t.clone() for t in gdn.forward(*(d[n] for n in NAMES)))
+    bufs = dict(output=out, state_out=st)
+    if opts.get("capture"):
+        bufs["state_capture"] = torch.empty(
+            (w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k), device="cuda")
+    eager = [t.clone() for t in gdn.forward(*(d[n] for n in NAMES), **opts)]
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            gdn.forward(*(d[n] for n in NAMES), output=out, state_out=st)
+            gdn.forward(*(d[n] for n in NAMES), **opts, **bufs)
     torch.cuda.current_stream().wait_stream(s)
+    got = [out, st] + ([bufs["state_capture"]] if opts.get("capture") else [])
     for i in range(4):
-        out.fill_(float("nan"))
-        st.fill_(float("nan"))
+        for t in got:
+            t.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out, eager_out), f"replay {i} output"
-        assert torch.equal(st, eager_st), f"replay {i} state"
+        for t, e, what in zip(got, eager, ("output", "state_out", "capture")):
+            assert torch.equal(t, e), f"{case} replay {i} {what}"
         _ = (d["q"] * 2).sum().item()  # unrelated eager work between replays
 
 
