@@ -22,7 +22,10 @@
 //     groups). No barriers. Each butterfly step adds a value to its partner's,
 //     so every lane of the row ends with the same bits. With two rows per lane
 //     the halves of a row group hold the rows in swapped order, so that one
-//     butterfly reduces both rows (see partner()).
+//     butterfly reduces both rows (see partner()). In multi-token calls with
+//     two rows per lane y needs no butterfly per token: the partials of a
+//     batch of tokens are reduced together by one reduce-scatter that leaves
+//     token t0+j's y in lane j (see scatter_sum()).
 //   * In multi-token calls every row group of a wave needs the same k and q
 //     columns; the wave loads each token's k and q rows once and hands them
 //     out through a per-wave LDS slot, so the vector memory unit sees each
@@ -33,18 +36,21 @@
 //   * Multi-token calls without capture carry the state divided by a running
 //     product of alphas inside each ring group (the lazy form of step()): one
 //     multiply per cell and token fewer, the same recurrence reassociated.
-//   * Token t+NB-1's k, q and v are requested while token t computes (a ring
-//     of NB register sets).
+//   * Token t+NB-1's k and q rows are requested while token t computes (a
+//     ring of NB register sets); v is requested once per ring group, a group
+//     ahead, for all rows of the wave.
 //   * Every access goes through a buffer resource (a 128-bit scalar
 //     descriptor: base address and size in bytes) plus a 32-bit per-lane byte
 //     offset that is fixed for the whole loop; per-token bases advance with
 //     scalar arithmetic only. Every offset is computed in range; the
 //     descriptor size is a bound, not a mechanism the code relies on.
-//   * Optionally (NORMK) every key row is used L2-normalised.
+//   * Optionally (NK) every key row is used L2-normalised, its factor folded
+//     into sk and delta: computed per token, or a ring group ahead in calls of
+//     16 tokens or more.
 // Two launch geometries instantiate the same template: one for a single decode
-// token (HBM-bound on the state read and write; straight-line, no ring) and one
-// for multi-token calls (bound by the VALU and the vector memory unit together;
-// two rows per lane share each k/q register).
+// token (HBM-bound on the state read and write; straight-line, no ring, a 3-D
+// grid) and one for multi-token calls (bound by VALU issue; two rows per lane
+// share each k/q register).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   };
   struct KQ {
     f4 k[NV], q[NV];
-    float inv;  // NORMK: 1 / sqrt(sum k^2 + kNormEps) of the token's key row
+    float inv;  // NK: 1 / sqrt(sum k^2 + kNormEps) of the token's key row
   };
   // k, q, v and output are read through descriptors based at token base_t
   // that reach to the end of this sequence; token t's row is at scalar byte
@@ -719,7 +725,7 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   // an output batch anyway).
   auto step = [&](uint32_t t, uint32_t j, bool may_end, const KQ &kq, const float (&v)[NY],
                   uint32_t decay, float alpha, float b, float c) {
-    // Normalised keys (NORMK): sk = c * inv * (cells . k) and the write adds
+    // Normalised keys (NK): sk = c * inv * (cells . k) and the write adds
     // delta * inv along the raw k, the same as using k * inv throughout.
     float cs = c, bs = b;
     if constexpr (NORMK) {
