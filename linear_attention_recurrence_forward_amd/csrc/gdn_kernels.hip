@@ -329,9 +329,11 @@ struct KernelArgs {
   // Descriptor sizes of the k/q and v rows of a whole sequence (the first
   // rebase), the same for every workgroup.
   uint32_t kq_ext0, v_ext0;
-  // ceil(2^40 / n_k_heads) when n_k_heads < 2^16 (then vh / n_k_heads is
-  // (vh * kh_magic) >> 40 for every vh < 2^24), else 0.
+  // vh / n_k_heads == (vh * kh_magic) >> kh_shift for every vh < 2^23:
+  // kh_magic = ceil(2^kh_shift / n_k_heads), kh_shift = 40 below 2^16 key
+  // heads and 48 from there (the host bounds n_k_heads below 2^18).
   uint64_t kh_magic;
+  uint32_t kh_shift;
   // One-token calls: first value head and sequence of this launch (the host
   // splits the heads and sequences of a call into launches of at most 65535
   // each, the limit of a grid's y and z dimensions).
@@ -385,9 +387,9 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
     rb = blockIdx.x;
     vh = blockIdx.y + a.vh0;
     s = blockIdx.z + a.s0;
-    kh = a.kh_magic != 0
-             ? vh - a.n_k_heads * (uint32_t)(((uint64_t)vh * a.kh_magic) >> 40)
-             : vh % a.n_k_heads;
+    // No branch: a branch here would hold the load of the array pointers
+    // back behind the first kernel-argument round trip.
+    kh = vh - a.n_k_heads * (uint32_t)(((uint64_t)vh * a.kh_magic) >> a.kh_shift);
   } else {
     const uint32_t n = gridDim.x, xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
     const uint32_t per = n / 8u, extra = n % 8u;
@@ -1133,9 +1135,8 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   const uint64_t kq_bytes = (last * kq_row + f.d_k) * io, v_bytes = (last * v_row + f.d_v) * io;
   a.kq_ext0 = kq_bytes < 0xFFFFFFFFull ? (uint32_t)kq_bytes : 0xFFFFFFFFu;
   a.v_ext0 = v_bytes < 0xFFFFFFFFull ? (uint32_t)v_bytes : 0xFFFFFFFFu;
-  a.kh_magic = f.n_k_heads < (1u << 16)
-                   ? ((1ull << 40) + f.n_k_heads - 1) / f.n_k_heads
-                   : 0;
+  a.kh_shift = f.n_k_heads < (1u << 16) ? 40 : 48;
+  a.kh_magic = ((1ull << a.kh_shift) + f.n_k_heads - 1) / f.n_k_heads;
 
   void *args[] = {&a};
   a.vh0 = a.s0 = 0;
