@@ -1039,7 +1039,12 @@ constexpr Geometry make_geometry() {
 //                streaming of the state, read with non-temporal loads (single
 //                decode 3.58 -> 3.23 us, 64-sequence decode 48.3 -> 43.0 us).
 //                At D_k = 128 two rows per lane (paired): 3.23 -> 3.13 us;
-//                other cell counts and wave counts measured no better.
+//                other cell counts and wave counts measured no better, except
+//                where that grid has fewer workgroups than the chip has
+//                compute units: one sequence of the dense shape (192
+//                workgroups) runs 3.14 -> 2.93 us with one row per lane and
+//                two waves (768 workgroups); from two sequences on the
+//                two-row grid is faster again (4.05 vs 4.29 us).
 //   two or more: two rows per lane (each k/q register feeds two rows, which
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
 //                tokens against one row per lane), 16 lanes per row, 4 waves.
@@ -1052,8 +1057,12 @@ constexpr Geometry make_geometry() {
 //                up (2 to 512), so one token is the only short-run case. At
 //                D_k = 64, 8 lanes per row (8 cells each): 512-token prefill
 //                145 -> 135 us against 16.
+// Compute units of an MI355X.
+constexpr uint64_t kComputeUnits = 256;
+
+// heads: n_v_heads * n_seqs (the one-token grid's second and third axes).
 template <bool CAPTURE, typename IO, int NK>
-Geometry pick(uint32_t d_k, uint32_t n_tokens) {
+Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
   constexpr int NK1 = NK == 2 ? 1 : NK;  // one-token calls have no ring group
   switch (d_k) {
@@ -1064,7 +1073,14 @@ Geometry pick(uint32_t d_k, uint32_t n_tokens) {
       return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO, NK1>()
                        : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO, NK>();
     case 128:
-      if (one_token) return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO, NK1>();
+      if (one_token) {
+        // A grid of two-row workgroups that leaves compute units idle (one
+        // dense-shape layer of one sequence: 192 workgroups) is spread over
+        // four times as many workgroups of one row per lane and two waves.
+        if (heads * ((d_v + 31) / 32) < kComputeUnits)
+          return make_geometry<128, 8, 1, 2, 1, CAPTURE, IO, NK1>();
+        return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO, NK1>();
+      }
       if constexpr (CAPTURE)
         return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NK>();
       else
@@ -1075,12 +1091,13 @@ Geometry pick(uint32_t d_k, uint32_t n_tokens) {
 }
 
 template <int NK>
-Geometry pick_io(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16) {
+Geometry pick_io(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens, bool capture,
+                 bool bf16) {
   if (bf16)
-    return capture ? pick<true, __bf16, NK>(d_k, n_tokens)
-                   : pick<false, __bf16, NK>(d_k, n_tokens);
-  return capture ? pick<true, float, NK>(d_k, n_tokens)
-                 : pick<false, float, NK>(d_k, n_tokens);
+    return capture ? pick<true, __bf16, NK>(d_k, d_v, heads, n_tokens)
+                   : pick<false, __bf16, NK>(d_k, d_v, heads, n_tokens);
+  return capture ? pick<true, float, NK>(d_k, d_v, heads, n_tokens)
+                 : pick<false, float, NK>(d_k, d_v, heads, n_tokens);
 }
 
 // Key normalisation takes the group-ahead factors from this many tokens on:
@@ -1088,18 +1105,20 @@ Geometry pick_io(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16) {
 // round trip before the first token (~0.3 us on a 4-token verify).
 constexpr uint32_t kGroupNormMinTokens = 16;
 
-Geometry pick_geometry(uint32_t d_k, uint32_t n_tokens, bool capture, bool bf16,
-                       bool normalize_k) {
-  if (!normalize_k) return pick_io<0>(d_k, n_tokens, capture, bf16);
-  return n_tokens >= kGroupNormMinTokens ? pick_io<2>(d_k, n_tokens, capture, bf16)
-                                         : pick_io<1>(d_k, n_tokens, capture, bf16);
+Geometry pick_geometry(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens,
+                       bool capture, bool bf16, bool normalize_k) {
+  if (!normalize_k) return pick_io<0>(d_k, d_v, heads, n_tokens, capture, bf16);
+  return n_tokens >= kGroupNormMinTokens
+             ? pick_io<2>(d_k, d_v, heads, n_tokens, capture, bf16)
+             : pick_io<1>(d_k, d_v, heads, n_tokens, capture, bf16);
 }
 
 }  // namespace
 
 uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
                      uint32_t n_seqs, uint32_t n_tokens, bool capture) {
-  const Geometry geo = pick_geometry(d_k, n_tokens, capture, false, false);
+  const Geometry geo =
+      pick_geometry(d_k, d_v, (uint64_t)n_v_heads * n_seqs, n_tokens, capture, false, false);
   if (geo.kernel == nullptr) return 0;
   const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
   return row_blocks * n_v_heads * n_seqs;
@@ -1107,7 +1126,8 @@ uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
 
 hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   const bool capture = f.capture != nullptr;
-  const Geometry geo = pick_geometry(f.d_k, f.n_tokens, capture, f.bf16, f.normalize_k);
+  const Geometry geo = pick_geometry(f.d_k, f.d_v, (uint64_t)f.n_v_heads * f.n_seqs, f.n_tokens,
+                                     capture, f.bf16, f.normalize_k);
   if (geo.kernel == nullptr) return hipErrorInvalidValue;
   const uint32_t row_blocks =
       (f.d_v + geo.rows_per_block - 1) / geo.rows_per_block;
