@@ -28,6 +28,9 @@ FLAGS = [
     "-Wall", "-mcode-object-version=5",
     # Keep the compiler from forming packed-FP32 VALU instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Preload the first 13 dwords of kernel arguments into scalar registers
+    # at dispatch (the one-token kernel's leading parameters).
+    "-mllvm", "-amdgpu-kernarg-preload-count=13",
 ]
 
 

@@ -47,10 +47,10 @@
 //   * Optionally (NK) every key row is used L2-normalised, its factor folded
 //     into sk and delta: computed per token, or a ring group ahead in calls of
 //     16 tokens or more.
-// Two launch geometries instantiate the same template: one for a single decode
-// token (HBM-bound on the state read and write; straight-line, no ring, a 3-D
-// grid) and one for multi-token calls (bound by VALU issue; two rows per lane
-// share each k/q register).
+// Two kernels: gdn_decode for a single decode token (HBM-bound on the state
+// read and write; straight-line code, its leading arguments preloaded into
+// scalar registers) and gdn_recurrent for multi-token calls (bound by VALU
+// issue; two rows per lane share each k/q register).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -329,15 +329,6 @@ struct KernelArgs {
   // Descriptor sizes of the k/q and v rows of a whole sequence (the first
   // rebase), the same for every workgroup.
   uint32_t kq_ext0, v_ext0;
-  // vh / n_k_heads == (vh * kh_magic) >> kh_shift for every vh < 2^23:
-  // kh_magic = ceil(2^kh_shift / n_k_heads), kh_shift = 40 below 2^16 key
-  // heads and 48 from there (the host bounds n_k_heads below 2^18).
-  uint64_t kh_magic;
-  uint32_t kh_shift;
-  // One-token calls: first value head and sequence of this launch (the host
-  // splits the heads and sequences of a call into launches of at most 65535
-  // each, the limit of a grid's y and z dimensions).
-  uint32_t vh0, s0;
 };
 
 // Epsilon of the key-normalisation option (binary32 value of 1e-6).
@@ -345,17 +336,18 @@ constexpr float kNormEps = 1e-6f;
 
 // DK: key dim. C: cells per lane per row. R: rows per lane. WAVES: waves per
 // workgroup. NB: token buffers in the prefetch ring (token t + NB - 1 is
-// requested while token t computes); NB = 1 selects the one-token path, used
-// only for n_tokens == 1. CAPTURE: also write the per-token state. IO: element
+// requested while token t computes), at least 2: one-token calls take
+// gdn_decode. CAPTURE: also write the per-token state. IO: element
 // type of q, k, v and output (float or __bf16). NK: 0, or use every key row
 // as k / sqrt(sum k^2 + kNormEps), its factor computed per token (1) or a ring
-// group ahead (2, multi-token calls; see GNORM).
+// group ahead (2; see GNORM).
 // Kernels with group-ahead factors ask for 3 waves per SIMD: the prefetch of
 // the next group's key rows would otherwise take the D_k = 128 instance one
 // register past the 168 that 3 waves allow (the compiler then spills two
 // values outside the token loop instead).
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
-__global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_recurrent(KernelArgs a) {
+__global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(KernelArgs a) {
+  static_assert(NB >= 2, "a ring of two or more tokens");
   constexpr bool NORMK = NK != 0;
   constexpr int L = DK / C;      // lanes sharing one state row
   constexpr int G = 64 / L;      // row groups per wave
@@ -372,25 +364,14 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   constexpr int NY = PAIRED ? 1 : R;  // rows whose v and output a lane handles
 
   // Workgroup -> (sequence s, value head vh, block of rows); all uniform.
-  // One-token calls take the plain order (s, vh, block). Multi-token calls
-  // read every token's k and q rows once per key head, so their workgroups are
+  // Every token's k and q rows are read once per key head, so workgroups are
   // ordered (s, kh, g, block) with vh = kh + g * n_k_heads (the value heads of
   // the modulo GQA map that share key head kh) and renumbered so that each of
   // the 8 XCDs, which receive workgroups round-robin and each have their own
   // L2, runs one contiguous range of that order: a key head's k/q rows are
   // then fetched into one L2 instead of several.
-  // One-token calls are latency-bound: a 3-D grid (row block, value head,
-  // sequence) and a multiply by a host-computed reciprocal keep integer
-  // divisions off the path to the first state load.
   uint32_t s, vh, rb, kh;
-  if constexpr (NB == 1) {
-    rb = blockIdx.x;
-    vh = blockIdx.y + a.vh0;
-    s = blockIdx.z + a.s0;
-    // No branch: a branch here would hold the load of the array pointers
-    // back behind the first kernel-argument round trip.
-    kh = vh - a.n_k_heads * (uint32_t)(((uint64_t)vh * a.kh_magic) >> a.kh_shift);
-  } else {
+  {
     const uint32_t n = gridDim.x, xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
     const uint32_t per = n / 8u, extra = n % 8u;
     const uint32_t bid = xcd * per + (xcd < extra ? xcd : extra) + local;
@@ -452,7 +433,7 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
 
   // Per-lane byte offsets, fixed for the whole call: vector m of row r starts
   // at column m*4L + 4*sub (state: 16 bytes per vector; k/q: 4*IB bytes).
-  const uint32_t col = 16 * sub, col_io = 4 * IB * sub;
+  const uint32_t col = 16 * sub;
   uint32_t cell[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) cell[r] = row[r] * ROW_BYTES + col;
@@ -472,7 +453,7 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   // of each half per TB tokens leaves token t0 + j's output in lane j. The
   // per-token butterfly (log2(TB) dependent cross-lane adds) leaves the
   // token's instruction stream.
-  constexpr bool DEFER = PAIRED && NB > 1;
+  constexpr bool DEFER = PAIRED;
   static_assert(!DEFER || NB % TB == 0, "ring groups hold whole output batches");
   float yp[DEFER ? TB : 1];
 #pragma unroll
@@ -497,14 +478,14 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   // operand from that bank too, which costs the VALU a second cycle. ROT = 1
   // puts them in different banks (multi-token calls without capture; capture
   // stores the cells every token and keeps ROT = 0).
-  constexpr int ROT = (NB > 1 && !CAPTURE) ? 1 : 0;
+  constexpr int ROT = CAPTURE ? 0 : 1;
   if constexpr (ROT == 1)
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < NV; ++m) st[r][m] = st[r][m].yzwx;
 
-  // Multi-token calls stage k and q through LDS. All G row groups of a wave
+  // k and q are staged through LDS. All G row groups of a wave
   // need the same k and q columns, so direct per-lane loads would pull every
   // byte through the vector memory unit G times. Instead the wave reads each
   // token's k and q rows once (RB bytes per lane), parks them in a per-wave
@@ -512,19 +493,16 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   // Lane j loads elements EPL*j .. EPL*j+EPL-1 of each row (lanes past the
   // row repeat its last part and write nothing) and stores them widened to
   // f32, so the column reads need no conversion.
-  constexpr bool STAGE = NB > 1;
   constexpr uint32_t EPL = DK >= 64 ? DK / 64 : 1;  // elements per lane
   constexpr uint32_t SLANES = DK / EPL;              // lanes holding a part
   constexpr int RB = EPL * IB;                       // staged bytes per lane
-  static_assert(!STAGE || RB == 2 || RB == 4 || RB == 8, "staged row size");
-  typedef typename Raw<STAGE ? RB : 4>::T RawT;
-  __shared__ __attribute__((aligned(16))) float kq_lds[STAGE ? WAVES : 1][2 * DK];
-  float *const kq_row = kq_lds[STAGE ? wave : 0];  // k row, then q row (f32)
+  static_assert(RB == 2 || RB == 4 || RB == 8, "staged row size");
+  typedef typename Raw<RB>::T RawT;
+  __shared__ __attribute__((aligned(16))) float kq_lds[WAVES][2 * DK];
+  float *const kq_row = kq_lds[wave];  // k row, then q row (f32)
   const uint32_t slane = lane < SLANES ? lane : SLANES - 1;
   struct Tok {
-    f4 k[STAGE ? 1 : NV], q[STAGE ? 1 : NV];  // direct loads (one-token calls)
-    RawT kr, qr;                              // staged bytes (multi-token)
-    float v[STAGE ? 1 : NY];                  // one-token calls; see load_vgroup
+    RawT kr, qr;  // this lane's part of the token's k and q rows (raw bytes)
   };
   struct KQ {
     f4 k[NV], q[NV];
@@ -560,20 +538,8 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   auto load_token = [&](uint32_t t, Tok &x) {
     const uint32_t kq_off = uniform((t - base_t) * kq_bytes);
     const rsrc_t k_rs = buffer(k_b, kq_ext), q_rs = buffer(q_b, kq_ext);
-    if constexpr (STAGE) {
-      x.kr = Raw<RB>::load(k_rs, slane * RB, kq_off);
-      x.qr = Raw<RB>::load(q_rs, slane * RB, kq_off);
-    } else {
-      const uint32_t v_off = uniform((t - base_t) * v_bytes);
-      const rsrc_t v_rs = buffer(v_b, v_ext);
-#pragma unroll
-      for (int m = 0; m < NV; ++m) {
-        x.k[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, kq_off);
-        x.q[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, kq_off);
-      }
-#pragma unroll
-      for (int r = 0; r < NY; ++r) x.v[r] = Io<IO>::load1(v_rs, vrow[r], v_off);
-    }
+    x.kr = Raw<RB>::load(k_rs, slane * RB, kq_off);
+    x.qr = Raw<RB>::load(q_rs, slane * RB, kq_off);
   };
 
   // Multi-token calls read v once per ring group: the wave's ROWS_PER_WAVE
@@ -583,9 +549,9 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   // out row by row, and every lane reads its rows' NB values back. One
   // vector-memory request per group instead of one per token.
   constexpr uint32_t VT = ROWS_PER_WAVE * NB;
-  static_assert(!STAGE || VT <= 64, "one value per lane per ring group");
-  __shared__ __attribute__((aligned(16))) float v_lds[STAGE ? WAVES : 1][STAGE ? VT : 1];
-  float *const vslot = v_lds[STAGE ? wave : 0];
+  static_assert(VT <= 64, "one value per lane per ring group");
+  __shared__ __attribute__((aligned(16))) float v_lds[WAVES][VT];
+  float *const vslot = v_lds[wave];
   const uint32_t vl = lane < VT ? lane : VT - 1;
   const uint32_t vl_row = rb * ROWS + wave * ROWS_PER_WAVE + vl % ROWS_PER_WAVE;
   const uint32_t vl_off = (vl_row < Dv ? vl_row : Dv - 1) * IB;
@@ -595,7 +561,7 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
     return Io<IO>::load1(buffer(v_b, v_ext), vl_off + (tk - base_t) * v_bytes, 0);
   };
   // Park a group's raw v and return this lane's rows' NB values.
-  auto park_vgroup = [&](float raw, float (&vg)[NY][STAGE ? NB : 1]) {
+  auto park_vgroup = [&](float raw, float (&vg)[NY][NB]) {
     if (lane < VT) vslot[(vl % ROWS_PER_WAVE) * NB + vl_tok] = raw;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -615,8 +581,8 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
   // square root per group instead of a wave-wide sum per token. A lane's
   // slice is requested in KP parts (two when it holds 8 or more elements, at
   // the group's start and middle) to bound the registers in flight.
-  constexpr bool GNORM = NK == 2 && STAGE;
-  constexpr uint32_t LPT = STAGE ? 64 / NB : 16;
+  constexpr bool GNORM = NK == 2;
+  constexpr uint32_t LPT = 64 / NB;
   constexpr uint32_t EPT = DK / LPT;
   static_assert(!GNORM || EPT == 2 || EPT % 4 == 0, "key row split");
   constexpr uint32_t KP = EPT >= 8 ? 2 : 1;          // parts per slice
@@ -661,61 +627,44 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
     for (uint32_t u = 0; u < (GNORM ? NB : 1); ++u) inv[u] = inv_slot[u];
   };
 
-  // This lane's k and q columns of a token: from the staged LDS slot, or
-  // the direct loads. The slot is rewritten per token; LDS operations of a
-  // wave run in order, so the reads of one token complete before the next
-  // token's write.
+  // This lane's k and q columns of a token, through the staged LDS slot. The
+  // slot is rewritten per token; LDS operations of a wave run in order, so
+  // the reads of one token complete before the next token's write.
   auto columns = [&](const Tok &x) {
     KQ c;
     c.inv = 1.f;
-    if constexpr (STAGE) {
-      float kw[EPL], qw[EPL];
-      widen<IO, EPL>(x.kr, kw);
-      widen<IO, EPL>(x.qr, qw);
-      if constexpr (NORMK && !GNORM) {
-        // The wave holds the whole key row: its sum of squares over all lanes
-        // (lanes past the row repeat its last part and count zero). The keys
-        // stay unscaled; step() folds the factor into sk and delta, so this
-        // reduction overlaps the LDS round trip instead of preceding it.
-        float ss = 0.f;
+    float kw[EPL], qw[EPL];
+    widen<IO, EPL>(x.kr, kw);
+    widen<IO, EPL>(x.qr, qw);
+    if constexpr (NORMK && !GNORM) {
+      // The wave holds the whole key row: its sum of squares over all lanes
+      // (lanes past the row repeat its last part and count zero). The keys
+      // stay unscaled; step() folds the factor into sk and delta, so this
+      // reduction overlaps the LDS round trip instead of preceding it.
+      float ss = 0.f;
 #pragma unroll
-        for (uint32_t e = 0; e < EPL; ++e) ss = __builtin_fmaf(kw[e], kw[e], ss);
-        c.inv = __builtin_amdgcn_rsqf(wave_sum(lane < SLANES ? ss : 0.f) + kNormEps);
+      for (uint32_t e = 0; e < EPL; ++e) ss = __builtin_fmaf(kw[e], kw[e], ss);
+      c.inv = __builtin_amdgcn_rsqf(wave_sum(lane < SLANES ? ss : 0.f) + kNormEps);
+    }
+    if (SLANES == 64 || lane < SLANES) {
+#pragma unroll
+      for (uint32_t e = 0; e < EPL; ++e) {
+        kq_row[EPL * lane + e] = kw[e];
+        kq_row[DK + EPL * lane + e] = qw[e];
       }
-      if (SLANES == 64 || lane < SLANES) {
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (uint32_t e = 0; e < EPL; ++e) {
-          kq_row[EPL * lane + e] = kw[e];
-          kq_row[DK + EPL * lane + e] = qw[e];
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int m = 0; m < NV; ++m) {
-        c.k[m] = *reinterpret_cast<const f4 *>(kq_row + m * 4 * L + 4 * sub);
-        c.q[m] = *reinterpret_cast<const f4 *>(kq_row + DK + m * 4 * L + 4 * sub);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < NV; ++m) {
-        c.k[m] = x.k[m];
-        c.q[m] = x.q[m];
-      }
-      if constexpr (NORMK) {  // the L lanes of a row group hold the key row
-        float ss = 0.f;
-#pragma unroll
-        for (int m = 0; m < NV; ++m)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(c.k[m][e], c.k[m][e], ss);
-        c.inv = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
-      }
+    for (int m = 0; m < NV; ++m) {
+      c.k[m] = *reinterpret_cast<const f4 *>(kq_row + m * 4 * L + 4 * sub);
+      c.q[m] = *reinterpret_cast<const f4 *>(kq_row + DK + m * 4 * L + 4 * sub);
     }
     return c;
   };
 
   // One token. With decay set (c = 1, b = beta): the cells are multiplied by
   // alpha, then sk, delta = (v - sk) * beta, the rank-1 write and y, as the
-  // recurrence is written. Lazy tokens (decay clear; multi-token calls only)
+  // recurrence is written. Lazy tokens (decay clear)
   // keep the state divided by c, the product of the alphas of the ring
   // group's tokens after its first, up to this one, and leave the cells
   // undecayed: sk = c * (cells . k), the write adds delta / c along k
@@ -819,13 +768,7 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
     }
   };
 
-  if constexpr (NB == 1) {
-    // One token (n_tokens == 1): straight line, g and beta read directly.
-    Tok x;
-    load_token(0, x);
-    const rsrc_t gb = buffer(g_tok, 4), bb = buffer(b_tok, 4);
-    step(0, 0, true, columns(x), x.v, true, expf(-load1(gb, 0)), load1(bb, 0), 1.f);
-  } else {
+  {
     // Raw g and beta of the 64-token chunk starting at t0: lane j holds token
     // t0 + j (clamped to the last token; lanes past the end are never read).
     auto load_chunk = [&](uint32_t t0, float &gr, float &br) {
@@ -1017,27 +960,219 @@ __global__ __launch_bounds__(WAVES * 64, NB > 1 && NK == 2 ? 3 : 1) void gdn_rec
         store4_stream(s_out, cell[r] + m * 16 * L, ROT == 1 ? st[r][m].wxyz : st[r][m]);
 }
 
+// ---------------------------------------------------------------- one token
+
+// Arguments of the one-token kernel that its first loads do not need. The
+// kernel's leading parameters (the state, k, q and g bases and the sizes
+// that address them) are preloaded into scalar registers at dispatch (the
+// library is built with a kernel-argument preload count that covers them),
+// so those loads need no kernel-argument memory; these fields are read from
+// it (the compiler schedules that read; forcing it after the first loads
+// with a scheduling barrier measured slower).
+struct DecodeArgs {
+  const float *beta;
+  const void *v;  // IO type
+  void *output;   // IO type
+  float *state_out, *capture;
+  float q_scale;
+};
+
+// One decode token (n_tokens == 1) for a tile of sequences: straight-line
+// code, the state streamed in and out once (HBM-bound). Grid: x = (value
+// head << rb_shift) | row block, the row blocks of a head padded to a power
+// of two (padding blocks exit at once); y = sequence within the tile (the
+// host offsets every base to the tile's first sequence). shifts: kh_shift in
+// bits 0-7, rb_shift in bits 8-15; vh / n_k_heads == (vh * kh_magic) >>
+// kh_shift for every value head (host-computed, exact below 2^23 heads).
+// DK, C, R, WAVES, IO and NK as for gdn_recurrent (NK: 0 or 1).
+template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
+__global__ __launch_bounds__(WAVES * 64) void gdn_decode(
+    const float *state_in, const void *k_in, const void *q_in, const float *g_in,
+    uint32_t d_v, uint32_t n_v_heads, uint32_t n_k_heads, uint32_t kh_magic,
+    uint32_t shifts, DecodeArgs a) {
+  constexpr bool NORMK = NK != 0;
+  constexpr int L = DK / C;
+  constexpr int G = 64 / L;
+  constexpr int NV = C / 4;
+  constexpr int ROWS_PER_WAVE = G * R;
+  constexpr uint32_t ROWS = WAVES * ROWS_PER_WAVE;
+  constexpr uint32_t ROW_BYTES = DK * 4;
+  constexpr uint32_t IB = Io<IO>::bytes;
+  static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
+  static_assert(R == 1 || R == 2, "one row per lane, or two paired");
+  constexpr bool PAIRED = R == 2;
+  constexpr int NY = PAIRED ? 1 : R;           // rows whose v and output a lane handles
+  constexpr uint32_t TB = PAIRED ? L / 2 : L;  // lanes that hold a row's sums
+
+  const uint32_t rb_shift = shifts >> 8, kh_shift = shifts & 0xFFu;
+  const uint32_t rb = blockIdx.x & ((1u << rb_shift) - 1u);
+  const uint32_t vh = blockIdx.x >> rb_shift;
+  const uint32_t s = blockIdx.y;
+  if (rb * ROWS >= d_v) return;  // padding of the row blocks: the whole workgroup
+  const uint32_t kh = vh - n_k_heads * (uint32_t)(((uint64_t)vh * kh_magic) >> kh_shift);
+  const uint32_t hs = s * n_v_heads + vh;  // (s, vh) and its g/beta index (T = 1)
+
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t grp = lane / L;
+  const uint32_t sub = lane % L;
+  // Rows past d_v compute on a clamped (valid) row and store nothing; the
+  // high half of a paired group holds the group's two rows in swapped order.
+  const bool high = PAIRED && sub >= L / 2;
+  uint32_t row[R];
+  bool ok[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t slot = high ? R - 1 - r : r;
+    const uint32_t i = rb * ROWS + wave * ROWS_PER_WAVE + slot * G + grp;
+    ok[r] = i < d_v;
+    row[r] = ok[r] ? i : d_v - 1;
+  }
+
+  // The loads that need only preloaded arguments: state rows, the k and q
+  // columns of this lane, g. Then v and beta.
+  const uint32_t head_bytes = d_v * ROW_BYTES;  // host-checked < 2^32
+  const uint64_t head = (uint64_t)hs * d_v * DK;
+  const uint32_t col = 16 * sub, col_io = 4 * IB * sub;
+  uint32_t cell[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) cell[r] = row[r] * ROW_BYTES + col;
+  const rsrc_t s_in = buffer(state_in + head, head_bytes);
+  f4 st[R][NV];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NV; ++m) st[r][m] = load4_stream(s_in, cell[r] + m * 16 * L);
+  const uint64_t kq = ((uint64_t)s * n_k_heads + kh) * DK * IB;
+  const rsrc_t k_rs = buffer(static_cast<const char *>(k_in) + kq, DK * IB);
+  const rsrc_t q_rs = buffer(static_cast<const char *>(q_in) + kq, DK * IB);
+  f4 kc[NV], qc[NV];
+#pragma unroll
+  for (int m = 0; m < NV; ++m) {
+    kc[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, 0);
+    qc[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, 0);
+  }
+  const float g = load1(buffer(g_in + hs, 4), 0);
+
+  const rsrc_t v_rs = buffer(static_cast<const char *>(a.v) + (uint64_t)hs * d_v * IB, d_v * IB);
+  float v[NY];
+#pragma unroll
+  for (int r = 0; r < NY; ++r) v[r] = Io<IO>::load1(v_rs, row[r] * IB, 0);
+  const float beta = load1(buffer(a.beta + hs, 4), 0);
+
+  // Normalised keys (NK): the L lanes of a row group hold the whole key row;
+  // 1 / sqrt(sum k^2 + kNormEps) is folded into sk and delta.
+  float inv = 1.f;
+  if constexpr (NORMK) {
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kc[m][e], kc[m][e], ss);
+    inv = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
+  }
+  const float alpha = expf(-g);
+  const float bs = beta * inv;
+
+  // The step as written: decay, sk, delta = (v - sk) * beta, the rank-1
+  // write, y on the updated state.
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NV; ++m) st[r][m] *= alpha;
+  float part[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    part[r] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[r] = __builtin_fmaf(st[r][m][e], kc[m][e], part[r]);
+  }
+  float d[R];
+  if constexpr (PAIRED) {
+    d[0] = __builtin_fmaf(-inv, pair_sum<L>(part[0], part[1]), v[0]) * bs;
+    d[1] = partner<L>(d[0]);  // the partner's A row is this lane's B row
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) d[r] = __builtin_fmaf(-inv, group_sum<L>(part[r]), v[r]) * bs;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    part[r] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st[r][m][e] = __builtin_fmaf(d[r], kc[m][e], st[r][m][e]);
+        part[r] = __builtin_fmaf(st[r][m][e], qc[m][e], part[r]);
+      }
+  }
+  float y[NY];
+  if constexpr (PAIRED) {
+    y[0] = pair_sum<L>(part[0], part[1]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) y[r] = group_sum<L>(part[r]);
+  }
+
+  // Lane 0 of each set of TB lanes writes its rows' outputs, q_scale
+  // applied; then the capture slice (the state after the token) and the
+  // state.
+  const rsrc_t o_rs =
+      buffer(static_cast<char *>(a.output) + (uint64_t)hs * d_v * IB, d_v * IB);
+  if (sub % TB == 0)
+#pragma unroll
+    for (int r = 0; r < NY; ++r)
+      if (ok[r]) Io<IO>::store1(o_rs, row[r] * IB, 0, y[r] * a.q_scale);
+  if constexpr (CAPTURE) {
+    const rsrc_t ct = buffer(a.capture + head, head_bytes);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (ok[r])
+#pragma unroll
+        for (int m = 0; m < NV; ++m) store4_stream(ct, cell[r] + m * 16 * L, st[r][m]);
+  }
+  const rsrc_t s_out = buffer(a.state_out + head, head_bytes);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (ok[r])
+#pragma unroll
+      for (int m = 0; m < NV; ++m) store4_stream(s_out, cell[r] + m * 16 * L, st[r][m]);
+}
+
 // ---------------------------------------------------------------- geometry
 
 struct Geometry {
   int rows_per_block;  // WAVES * (64 / L) * R
   int threads;
   const void *kernel;
+  bool decode;  // gdn_decode (one token) rather than gdn_recurrent
 };
 
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
 constexpr Geometry make_geometry() {
   return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
                   reinterpret_cast<const void *>(
-                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO, NK>)};
+                      &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO, NK>),
+                  false};
+}
+
+template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
+constexpr Geometry make_decode_geometry() {
+  return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
+                  reinterpret_cast<const void *>(&gdn_decode<DK, C, R, WAVES, CAPTURE, IO, NK>),
+                  true};
 }
 
 // Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
 // HBM-resident inputs; D_k = 128 workloads of one-token decode, 64-sequence
 // batched decode, 4-token capture and 512-token prefill):
-//   one token  : 16 lanes per row, 4 waves, straight-line code; pure
-//                streaming of the state, read with non-temporal loads (single
-//                decode 3.58 -> 3.23 us, 64-sequence decode 48.3 -> 43.0 us).
+//   one token  : gdn_decode. 16 lanes per row, 4 waves, straight-line code;
+//                pure streaming of the state, read with non-temporal loads
+//                (single decode 3.58 -> 3.23 us, 64-sequence decode 48.3 ->
+//                43.0 us). Its own kernel with preloaded leading arguments:
+//                single decode 2.93 -> 2.88 us.
 //                At D_k = 128 two rows per lane (paired): 3.23 -> 3.13 us;
 //                other cell counts and wave counts measured no better, except
 //                where that grid has fewer workgroups than the chip has
@@ -1060,17 +1195,17 @@ constexpr Geometry make_geometry() {
 // Compute units of an MI355X.
 constexpr uint64_t kComputeUnits = 256;
 
-// heads: n_v_heads * n_seqs (the one-token grid's second and third axes).
+// heads: n_v_heads * n_seqs.
 template <bool CAPTURE, typename IO, int NK>
 Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
   constexpr int NK1 = NK == 2 ? 1 : NK;  // one-token calls have no ring group
   switch (d_k) {
     case 32:
-      return one_token ? make_geometry<32, 4, 1, 4, 1, CAPTURE, IO, NK1>()
+      return one_token ? make_decode_geometry<32, 4, 1, 4, CAPTURE, IO, NK1>()
                        : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NK>();
     case 64:
-      return one_token ? make_geometry<64, 4, 1, 4, 1, CAPTURE, IO, NK1>()
+      return one_token ? make_decode_geometry<64, 4, 1, 4, CAPTURE, IO, NK1>()
                        : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO, NK>();
     case 128:
       if (one_token) {
@@ -1078,15 +1213,15 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
         // dense-shape layer of one sequence: 192 workgroups) is spread over
         // four times as many workgroups of one row per lane and two waves.
         if (heads * ((d_v + 31) / 32) < kComputeUnits)
-          return make_geometry<128, 8, 1, 2, 1, CAPTURE, IO, NK1>();
-        return make_geometry<128, 8, 2, 4, 1, CAPTURE, IO, NK1>();
+          return make_decode_geometry<128, 8, 1, 2, CAPTURE, IO, NK1>();
+        return make_decode_geometry<128, 8, 2, 4, CAPTURE, IO, NK1>();
       }
       if constexpr (CAPTURE)
         return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NK>();
       else
         return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NK>();
     default:
-      return Geometry{0, 0, nullptr};
+      return Geometry{0, 0, nullptr, false};
   }
 }
 
@@ -1113,6 +1248,13 @@ Geometry pick_geometry(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_to
              : pick_io<1>(d_k, d_v, heads, n_tokens, capture, bf16);
 }
 
+// Smallest s with 2^s >= x (x >= 1).
+uint32_t ceil_log2(uint64_t x) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < x) ++s;
+  return s;
+}
+
 }  // namespace
 
 uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
@@ -1121,7 +1263,9 @@ uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
       pick_geometry(d_k, d_v, (uint64_t)n_v_heads * n_seqs, n_tokens, capture, false, false);
   if (geo.kernel == nullptr) return 0;
   const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
-  return row_blocks * n_v_heads * n_seqs;
+  // One-token grids pad each head's row blocks to a power of two.
+  const uint64_t padded = geo.decode ? uint64_t(1) << ceil_log2(row_blocks) : row_blocks;
+  return padded * n_v_heads * n_seqs;
 }
 
 hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
@@ -1132,6 +1276,44 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   const uint32_t row_blocks =
       (f.d_v + geo.rows_per_block - 1) / geo.rows_per_block;
   const uint64_t blocks = (uint64_t)row_blocks * f.n_v_heads * f.n_seqs;
+
+  const uint64_t io = f.bf16 ? 2 : 4;
+  if (geo.decode) {
+    // One token: grid x = (value head << rb_shift) | row block, the row
+    // blocks padded to 2^rb_shift; grid y = sequence, one launch per 65535
+    // sequences with every base moved to the launch's first sequence
+    // (sequences are independent and T = 1).
+    const uint32_t rb_shift = ceil_log2(row_blocks);
+    const uint32_t kh_shift = 23 + ceil_log2(f.n_k_heads);
+    const uint32_t kh_magic =
+        (uint32_t)(((uint64_t(1) << kh_shift) + f.n_k_heads - 1) / f.n_k_heads);
+    uint32_t shifts = kh_shift | rb_shift << 8;
+    const uint32_t gx = f.n_v_heads << rb_shift;
+    const uint64_t state_seq = (uint64_t)f.n_v_heads * f.d_v * f.d_k;  // floats
+    const uint64_t kq_seq = (uint64_t)f.n_k_heads * f.d_k * io;       // bytes
+    const uint64_t v_seq = (uint64_t)f.n_v_heads * f.d_v * io;        // bytes
+    constexpr uint32_t kMaxY = 65535;
+    for (uint32_t s0 = 0; s0 < f.n_seqs; s0 += kMaxY) {
+      const uint32_t ny = f.n_seqs - s0 < kMaxY ? f.n_seqs - s0 : kMaxY;
+      const float *state_in = f.state_in + s0 * state_seq;
+      const void *k = static_cast<const char *>(f.k) + s0 * kq_seq;
+      const void *q = static_cast<const char *>(f.q) + s0 * kq_seq;
+      const float *g = f.g + (uint64_t)s0 * f.n_v_heads;
+      uint32_t d_v = f.d_v, n_v = f.n_v_heads, n_k = f.n_k_heads, magic = kh_magic;
+      DecodeArgs d;
+      d.beta = f.beta + (uint64_t)s0 * f.n_v_heads;
+      d.v = static_cast<const char *>(f.v) + s0 * v_seq;
+      d.output = static_cast<char *>(f.output) + s0 * v_seq;
+      d.state_out = f.state_out + s0 * state_seq;
+      d.capture = f.capture != nullptr ? f.capture + s0 * state_seq : nullptr;
+      d.q_scale = f.q_scale;
+      void *args[] = {&state_in, &k, &q, &g, &d_v, &n_v, &n_k, &magic, &shifts, &d};
+      const hipError_t e =
+          hipLaunchKernel(geo.kernel, dim3(gx, ny), dim3(geo.threads), args, 0, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
 
   KernelArgs a;
   a.q = f.q;
@@ -1149,34 +1331,13 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   a.n_tokens = f.n_tokens;
   a.row_blocks = row_blocks;
   a.q_scale = f.q_scale;
-
   const uint64_t kq_row = (uint64_t)f.n_k_heads * f.d_k, v_row = (uint64_t)f.n_v_heads * f.d_v;
-  const uint64_t io = f.bf16 ? 2 : 4, last = f.n_tokens - 1u;
+  const uint64_t last = f.n_tokens - 1u;
   const uint64_t kq_bytes = (last * kq_row + f.d_k) * io, v_bytes = (last * v_row + f.d_v) * io;
   a.kq_ext0 = kq_bytes < 0xFFFFFFFFull ? (uint32_t)kq_bytes : 0xFFFFFFFFu;
   a.v_ext0 = v_bytes < 0xFFFFFFFFull ? (uint32_t)v_bytes : 0xFFFFFFFFu;
-  a.kh_shift = f.n_k_heads < (1u << 16) ? 40 : 48;
-  a.kh_magic = ((1ull << a.kh_shift) + f.n_k_heads - 1) / f.n_k_heads;
-
   void *args[] = {&a};
-  a.vh0 = a.s0 = 0;
-  if (f.n_tokens != 1)
-    return hipLaunchKernel(geo.kernel, dim3((uint32_t)blocks), dim3(geo.threads), args, 0,
-                           stream);
-  // One-token geometries take a 3-D grid (row block, value head, sequence),
-  // one launch per 65535 x 65535 tile of (heads, sequences).
-  constexpr uint32_t kMaxYZ = 65535;
-  for (uint32_t s0 = 0; s0 < f.n_seqs; s0 += kMaxYZ)
-    for (uint32_t vh0 = 0; vh0 < f.n_v_heads; vh0 += kMaxYZ) {
-      a.s0 = s0;
-      a.vh0 = vh0;
-      const uint32_t ny = f.n_v_heads - vh0 < kMaxYZ ? f.n_v_heads - vh0 : kMaxYZ;
-      const uint32_t nz = f.n_seqs - s0 < kMaxYZ ? f.n_seqs - s0 : kMaxYZ;
-      const hipError_t e =
-          hipLaunchKernel(geo.kernel, dim3(row_blocks, ny, nz), dim3(geo.threads), args, 0, stream);
-      if (e != hipSuccess) return e;
-    }
-  return hipSuccess;
+  return hipLaunchKernel(geo.kernel, dim3((uint32_t)blocks), dim3(geo.threads), args, 0, stream);
 }
 
 }  // namespace gdn

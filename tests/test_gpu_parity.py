@@ -130,7 +130,8 @@ SHAPES = [
     (128, 17, 3, 3, 130, 1),
     (128, 128, 16, 48, 1, 2),
     # one-token grids on both sides of the compute-unit count (the small one
-    # takes one row per lane): ragged rows in each
+    # takes one row per lane): ragged rows in each, row blocks padded to a
+    # power of two
     (128, 40, 4, 64, 1, 2),
     (128, 72, 4, 12, 1, 3),
     (128, 256, 1, 2, 129, 1),
@@ -162,13 +163,13 @@ def test_shapes(shape, capture):
 @pytest.mark.parametrize("shape", [
     (32, 1, 1, 1, 1, 70000),      # sequences past one launch's 65535
     (32, 1, 1, 65540, 1, 1),      # value heads past 65535 (GQA ratio 65540)
-    (32, 1, 65540, 65540, 1, 1),  # key heads past 2^16: the reciprocal's wider shift
+    (32, 1, 65540, 65540, 1, 1),  # key heads past 2^16
 ], ids=["seqs70000", "vheads65540", "kheads65540"])
 def test_one_token_large_grids(shape):
-    """One-token calls launch a 3-D grid (row block, value head, sequence) of
-    at most 65535 heads and sequences at a time and take vh mod n_k_heads
-    through a host-computed reciprocal whose shift widens from 2^16 key heads
-    on: calls past those limits."""
+    """One-token calls launch a grid of (value head x row block, sequence),
+    at most 65535 sequences per launch, and take vh mod n_k_heads through a
+    host-computed reciprocal: calls past 65535 sequences, value heads and key
+    heads."""
     dk, dv, hk, hv, t, s = shape
     x = make_inputs(Workload("grid", 0, dk, dv, hk, hv, t, s), seed=77)
     got = run(x)
