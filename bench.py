@@ -39,7 +39,8 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X FP32 vector, published (packed issue)
 INFINITY_CACHE_BYTES = 256 << 20
 RESIDENT_TARGET_BYTES = 1 << 30  # input sets cycled per run: >= 4x the cache
 METRIC = "GDN decode µs/layer + state HBM GB/s (%peak); prefill tokens/s at n_tokens=512"
-KERNEL_NAME = "gdn_recurrent"
+KERNEL_NAME = "gdn_recurrent"      # multi-token forward calls
+DECODE_KERNEL_NAME = "gdn_decode"  # one-token forward calls
 NAMES = ("q", "k", "v", "g", "beta", "state_in")
 
 
@@ -113,17 +114,18 @@ def workload_info(name: str, io: str = "f32"):
         return (w, "gdn_rollback_kernel", w.state_bytes() + 4 * w.n_seqs,
                 "accepted-prefix rollback after " + w.description)
     w = WORKLOADS[name]
+    kernel = DECODE_KERNEL_NAME if w.n_tokens == 1 else KERNEL_NAME
     if io == "bf16":
-        return (w, KERNEL_NAME, w.algorithmic_bytes(io_bytes=2),
+        return (w, kernel, w.algorithmic_bytes(io_bytes=2),
                 w.description + ", bf16 q/k/v/output")
-    return w, KERNEL_NAME, w.algorithmic_bytes(), w.description
+    return w, kernel, w.algorithmic_bytes(), w.description
 
 
 def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict,
                       out_dir: str | None = None) -> str:
     """Summaries under profiles/ from rocprofv3 CSV output (see --summarize-rocprof):
     the kernel-trace statistics of every kernel, and the HBM bytes per launch of
-    gdn_recurrent from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
+    the workload's kernel from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
     counter reads for a plain device copy of calib_mib MiB."""
     w, kernel, alg, description = workload_info(workload)
     digests = set()

@@ -50,7 +50,7 @@ def test_algorithmic_bytes(bench, name, shape, capture, total):
     w, kernel, alg, _ = bench.workload_info(name)
     assert (w.d_k, w.d_v, w.n_k_heads, w.n_v_heads, w.n_tokens, w.n_seqs) == shape
     assert alg == expected_bytes(*shape, capture=capture) == total
-    assert kernel == "gdn_recurrent"
+    assert kernel == ("gdn_decode" if shape[4] == 1 else "gdn_recurrent")
     _, _, alg16, _ = bench.workload_info(name, "bf16")
     assert alg16 == expected_bytes(*shape, capture=capture, io=2)
 
@@ -87,7 +87,7 @@ def test_summarize_rocprof(bench, tmp_path):
             f.write("noise\n" + json.dumps({"kernel_digest": digest}) + "\n")
     write_csv(str(src / f"kt_{wl}" / "run_kernel_stats.csv"),
               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
-              [["void gdn::gdn_recurrent<128>", 220, 3650.0, 2800.0, 7000.0, 30.0],
+              [["void gdn::gdn_decode<128>", 220, 3650.0, 2800.0, 7000.0, 30.0],
                ["__amd_rocclr_copyBuffer", 10, 3000.0, 2000.0, 9000.0, 70.0]])
     calib_mib = 1024
     for ctr, copy_kib, ours in (("FETCH_SIZE", 524288.0, [1600.0, 1700.0]),
@@ -95,11 +95,11 @@ def test_summarize_rocprof(bench, tmp_path):
         write_csv(str(src / f"pmc_{ctr}_{wl}" / "run_counter_collection.csv"),
                   ["Kernel_Name", "Counter_Value"],
                   [["__amd_rocclr_copyBuffer", 10.0], ["__amd_rocclr_copyBuffer", copy_kib]]
-                  + [["void gdn::gdn_recurrent<128>", v] for v in ours])
+                  + [["void gdn::gdn_decode<128>", v] for v in ours])
     md = bench.summarize_rocprof(str(src), wl, calib_mib,
                                  dict(kt="kt-cmd", fetch="fetch-cmd", write="write-cmd"),
                                  out_dir=str(out))
-    with open(out / f"gdn_recurrent_{wl}_hbm_traffic.json") as f:
+    with open(out / f"gdn_decode_{wl}_hbm_traffic.json") as f:
         rec = json.load(f)
     fetch = 1650.0 * 2 * 1024
     write = 3000.0 * 1 * 1024
@@ -110,9 +110,10 @@ def test_summarize_rocprof(bench, tmp_path):
     text = open(md).read()
     assert "kt-cmd" in text and "fetch-cmd" in text and "write-cmd" in text
     assert f"ratio {(fetch + write) / 6_357_376:.3f}" in text
-    assert bench.traffic_from_profiles(wl, digest, profiles=str(out)) == \
+    assert bench.traffic_from_profiles(wl, digest, "gdn_decode", profiles=str(out)) == \
         pytest.approx(fetch + write)
-    assert bench.traffic_from_profiles(wl, "other-build", profiles=str(out)) is None
+    assert bench.traffic_from_profiles(wl, "other-build", "gdn_decode",
+                                       profiles=str(out)) is None
     assert bench.traffic_from_profiles("prefill", digest, profiles=str(out)) is None
 
 
