@@ -1108,23 +1108,16 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_decode(
         part[r] = __builtin_fmaf(st[r][m][e], qc[m][e], part[r]);
       }
   }
-  float y[NY];
-  if constexpr (PAIRED) {
-    y[0] = pair_sum<L>(part[0], part[1]);
-  } else {
-#pragma unroll
-    for (int r = 0; r < R; ++r) y[r] = group_sum<L>(part[r]);
-  }
 
-  // Lane 0 of each set of TB lanes writes its rows' outputs, q_scale
-  // applied; then the capture slice (the state after the token) and the
-  // state.
-  const rsrc_t o_rs =
-      buffer(static_cast<char *>(a.output) + (uint64_t)hs * d_v * IB, d_v * IB);
-  if (sub % TB == 0)
+  // The state (and the capture slice, the state after the token) is stored
+  // before y's cross-lane sum: the call ends when its last store completes
+  // and the stores keep program order, so the state's writes run under that
+  // sum instead of after it. y's lane partials come first, so the wait for
+  // the q columns precedes every store (the vector memory counter counts
+  // stores too). An empty asm with each partial as an operand keeps the
+  // compiler from sinking their arithmetic below the stores.
 #pragma unroll
-    for (int r = 0; r < NY; ++r)
-      if (ok[r]) Io<IO>::store1(o_rs, row[r] * IB, 0, y[r] * a.q_scale);
+  for (int r = 0; r < R; ++r) asm volatile("" : "+v"(part[r]));
   if constexpr (CAPTURE) {
     const rsrc_t ct = buffer(a.capture + head, head_bytes);
 #pragma unroll
@@ -1139,6 +1132,21 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_decode(
     if (ok[r])
 #pragma unroll
       for (int m = 0; m < NV; ++m) store4_stream(s_out, cell[r] + m * 16 * L, st[r][m]);
+
+  float y[NY];
+  if constexpr (PAIRED) {
+    y[0] = pair_sum<L>(part[0], part[1]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) y[r] = group_sum<L>(part[r]);
+  }
+  // Lane 0 of each set of TB lanes writes its rows' outputs, q_scale applied.
+  const rsrc_t o_rs =
+      buffer(static_cast<char *>(a.output) + (uint64_t)hs * d_v * IB, d_v * IB);
+  if (sub % TB == 0)
+#pragma unroll
+    for (int r = 0; r < NY; ++r)
+      if (ok[r]) Io<IO>::store1(o_rs, row[r] * IB, 0, y[r] * a.q_scale);
 }
 
 // ---------------------------------------------------------------- geometry
