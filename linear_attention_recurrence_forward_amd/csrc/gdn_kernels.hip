@@ -718,6 +718,20 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
           part[r] = __builtin_fmaf(st[r][m][e], kq.q[m][(e + ROT) % 4], part[r]);
         }
     }
+    if constexpr (CAPTURE) {
+      // The token's capture slice is stored before y's cross-lane sum, so
+      // its writes run under that sum (stores keep program order). The
+      // empty asm keeps the compiler from sinking the partials' arithmetic
+      // below the stores.
+#pragma unroll
+      for (int r = 0; r < R; ++r) asm volatile("" : "+v"(part[r]));
+      const rsrc_t ct = buffer(c_tok + t * cap_step, head_bytes);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (ok[r])
+#pragma unroll
+          for (int m = 0; m < NV; ++m) store4_stream(ct, cell[r] + m * 16 * L, st[r][m]);
+    }
     const bool mine = slot_t == (t & (TB - 1));
     if constexpr (DEFER) {
       // Only the flush reads the partial; the empty asm keeps the compiler
@@ -757,14 +771,6 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
 #pragma unroll
         for (int r = 0; r < NY; ++r)
           if (ok[r]) Io<IO>::store1(o_rs, yoff[r], soff, yk[r] * a.q_scale);
-    }
-    if constexpr (CAPTURE) {
-      const rsrc_t ct = buffer(c_tok + t * cap_step, head_bytes);
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (ok[r])
-#pragma unroll
-          for (int m = 0; m < NV; ++m) store4_stream(ct, cell[r] + m * 16 * L, st[r][m]);
     }
   };
 
