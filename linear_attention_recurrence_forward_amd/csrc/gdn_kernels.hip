@@ -662,6 +662,10 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     return c;
   };
 
+  // Factor table of the current 64-token chunk (see next_chunk below).
+  __shared__ float4 ab_lds[WAVES][64];
+  float4 *const ab = ab_lds[wave];
+
   // One token. With decay set (c = 1, b = beta): the cells are multiplied by
   // alpha, then sk, delta = (v - sk) * beta, the rank-1 write and y, as the
   // recurrence is written. Lazy tokens (decay clear)
@@ -736,8 +740,9 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     if constexpr (DEFER) {
       // Only the flush reads the partial; the empty asm keeps the compiler
       // from sinking the token's dot product there, which would hold every
-      // token's cells live until the end of the batch.
-      float y = c * pair_part<L>(part[0], part[1]);
+      // token's cells live until the end of the batch. The partial is kept
+      // without the token's c: the flush applies c once to the lane's sum.
+      float y = pair_part<L>(part[0], part[1]);
       asm volatile("" : "+v"(y));
 #pragma unroll
       for (uint32_t i = 0; i < TB; ++i) yp[i] = i == j ? y : yp[i];
@@ -765,7 +770,10 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
 #pragma unroll
         for (uint32_t i = 0; i < TB; ++i) w[i] = yp[i];
         scatter_sum<TB / 2>(w, slot_t);
-        yk[0] = w[0];
+        // Token t0 + slot_t's c: from the factor table in a ring group (1
+        // when the group ran eagerly); tokens after the last whole group run
+        // with c = 1.
+        yk[0] = may_end ? w[0] : w[0] * ab[(t0 & 63u) + slot_t].z;
       }
       if (slot_t <= (t & (TB - 1)))
 #pragma unroll
@@ -783,22 +791,16 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       br = *(b_tok + (uint64_t)t * Hv);
     };
 
-    // alpha = exp(-g) and beta for the current 64-token chunk live in a small
-    // per-wave LDS slot: computed once per chunk (one exp per lane), read per
-    // token as one broadcast ds_read_b64. The raw g/beta of the next chunk
-    // are requested a chunk ahead into registers that nothing else reads.
     // Per-token factors of the current 64-token chunk live in a small
-    // per-wave LDS slot, computed once per chunk (lane j: token t0 + j) and
-    // read per token as broadcasts: {alpha = exp(-g), b, c, beta}. In a ring
-    // group that runs lazily, c is the product of the alphas of the group's
-    // tokens 1 .. u (1 at u = 0) and b = beta / c. A group runs eagerly
-    // (every token decays; c = 1, b = beta) if any of its c or beta / c
-    // would leave [2^-64, 2^64] or is not finite (strong decay or growth,
-    // special values), and always when the state is captured. The raw
-    // g/beta of the next chunk are requested a chunk ahead into registers
+    // per-wave LDS slot (ab), computed once per chunk (lane j: token t0 + j)
+    // and read per ring group as broadcasts: {alpha = exp(-g), b, c, beta}.
+    // In a ring group that runs lazily, c is the product of the alphas of the
+    // group's tokens 1 .. u (1 at u = 0) and b = beta / c. A group runs
+    // eagerly (every token decays; c = 1, b = beta) if any of its c or
+    // beta / c would leave [2^-64, 2^64] or is not finite (strong decay or
+    // growth, special values), and always when the state is captured. The
+    // raw g/beta of the next chunk are requested a chunk ahead into registers
     // that nothing else reads.
-    __shared__ float4 ab_lds[WAVES][64];
-    float4 *ab = ab_lds[wave];
     float g_raw, b_raw;
     load_chunk(0, g_raw, b_raw);
     // Bit j set: token t0 + j belongs to an eager group (wave-uniform).
