@@ -163,8 +163,9 @@ gdn_status gdn_check_params(const gdn_params *p) {
   if ((uint64_t)p->n_v_heads * p->d_v >= (uint64_t(1) << 23) ||
       (uint64_t)p->n_k_heads * p->d_k >= (uint64_t(1) << 23))
     return GDN_ERR_SIZE_OVERFLOW;
-  // One-dimensional grid: blocks * threads (at most 256 per block) must stay
-  // below 2^32 work-items, for either geometry, with or without capture.
+  // The grid (one-token calls: row blocks padded to a power of two) times the
+  // threads per block (at most 256) must stay below 2^32 work-items, for
+  // either kernel, with or without capture.
   for (bool cap : {false, true}) {
     const uint64_t blocks = gdn::grid_blocks(p->d_k, p->d_v, p->n_v_heads,
                                              p->n_seqs, p->n_tokens, cap);
