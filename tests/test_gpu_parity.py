@@ -134,6 +134,11 @@ SHAPES = [
     # power of two
     (128, 40, 4, 64, 1, 2),
     (128, 72, 4, 12, 1, 3),
+    # one-token grids whose row blocks (3 per head) are padded to 4: the
+    # two-row D_k = 128 geometry, D_k = 64 and D_k = 32
+    (128, 72, 8, 96, 1, 1),
+    (64, 40, 2, 4, 1, 3),
+    (32, 70, 1, 3, 1, 2),
     (128, 256, 1, 2, 129, 1),
     # one ring group exactly; 64 + 8 tokens with rows that split a wave's
     # rows unevenly; a 64-token chunk plus one D_k = 64 group
