@@ -21,11 +21,14 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kVecsPerThread = 4;  // float4s per lane per pass
 
+// Grid: x = block within a sequence (blocks_per_seq of them), y = sequence
+// within the launch (the host moves every base to the launch's first
+// sequence), so the index read needs no division.
 __global__ __launch_bounds__(kThreads) void gdn_rollback_kernel(
     const float *capture, const uint32_t *accepted, float *state,
     uint32_t n_tokens, uint64_t seq_vecs, uint32_t blocks_per_seq) {
-  const uint32_t s = blockIdx.x / blocks_per_seq;
-  const uint32_t b = blockIdx.x % blocks_per_seq;
+  const uint32_t s = blockIdx.y;
+  const uint32_t b = blockIdx.x;
   const uint32_t a = accepted[s];  // same address in every lane
   if (a >= n_tokens) return;       // uniform: the whole block leaves
   const f4 *src = reinterpret_cast<const f4 *>(capture) +
@@ -63,10 +66,20 @@ hipError_t enqueue_rollback(const float *capture, const uint32_t *accepted,
   const uint64_t blocks = blocks_per_seq * n_seqs;
   if (blocks == 0 || blocks >= (uint64_t(1) << 31)) return hipErrorInvalidValue;
   uint32_t bps = (uint32_t)blocks_per_seq;
-  void *args[] = {&capture, &accepted, &state, &n_tokens,
-                  const_cast<uint64_t *>(&seq_vecs), &bps};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_rollback_kernel),
-                         dim3((uint32_t)blocks), dim3(kThreads), args, 0, stream);
+  // One launch per 65535 sequences (the limit of a grid's y dimension).
+  constexpr uint32_t kMaxY = 65535;
+  for (uint32_t s0 = 0; s0 < n_seqs; s0 += kMaxY) {
+    const uint32_t ny = n_seqs - s0 < kMaxY ? n_seqs - s0 : kMaxY;
+    const float *cap = capture + (uint64_t)s0 * n_tokens * seq_vecs * 4;
+    const uint32_t *acc = accepted + s0;
+    float *st = state + (uint64_t)s0 * seq_vecs * 4;
+    void *args[] = {&cap, &acc, &st, &n_tokens, const_cast<uint64_t *>(&seq_vecs), &bps};
+    const hipError_t e =
+        hipLaunchKernel(reinterpret_cast<const void *>(&gdn_rollback_kernel), dim3(bps, ny),
+                        dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdn

@@ -501,6 +501,23 @@ def test_rollback(name):
                 close(got[s_], s_plain[0], f"rollback to {a_} vs a plain {a_ + 1}-token call")
 
 
+def test_rollback_past_one_launch():
+    """Rollback launches cover at most 65535 sequences each (the grid's second
+    axis), with every base moved to the launch's first sequence: 70000
+    sequences, bit-exact against the oracle's copy."""
+    S, T, Dk = 70000, 2, 32
+    rng = np.random.default_rng(11)
+    cap_np = rng.standard_normal((S, T, 1, 1, Dk)).astype(np.float32)
+    acc = rng.integers(0, T + 1, size=S).astype(np.uint32)
+    cap = torch.from_numpy(cap_np).cuda()
+    slot = torch.full((S, 1, 1, Dk), 5.0, device="cuda")
+    acc_dev = torch.from_numpy(acc.view(np.int32).copy()).cuda()
+    gdn.gdn_rollback(cap, acc_dev, slot, gdn.make_params(Dk, 1, 1, 1, T, S))
+    torch.cuda.synchronize()
+    expect = oracle.rollback(cap_np, acc, np.full((S, 1, 1, Dk), 5.0, np.float32))
+    assert np.array_equal(slot.cpu().numpy().view(np.uint32), expect.view(np.uint32))
+
+
 # ------------------------------------------------------------------ key normalisation
 
 NORM_SHAPES = [
