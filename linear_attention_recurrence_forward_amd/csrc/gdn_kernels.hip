@@ -329,6 +329,11 @@ struct KernelArgs {
   // Descriptor sizes of the k/q and v rows of a whole sequence (the first
   // rebase), the same for every workgroup.
   uint32_t kq_ext0, v_ext0;
+  // Value heads per key head, and host-computed reciprocals for the
+  // workgroup index split: x / d == (x * magic) >> shift for every x < 2^24
+  // (the grid size), d = row_blocks, groups, n_k_heads; shifts holds the
+  // three shifts in bits 0-7, 8-15 and 16-23.
+  uint32_t groups, rb_magic, g_magic, kh_magic, shifts;
 };
 
 // Epsilon of the key-normalisation option (binary32 value of 1e-6).
@@ -375,13 +380,17 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     const uint32_t n = gridDim.x, xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
     const uint32_t per = n / 8u, extra = n % 8u;
     const uint32_t bid = xcd * per + (xcd < extra ? xcd : extra) + local;
-    const uint32_t groups = a.n_v_heads / a.n_k_heads;  // value heads per key head
-    rb = bid % a.row_blocks;
-    uint32_t rest = bid / a.row_blocks;  // (s * n_k_heads + kh) * groups + g
-    const uint32_t g = rest % groups;
-    rest /= groups;
-    const uint32_t khead = rest % a.n_k_heads;
-    s = rest / a.n_k_heads;
+    // bid = ((s * n_k_heads + kh) * groups + g) * row_blocks + rb, split by
+    // multiplies with the host's reciprocals (no integer division).
+    auto divmod = [](uint32_t x, uint32_t d, uint32_t magic, uint32_t shift, uint32_t &r) {
+      const uint32_t q = (uint32_t)(((uint64_t)x * magic) >> shift);
+      r = x - q * d;
+      return q;
+    };
+    uint32_t g, khead;
+    uint32_t rest = divmod(bid, a.row_blocks, a.rb_magic, a.shifts & 0xFFu, rb);
+    rest = divmod(rest, a.groups, a.g_magic, (a.shifts >> 8) & 0xFFu, g);
+    s = divmod(rest, a.n_k_heads, a.kh_magic, a.shifts >> 16, khead);
     vh = khead + g * a.n_k_heads;
     kh = khead;  // vh % n_k_heads
   }
@@ -1352,6 +1361,19 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   const uint64_t kq_bytes = (last * kq_row + f.d_k) * io, v_bytes = (last * v_row + f.d_v) * io;
   a.kq_ext0 = kq_bytes < 0xFFFFFFFFull ? (uint32_t)kq_bytes : 0xFFFFFFFFu;
   a.v_ext0 = v_bytes < 0xFFFFFFFFull ? (uint32_t)v_bytes : 0xFFFFFFFFu;
+  // Reciprocals for the workgroup index split (every quotient's numerator is
+  // below the grid size, < 2^24): shift = 24 + ceil(log2 d), magic =
+  // ceil(2^shift / d) <= 2^25, exact because x * (magic * d - 2^shift) <
+  // 2^24 * d <= 2^shift.
+  if (blocks >= (uint64_t(1) << 24)) return hipErrorInvalidValue;
+  a.groups = f.n_v_heads / f.n_k_heads;
+  auto recip = [](uint32_t d, uint32_t &magic) {
+    const uint32_t shift = 24 + ceil_log2(d);
+    magic = (uint32_t)(((uint64_t(1) << shift) + d - 1) / d);
+    return shift;
+  };
+  a.shifts = recip(row_blocks, a.rb_magic) | recip(a.groups, a.g_magic) << 8 |
+             recip(f.n_k_heads, a.kh_magic) << 16;
   void *args[] = {&a};
   return hipLaunchKernel(geo.kernel, dim3((uint32_t)blocks), dim3(geo.threads), args, 0, stream);
 }
