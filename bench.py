@@ -139,16 +139,26 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict,
         raise SystemExit(f"{workload}: profiled runs disagree on the kernel build: {digests}")
     digest = digests.pop()
     stats = _csv(os.path.join(src, f"kt_{workload}", "run_kernel_stats.csv"))
+    # Per-dispatch medians from the trace (short dispatches have long tails
+    # under the profiler, which pull the average up).
+    durations = {}
+    trace = os.path.join(src, f"kt_{workload}", "run_kernel_trace.csv")
+    if os.path.exists(trace):
+        for r in _csv(trace):
+            durations.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = [f"# {kernel}: {description}", "",
              f"kernel digest (sha256 of sources + flags) of the profiled build: `{digest}`", "",
              "## rocprofv3 --kernel-trace --stats", "", "```", commands["kt"], "```", "",
-             "| kernel | calls | average µs | min µs | max µs | share % |",
-             "|---|---|---|---|---|---|"]
+             "| kernel | calls | average µs | median µs | min µs | max µs | share % |",
+             "|---|---|---|---|---|---|---|"]
     for r in stats:
         name = r["Name"].replace("|", "/")
         if len(name) > 110:
             name = name[:107] + "..."
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        d = sorted(durations.get(r["Name"], []))
+        med = f"{(d[(len(d) - 1) // 2] + d[len(d) // 2]) / 2:.2f}" if d else "—"
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {med} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
     per = {}

@@ -89,6 +89,11 @@ def test_summarize_rocprof(bench, tmp_path):
               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
               [["void gdn::gdn_decode<128>", 220, 3650.0, 2800.0, 7000.0, 30.0],
                ["__amd_rocclr_copyBuffer", 10, 3000.0, 2000.0, 9000.0, 70.0]])
+    # per-dispatch durations 2.8, 3.0, 3.2 and 7.0 us: median 3.10 us
+    write_csv(str(src / f"kt_{wl}" / "run_kernel_trace.csv"),
+              ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+              [["void gdn::gdn_decode<128>", 1000 * i, 1000 * i + d]
+               for i, d in enumerate((2800, 3200, 7000, 3000))])
     calib_mib = 1024
     for ctr, copy_kib, ours in (("FETCH_SIZE", 524288.0, [1600.0, 1700.0]),
                                 ("WRITE_SIZE", 1048576.0, [3000.0, 3000.0])):
@@ -109,6 +114,7 @@ def test_summarize_rocprof(bench, tmp_path):
     assert rec["hbm_bytes_per_launch"] == pytest.approx(fetch + write)
     text = open(md).read()
     assert "kt-cmd" in text and "fetch-cmd" in text and "write-cmd" in text
+    assert "| 220 | 3.65 | 3.10 | 2.80 | 7.00 |" in text  # average, median, min, max
     assert f"ratio {(fetch + write) / 6_357_376:.3f}" in text
     assert bench.traffic_from_profiles(wl, digest, "gdn_decode", profiles=str(out)) == \
         pytest.approx(fetch + write)
