@@ -15,7 +15,10 @@ The K timed steps are enqueued as one HIP graph (launch-bound decode calls are
 captured in serving loops for the same reason) or, with --launch direct, one
 launch at a time. HIP events on the launch stream bracket the timed region and
 give the kernel's average launch duration, from which the roofline fraction is
-computed. Prints one JSON line.
+computed. Prints one JSON line. The single-layer decode line (the default)
+also carries a "prefill" object: the 512-token prefill workload measured the
+same way (tokens/s and its roofline), the other half of the headline metric
+(--no-prefill leaves it out).
 """
 
 from __future__ import annotations
@@ -63,6 +66,12 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave out the 512-token prefill measurement that the "
+                         "single-layer decode line carries as its 'prefill' object")
+    ap.add_argument("--prefill-steps", type=int, default=1000,
+                    help="timed calls of that prefill measurement (after 200 untimed "
+                         "ones: shorter runs catch the clock below its loaded level)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference kernel for the HBM byte counters)")
@@ -341,10 +350,11 @@ def main(argv=None):
         return 0
     if args.summarize_rocprof:
         cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt_{w} -o run "
-               "-- python3 bench.py --workload {w} --steps 200 --warmup 20 --no-cpu-baseline")
+               "-- python3 bench.py --workload {w} --steps 200 --warmup 20 --no-cpu-baseline "
+               "--no-prefill")
         pmc = ("rocprofv3 --pmc {c} --output-format csv -d <dir>/pmc_{c}_{w} -o run -- "
                "python3 bench.py --workload {w} --steps 10 --warmup 2 --layers 4 "
-               "--no-cpu-baseline --launch direct --calibrate-copy-mib 1024")
+               "--no-cpu-baseline --no-prefill --launch direct --calibrate-copy-mib 1024")
         for wl in sorted(WORKLOADS) + ["rollback"]:
             if os.path.isdir(os.path.join(args.summarize_rocprof, f"kt_{wl}")):
                 print(summarize_rocprof(args.summarize_rocprof, wl, 1024, dict(
@@ -366,151 +376,168 @@ def main(argv=None):
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    rollback = args.workload == "rollback"
-    if (args.io == "bf16" or args.normalize_k) and args.workload == "rollback":
-        print("bench.py: --io bf16 and --normalize-k apply to forward workloads",
-              file=sys.stderr)
-        return 2
-    bf16 = args.io == "bf16"
-    w, kernel_name, alg_bytes, description = workload_info(args.workload, args.io)
-    x = make_inputs(w)
-    bits = x["q_scale_bits"]
-    layers = args.layers or max(2, math.ceil(RESIDENT_TARGET_BYTES / max(alg_bytes, 1)))
-    layers = min(layers, 4096)
+    def measure(args):
+        """One workload's timed run; returns (line without cpu_baseline,
+        workload, bf16, rollback)."""
+        rollback = args.workload == "rollback"
+        if (args.io == "bf16" or args.normalize_k) and args.workload == "rollback":
+            raise SystemExit("bench.py: --io bf16 and --normalize-k apply to forward workloads")
+        bf16 = args.io == "bf16"
+        w, kernel_name, alg_bytes, description = workload_info(args.workload, args.io)
+        x = make_inputs(w)
+        bits = x["q_scale_bits"]
+        layers = args.layers or max(2, math.ceil(RESIDENT_TARGET_BYTES / max(alg_bytes, 1)))
+        layers = min(layers, 4096)
 
-    # Resident input sets: same values, distinct memory (state updated in place).
-    host = {n: torch.from_numpy(x[n]) for n in NAMES}
-    if bf16:
-        for n in ("q", "k", "v"):
-            host[n] = host[n].to(torch.bfloat16)
-    sets = []
-    for _ in range(layers):
-        d = {n: host[n].to(dev) for n in NAMES}
-        d["output"] = torch.empty(x["v"].shape, device=dev,
-                                  dtype=torch.bfloat16 if bf16 else torch.float32)
-        d["capture"] = (torch.empty((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
-                                    device=dev) if w.capture else None)
-        sets.append(d)
-    params = gdn.params_for(sets[0]["q"], sets[0]["v"], bits)
-    if rollback:
-        # Fill every set's capture with a real forward call, then pick per
-        # sequence a token to roll back to (all inside the call).
-        rng = torch.Generator().manual_seed(w.seed)
-        for d in sets:
-            gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                    d["state_in"], d["output"], d["state_in"],
-                                    d["capture"], params)
-            d["accepted"] = torch.randint(0, w.n_tokens, (w.n_seqs,), generator=rng,
-                                          dtype=torch.int32).to(dev)
-        torch.cuda.synchronize()
-
-    def launch(i, stream):
-        d = sets[i % layers]
+        # Resident input sets: same values, distinct memory (state updated in place).
+        host = {n: torch.from_numpy(x[n]) for n in NAMES}
+        if bf16:
+            for n in ("q", "k", "v"):
+                host[n] = host[n].to(torch.bfloat16)
+        sets = []
+        for _ in range(layers):
+            d = {n: host[n].to(dev) for n in NAMES}
+            d["output"] = torch.empty(x["v"].shape, device=dev,
+                                      dtype=torch.bfloat16 if bf16 else torch.float32)
+            d["capture"] = (torch.empty((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
+                                        device=dev) if w.capture else None)
+            sets.append(d)
+        params = gdn.params_for(sets[0]["q"], sets[0]["v"], bits)
         if rollback:
-            gdn.gdn_rollback(d["capture"], d["accepted"], d["state_in"], params, stream)
-        elif args.normalize_k:
-            gdn.gdn_forward_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
-                               d["output"], d["state_in"], d["capture"], params,
-                               gdn.OPT_NORMALIZE_K | (gdn.OPT_BF16_IO if bf16 else 0),
-                               stream)
-        elif bf16:
-            gdn.gdn_forward_bf16(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
-                                 d["output"], d["state_in"], d["capture"], params, stream)
-        elif w.capture:
-            gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                    d["state_in"], d["output"], d["state_in"],
-                                    d["capture"], params, stream)
-        else:
-            gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
-                            d["output"], d["state_in"], params, stream)
-
-    stream = torch.cuda.Stream(dev)
-    torch.cuda.synchronize()
-
-    def enqueue(n, offset):
-        if args.launch == "graph":
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(stream):
-                with torch.cuda.graph(graph, stream=stream):
-                    for i in range(n):
-                        launch(offset + i, stream)
+            # Fill every set's capture with a real forward call, then pick per
+            # sequence a token to roll back to (all inside the call).
+            rng = torch.Generator().manual_seed(w.seed)
+            for d in sets:
+                gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                        d["state_in"], d["output"], d["state_in"],
+                                        d["capture"], params)
+                d["accepted"] = torch.randint(0, w.n_tokens, (w.n_seqs,), generator=rng,
+                                              dtype=torch.int32).to(dev)
             torch.cuda.synchronize()
-            return graph.replay
-        return lambda: [launch(offset + i, stream) for i in range(n)]
 
-    run_warm = enqueue(args.warmup, 0) if args.warmup > 0 else (lambda: None)
-    run_timed = enqueue(args.steps, args.warmup)
-    with torch.cuda.stream(stream):
-        run_warm()
-    torch.cuda.synchronize()
+        def launch(i, stream):
+            d = sets[i % layers]
+            if rollback:
+                gdn.gdn_rollback(d["capture"], d["accepted"], d["state_in"], params, stream)
+            elif args.normalize_k:
+                gdn.gdn_forward_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                   d["output"], d["state_in"], d["capture"], params,
+                                   gdn.OPT_NORMALIZE_K | (gdn.OPT_BF16_IO if bf16 else 0),
+                                   stream)
+            elif bf16:
+                gdn.gdn_forward_bf16(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                     d["output"], d["state_in"], d["capture"], params, stream)
+            elif w.capture:
+                gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                        d["state_in"], d["output"], d["state_in"],
+                                        d["capture"], params, stream)
+            else:
+                gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                d["output"], d["state_in"], params, stream)
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()  # barrier: one rank only
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        run_timed()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
-
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 18  # floats
-        a = torch.ones(n, device=dev)
-        b = torch.empty_like(a)
+        stream = torch.cuda.Stream(dev)
         torch.cuda.synchronize()
-        b.copy_(a)
+
+        def enqueue(n, offset):
+            if args.launch == "graph":
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(stream):
+                    with torch.cuda.graph(graph, stream=stream):
+                        for i in range(n):
+                            launch(offset + i, stream)
+                torch.cuda.synchronize()
+                return graph.replay
+            return lambda: [launch(offset + i, stream) for i in range(n)]
+
+        run_warm = enqueue(args.warmup, 0) if args.warmup > 0 else (lambda: None)
+        run_timed = enqueue(args.steps, args.warmup)
+        with torch.cuda.stream(stream):
+            run_warm()
         torch.cuda.synchronize()
-        del a, b
 
-    ms_per_step = wall * 1e3 / args.steps
-    digest = kernel_digest()
-    if w.name == "prefill" and not rollback:
-        metric_value = w.n_seqs * w.n_tokens * args.steps / wall
-        unit = "tokens/s"
-        achieved = w.flops() / kernel_s / 1e12
-        roofline = dict(bound="alu", achieved=achieved, peak=FP32_VECTOR_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=achieved / FP32_VECTOR_PEAK_TFLOPS)
-    else:
-        metric_value = alg_bytes * args.steps / wall / 1e9
-        unit = "GB/s"
-        achieved = alg_bytes / kernel_s / 1e9
-        roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=achieved / HBM_PEAK_GBPS)
-    roofline["traffic"] = (None if bf16 or args.normalize_k else
-                           traffic_from_profiles(args.workload, digest, kernel_name))
-    roofline["kernel"] = kernel_name
-    roofline["kernel_us"] = kernel_s * 1e6
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()  # barrier: one rank only
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            run_timed()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
 
-    line = {
-        "metric": METRIC,
-        "value": metric_value,
-        "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32" if not bf16 else "bf16 q/k/v/output, f32 state and arithmetic",
-        "data": "synthetic",
-        "config": {
-            "workload": description,
-            "d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads, "n_v_heads": w.n_v_heads,
-            "n_tokens": w.n_tokens, "n_seqs": w.n_seqs, "q_scale_bits": bits,
-            "capture": w.capture, "normalize_k": args.normalize_k,
-            "launch": args.launch, "resident_sets": layers,
-            "algorithmic_bytes_per_step": alg_bytes,
-            "flops_per_step": 0 if rollback else w.flops(),
-        },
-        "us_per_layer": ms_per_step * 1e3,
-        "state_gbps": w.state_bytes() / kernel_s / 1e9,
-        "roofline": roofline,
-        "kernel_digest": digest,
-    }
+        if args.calibrate_copy_mib:
+            n = args.calibrate_copy_mib << 18  # floats
+            a = torch.ones(n, device=dev)
+            b = torch.empty_like(a)
+            torch.cuda.synchronize()
+            b.copy_(a)
+            torch.cuda.synchronize()
+            del a, b
+
+        ms_per_step = wall * 1e3 / args.steps
+        digest = kernel_digest()
+        if w.name == "prefill" and not rollback:
+            metric_value = w.n_seqs * w.n_tokens * args.steps / wall
+            unit = "tokens/s"
+            achieved = w.flops() / kernel_s / 1e12
+            roofline = dict(bound="alu", achieved=achieved, peak=FP32_VECTOR_PEAK_TFLOPS,
+                            unit="TFLOP/s", frac=achieved / FP32_VECTOR_PEAK_TFLOPS)
+        else:
+            metric_value = alg_bytes * args.steps / wall / 1e9
+            unit = "GB/s"
+            achieved = alg_bytes / kernel_s / 1e9
+            roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                            frac=achieved / HBM_PEAK_GBPS)
+        roofline["traffic"] = (None if bf16 or args.normalize_k else
+                               traffic_from_profiles(args.workload, digest, kernel_name))
+        roofline["kernel"] = kernel_name
+        roofline["kernel_us"] = kernel_s * 1e6
+
+        line = {
+            "metric": METRIC,
+            "value": metric_value,
+            "unit": unit,
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms_per_step,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f32" if not bf16 else "bf16 q/k/v/output, f32 state and arithmetic",
+            "data": "synthetic",
+            "config": {
+                "workload": description,
+                "d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads, "n_v_heads": w.n_v_heads,
+                "n_tokens": w.n_tokens, "n_seqs": w.n_seqs, "q_scale_bits": bits,
+                "capture": w.capture, "normalize_k": args.normalize_k,
+                "launch": args.launch, "resident_sets": layers,
+                "algorithmic_bytes_per_step": alg_bytes,
+                "flops_per_step": 0 if rollback else w.flops(),
+            },
+            "us_per_layer": ms_per_step * 1e3,
+            "state_gbps": w.state_bytes() / kernel_s / 1e9,
+            "roofline": roofline,
+            "kernel_digest": digest,
+        }
+        return line, w, bf16, rollback
+
+    line, w, bf16, rollback = measure(args)
+    if (args.workload == "decode" and not bf16 and not args.normalize_k
+            and not args.no_prefill):
+        # The metric's other half: prefill tokens/s at n_tokens = 512, measured
+        # the same way (resident inputs, graph replay, events on the stream).
+        pargs = argparse.Namespace(**vars(args))
+        pargs.workload, pargs.steps, pargs.warmup = "prefill", args.prefill_steps, 200
+        pargs.layers, pargs.calibrate_copy_mib = 0, 0
+        p, *_ = measure(pargs)
+        line["prefill"] = {
+            "metric": "prefill tokens/s at n_tokens=512", "value": p["value"],
+            "unit": p["unit"], "steps": p["steps"], "warmup": p["warmup"],
+            "ms_per_step": p["ms_per_step"], "workload": p["config"]["workload"],
+            "roofline": p["roofline"]}
     if not args.no_cpu_baseline and not bf16 and not args.normalize_k:
         line["cpu_baseline"] = (cpu_baseline_rollback(w, args.cpu_seconds) if rollback
                                 else cpu_baseline(w, args.cpu_seconds))
