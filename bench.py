@@ -159,16 +159,19 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict,
     lines = [f"# {kernel}: {description}", "",
              f"kernel digest (sha256 of sources + flags) of the profiled build: `{digest}`", "",
              "## rocprofv3 --kernel-trace --stats", "", "```", commands["kt"], "```", "",
-             "| kernel | calls | average µs | median µs | min µs | max µs | share % |",
-             "|---|---|---|---|---|---|---|"]
+             "| kernel | calls | average µs | median µs | p10 / p90 µs | min µs | max µs | share % |",
+             "|---|---|---|---|---|---|---|---|"]
     for r in stats:
         name = r["Name"].replace("|", "/")
         if len(name) > 110:
             name = name[:107] + "..."
         d = sorted(durations.get(r["Name"], []))
         med = f"{(d[(len(d) - 1) // 2] + d[len(d) // 2]) / 2:.2f}" if d else "—"
+        # nearest-rank percentiles
+        pct = (f"{d[max(0, math.ceil(0.1 * len(d)) - 1)]:.2f} / "
+               f"{d[max(0, math.ceil(0.9 * len(d)) - 1)]:.2f}") if d else "—"
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {med} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{pct} | {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
     per = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):

@@ -114,7 +114,8 @@ def test_summarize_rocprof(bench, tmp_path):
     assert rec["hbm_bytes_per_launch"] == pytest.approx(fetch + write)
     text = open(md).read()
     assert "kt-cmd" in text and "fetch-cmd" in text and "write-cmd" in text
-    assert "| 220 | 3.65 | 3.10 | 2.80 | 7.00 |" in text  # average, median, min, max
+    # average, median, p10 / p90 (nearest rank of 2.8, 3.0, 3.2, 7.0), min, max
+    assert "| 220 | 3.65 | 3.10 | 2.80 / 7.00 | 2.80 | 7.00 |" in text
     assert f"ratio {(fetch + write) / 6_357_376:.3f}" in text
     assert bench.traffic_from_profiles(wl, digest, "gdn_decode", profiles=str(out)) == \
         pytest.approx(fetch + write)
