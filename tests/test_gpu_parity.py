@@ -165,6 +165,40 @@ def test_shapes(shape, capture):
             assert_equal(got[2][:, -1], got[1], "capture[T-1] == state_out")
 
 
+def random_shapes(n, seed):
+    """n shapes drawn from a fixed seed: D_k in {32, 64, 128}, D_v 1-160, T 1-40
+    (a third of them one token), 1-3 sequences, 1-3 key heads, GQA ratio 1-4,
+    with or without capture, q_scale and in-kernel key normalisation."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dk = int(rng.choice([32, 64, 128]))
+        t = 1 if rng.random() < 1 / 3 else int(rng.integers(2, 41))
+        hk = int(rng.integers(1, 4))
+        out.append(dict(shape=(dk, int(rng.integers(1, 161)), hk, hk * int(rng.integers(1, 5)),
+                               t, int(rng.integers(1, 4))),
+                        capture=bool(rng.random() < 0.5), fold=bool(rng.random() < 0.5),
+                        normalize_k=bool(rng.random() < 0.25)))
+    return out
+
+
+@pytest.mark.parametrize("case", random_shapes(32, 2026),
+                         ids=lambda c: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % c["shape"])
+def test_random_shapes(case):
+    """Shapes off the hand-picked list, drawn once from a fixed seed, against
+    the oracle on every element."""
+    dk, dv, hk, hv, t, s = case["shape"]
+    w = Workload("rand", 0, dk, dv, hk, hv, t, s)
+    x = make_inputs(w, seed=sum(case["shape"]))
+    bits = q_scale_bits_for(dk) if case["fold"] else 0
+    got = run(x, q_scale_bits=bits, capture=case["capture"], normalize_k=case["normalize_k"])
+    exp = ref(x, q_scale_bits=bits, capture=case["capture"], normalize_k=case["normalize_k"])
+    for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
+        close(g_, e, f"{case} {what}")
+    if case["capture"]:
+        assert_equal(got[2][:, -1], got[1], "capture[T-1] == state_out")
+
+
 @pytest.mark.parametrize("shape", [
     (32, 1, 1, 1, 1, 70000),      # sequences past one launch's 65535
     (32, 1, 1, 65540, 1, 1),      # value heads past 65535 (GQA ratio 65540)
