@@ -777,6 +777,9 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     const bool flush = NB % TB == 0 ? j == TB - 1 || (may_end && t + 1 == T)
                                     : (t & (TB - 1)) == TB - 1 || t + 1 == T;
     if (flush) {
+      // The batch's reduce-scatter and store are a dependent chain as well:
+      // raised priority (512-token prefill -1.2%).
+      __builtin_amdgcn_s_setprio(1);
       // Token slots 0 .. t % TB hold tokens t0 .. t. base_t is a multiple of
       // 64 and at most t, so t0 - base_t >= 0. q_scale is applied here.
       const uint32_t t0 = t & ~(TB - 1);
@@ -796,6 +799,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
 #pragma unroll
         for (int r = 0; r < NY; ++r)
           if (ok[r]) Io<IO>::store1(o_rs, yoff[r], soff, yk[r] * a.q_scale);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
