@@ -935,6 +935,10 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
           }
           if (u == NB - 1) park_krow(add_krow(kn, KP == 2 ? kss : 0.f));
         }
+        // Raised issue priority from here through delta (step drops it):
+        // the prefetch request and the next token's staging are issued
+        // ahead of the other waves' throughput work (-1%).
+        __builtin_amdgcn_s_setprio(1);
         const uint32_t ahead = t + NB - 1;
         load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
         // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
