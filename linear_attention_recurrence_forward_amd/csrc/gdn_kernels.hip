@@ -1231,8 +1231,10 @@ constexpr Geometry make_decode_geometry() {
 //                four-token ring: 4-token verify 5.88 -> 5.64 us. The two-row geometry was
 //                best or within 2% of the best measured variant from 2 tokens
 //                up (2 to 512), so one token is the only short-run case. At
-//                D_k = 64, 8 lanes per row (8 cells each): 512-token prefill
-//                145 -> 135 us against 16.
+//                D_k = 64, 16 lanes per row (4 cells each), two waves and an
+//                eight-token ring (twice the waves of 8 lanes per row with
+//                8 cells): 512-token prefill 139 -> 96 us, 16 tokens 8.1 ->
+//                7.1 us, a 4-token verify with capture 4.6 -> 3.8 us.
 // Compute units of an MI355X.
 constexpr uint64_t kComputeUnits = 256;
 
@@ -1247,7 +1249,7 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
                        : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NK>();
     case 64:
       return one_token ? make_decode_geometry<64, 4, 1, 4, CAPTURE, IO, NK1>()
-                       : make_geometry<64, 8, 2, 4, 4, CAPTURE, IO, NK>();
+                       : make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
     case 128:
       if (one_token) {
         // A grid of two-row workgroups that leaves compute units idle (one
