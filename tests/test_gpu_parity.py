@@ -139,6 +139,10 @@ SHAPES = [
     (128, 72, 8, 96, 1, 1),
     (64, 40, 2, 4, 1, 3),
     (32, 70, 1, 3, 1, 2),
+    # D_k = 64 one-token grids large enough for two rows per lane, with and
+    # without padded row blocks
+    (64, 40, 4, 64, 1, 2),
+    (64, 72, 8, 96, 1, 1),
     (128, 256, 1, 2, 129, 1),
     # one ring group exactly; 64 + 8 tokens with rows that split a wave's
     # rows unevenly; a 64-token chunk plus one D_k = 64 group
