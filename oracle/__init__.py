@@ -6,7 +6,7 @@ never imports it.
 """
 
 from .gdn_oracle import (HEAD_MAP_DIV, HEAD_MAP_MOD, build, reference, reference_bf16,
-                         rollback, to_bf16)
+                         reference_threads, rollback, rollback_threads, to_bf16)
 
 __all__ = ["HEAD_MAP_DIV", "HEAD_MAP_MOD", "build", "reference", "reference_bf16",
-           "rollback", "to_bf16"]
+           "reference_threads", "rollback", "rollback_threads", "to_bf16"]

@@ -75,10 +75,14 @@ float scale_from_bits(uint32_t bits) {
 
 // kreal: element type of the key array the recurrence reads (the caller's f32
 // keys, or keys normalised in the oracle's own precision).
+// The (sequence, value head) pairs are independent: [pair_begin, pair_end)
+// selects which ones run, in the order s * n_v_heads + vh (all of them for a
+// whole call; the timing harness splits that range over threads).
 template <typename real, typename kreal>
 int run(const float *q, const kreal *k, const float *v, const float *g,
         const float *beta, const float *state_in, const oracle_gdn_shape *p,
-        int head_map, real *output, real *state_out, real *capture) {
+        int head_map, real *output, real *state_out, real *capture,
+        uint64_t pair_begin = 0, uint64_t pair_end = UINT64_MAX) {
   if (p == nullptr || q == nullptr || k == nullptr || v == nullptr ||
       g == nullptr || beta == nullptr || state_in == nullptr ||
       output == nullptr || state_out == nullptr)
@@ -114,49 +118,49 @@ int run(const float *q, const kreal *k, const float *v, const float *g,
   };
 
   std::vector<real> X(Dv * Dk);
-  for (uint64_t s = 0; s < S; ++s) {
-    for (uint64_t vh = 0; vh < Hv; ++vh) {
-      const uint64_t kh =
-          head_map == ORACLE_HEAD_MAP_MOD ? vh % Hk : vh / group_ratio;
+  if (pair_end > S * Hv) pair_end = S * Hv;
+  for (uint64_t pair = pair_begin; pair < pair_end; ++pair) {
+    const uint64_t s = pair / Hv, vh = pair % Hv;
+    const uint64_t kh =
+        head_map == ORACLE_HEAD_MAP_MOD ? vh % Hk : vh / group_ratio;
 
-      for (uint64_t i = 0; i < Dv; ++i)
-        for (uint64_t j = 0; j < Dk; ++j)
-          X[i * Dk + j] = static_cast<real>(state_in[at_state(s, vh, i, j)]);
+    for (uint64_t i = 0; i < Dv; ++i)
+      for (uint64_t j = 0; j < Dk; ++j)
+        X[i * Dk + j] = static_cast<real>(state_in[at_state(s, vh, i, j)]);
 
-      for (uint64_t t = 0; t < T; ++t) {
-        const real alpha = decay_factor<real>(g[at_scalar(s, t, vh)]);
-        const real b = static_cast<real>(beta[at_scalar(s, t, vh)]);
+    for (uint64_t t = 0; t < T; ++t) {
+      const real alpha = decay_factor<real>(g[at_scalar(s, t, vh)]);
+      const real b = static_cast<real>(beta[at_scalar(s, t, vh)]);
 
-        for (uint64_t i = 0; i < Dv; ++i) {
-          real *row = &X[i * Dk];
+      for (uint64_t i = 0; i < Dv; ++i) {
+        real *row = &X[i * Dk];
 
-          real sk = 0;
-          for (uint64_t j = 0; j < Dk; ++j) {
-            row[j] = alpha * row[j];
-            sk = sk + row[j] * static_cast<real>(k[at_qk(s, t, kh, j)]);
-          }
-
-          const real d = (static_cast<real>(v[at_v(s, t, vh, i)]) - sk) * b;
-
-          real y = 0;
-          for (uint64_t j = 0; j < Dk; ++j) {
-            row[j] = row[j] + d * static_cast<real>(k[at_qk(s, t, kh, j)]);
-            y = y + row[j] * static_cast<real>(q[at_qk(s, t, kh, j)]);
-          }
-
-          output[at_v(s, t, vh, i)] = y * q_scale;
+        real sk = 0;
+        for (uint64_t j = 0; j < Dk; ++j) {
+          row[j] = alpha * row[j];
+          sk = sk + row[j] * static_cast<real>(k[at_qk(s, t, kh, j)]);
         }
 
-        if (capture != nullptr)
-          for (uint64_t i = 0; i < Dv; ++i)
-            for (uint64_t j = 0; j < Dk; ++j)
-              capture[at_capture(s, t, vh, i, j)] = X[i * Dk + j];
+        const real d = (static_cast<real>(v[at_v(s, t, vh, i)]) - sk) * b;
+
+        real y = 0;
+        for (uint64_t j = 0; j < Dk; ++j) {
+          row[j] = row[j] + d * static_cast<real>(k[at_qk(s, t, kh, j)]);
+          y = y + row[j] * static_cast<real>(q[at_qk(s, t, kh, j)]);
+        }
+
+        output[at_v(s, t, vh, i)] = y * q_scale;
       }
 
-      for (uint64_t i = 0; i < Dv; ++i)
-        for (uint64_t j = 0; j < Dk; ++j)
-          state_out[at_state(s, vh, i, j)] = X[i * Dk + j];
+      if (capture != nullptr)
+        for (uint64_t i = 0; i < Dv; ++i)
+          for (uint64_t j = 0; j < Dk; ++j)
+            capture[at_capture(s, t, vh, i, j)] = X[i * Dk + j];
     }
+
+    for (uint64_t i = 0; i < Dv; ++i)
+      for (uint64_t j = 0; j < Dk; ++j)
+        state_out[at_state(s, vh, i, j)] = X[i * Dk + j];
   }
   return 0;
 }
@@ -243,6 +247,21 @@ int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
                            double *state_capture) {
   return run<double, float>(q, k, v, g, beta, state_in, p, head_map, output,
                             state_out, state_capture);
+}
+
+// oracle_gdn_forward_f32 restricted to the (sequence, value head) pairs
+// [pair_begin, pair_end) in the order s * n_v_heads + vh: the same loop body,
+// so disjoint ranges run on separate threads give the whole call's result bit
+// for bit. Only the selected pairs' outputs, state and capture are written.
+int oracle_gdn_forward_range_f32(const float *q, const float *k, const float *v,
+                                 const float *g, const float *beta,
+                                 const float *state_in,
+                                 const oracle_gdn_shape *p, int head_map,
+                                 uint64_t pair_begin, uint64_t pair_end,
+                                 float *output, float *state_out,
+                                 float *state_capture) {
+  return run<float, float>(q, k, v, g, beta, state_in, p, head_map, output,
+                           state_out, state_capture, pair_begin, pair_end);
 }
 
 // As the two above, with option bits: 2 = normalise every key row first

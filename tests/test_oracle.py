@@ -59,3 +59,26 @@ def test_f32_within_budget_of_f64_shadow(name):
     res64 = oracle.reference(**x, capture=w.capture, precision="f64")
     for a, e, what in zip(res32, res64, ("output", "state_out", "capture")):
         assert_within(a, e, 1e-5 + 1e-4 * np.abs(e), f"{name} {what}")
+
+
+@pytest.mark.parametrize("threads", [1, 3, 8])
+def test_threaded_oracle_is_bit_identical(threads):
+    """The all-core timing splits the independent (sequence, value head) pairs
+    over threads: the result equals one whole call bit for bit, with and
+    without capture, and the threaded rollback equals the plain one."""
+    w = WORKLOADS["spec_verify"].with_(n_seqs=3, n_v_heads=8, n_k_heads=4, d_v=40)
+    x = make_inputs(w, seed=3)
+    bits = x["q_scale_bits"]
+    names = ("q", "k", "v", "g", "beta", "state_in")
+    for capture in (False, True):
+        one = oracle.reference(**{n: x[n] for n in names}, q_scale_bits=bits,
+                               capture=capture)
+        par = oracle.reference_threads(**{n: x[n] for n in names}, q_scale_bits=bits,
+                                       capture=capture, threads=threads)
+        for a, b in zip(one, par):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    _, _, cap = oracle.reference(**{n: x[n] for n in names}, capture=True)
+    acc = np.array([0, w.n_tokens, 2], np.uint32)
+    base = np.full(x["state_in"].shape, 3.0, np.float32)
+    assert np.array_equal(oracle.rollback_threads(cap, acc, base, threads=threads),
+                          oracle.rollback(cap, acc, base))

@@ -25,7 +25,7 @@ Y = "y = y + row[j] * static_cast<real>(q[at_qk(s, t, kh, j)]);"
 
 MUTANTS = {
     # The other reading of the decay order: sk from the undecayed state.
-    "sk_before_decay": [(f"{DECAY}\n            {SK}", f"{SK}\n            {DECAY}")],
+    "sk_before_decay": [(f"{DECAY}\n          {SK}", f"{SK}\n          {DECAY}")],
     "no_decay": [(DECAY, "row[j] = row[j];")],
     "exp_of_plus_g": [("return expf(-g);", "return expf(g);"),
                       ("exp(-static_cast<double>(g))", "exp(static_cast<double>(g))")],
@@ -34,7 +34,7 @@ MUTANTS = {
     "no_beta": [("- sk) * b;", "- sk);")],
     "beta_read_from_g": [("static_cast<real>(beta[at_scalar(s, t, vh)])",
                           "static_cast<real>(g[at_scalar(s, t, vh)])")],
-    "y_before_update": [(f"{UPDATE}\n            {Y}", f"{Y}\n            {UPDATE}")],
+    "y_before_update": [(f"{UPDATE}\n          {Y}", f"{Y}\n          {UPDATE}")],
     "y_reads_k": [(Y, Y.replace("(q[", "(k["))],
     "update_uses_q": [(UPDATE, UPDATE.replace("(k[", "(q["))],
     "sk_drops_last_term": [(SK, f"if (j + 1 < Dk) {SK}")],
