@@ -13,12 +13,22 @@ other layers' traffic evicts it between steps.
 
 The K timed steps are enqueued as one HIP graph (launch-bound decode calls are
 captured in serving loops for the same reason) or, with --launch direct, one
-launch at a time. HIP events on the launch stream bracket the timed region and
-give the kernel's average launch duration, from which the roofline fraction is
-computed. Prints one JSON line. The single-layer decode line (the default)
-also carries a "prefill" object: the 512-token prefill workload measured the
-same way (tokens/s and its roofline), the other half of the headline metric
-(--no-prefill leaves it out).
+launch at a time, bracketed by a device synchronisation on both sides; `value`
+and `ms_per_step` come from the host clock over those K steps.
+
+The kernel's per-launch duration, from which the roofline fraction is computed,
+comes from HIP events on the launch stream. A graph replay carries a fixed
+entry and exit cost of several microseconds, which a short replay would spread
+over its few steps, so the per-launch duration is the difference of a 2K-step
+and the K-step replay divided by K (the median over several pairs): the fixed
+cost cancels, and the figure does not depend on K.
+
+Prints one JSON line. The single-layer decode line (the default) also carries
+one object per other workload of the headline metric: "prefill" (512-token
+prefill, tokens/s), "batched_decode", "spec_verify" and "rollback", each with
+its own roofline and CPU baseline (--no-extra leaves them out). Every CPU
+baseline times the oracle on one core and on all the host's cores (threads
+over the independent (sequence, value head) pairs) and names the CPU.
 """
 
 from __future__ import annotations
@@ -27,6 +37,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -45,6 +56,12 @@ METRIC = "GDN decode µs/layer + state HBM GB/s (%peak); prefill tokens/s at n_t
 KERNEL_NAME = "gdn_recurrent"      # multi-token forward calls
 DECODE_KERNEL_NAME = "gdn_decode"  # one-token forward calls
 NAMES = ("q", "k", "v", "g", "beta", "state_in")
+# The headline line's other workloads: (name, timed steps, warm-up steps). Each
+# timed region covers tens of milliseconds of GPU work whatever --steps is
+# (the 512-token prefill needs a longer warm-up to reach its loaded clock).
+EXTRA = (("prefill", 500, 200), ("batched_decode", 500, 50), ("spec_verify", 2000, 200),
+         ("rollback", 2000, 200))
+MAX_WORKER_THREADS = 16  # the host CPU share of one GPU on the GPU machines
 
 
 def parse_args(argv=None):
@@ -63,15 +80,13 @@ def parse_args(argv=None):
                     help="L2-normalise every key row in the kernel (gdn_forward_ex)")
     ap.add_argument("--layers", type=int, default=0,
                     help="input sets to cycle through (0: enough for 1 GiB)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU time budget of each oracle baseline sample (half on one "
+                         "core, half on all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="leave out the 512-token prefill measurement that the "
-                         "single-layer decode line carries as its 'prefill' object")
-    ap.add_argument("--prefill-steps", type=int, default=1000,
-                    help="timed calls of that prefill measurement (after 200 untimed "
-                         "ones: shorter runs catch the clock below its loaded level)")
+    ap.add_argument("--no-extra", "--no-prefill", dest="no_extra", action="store_true",
+                    help="leave out the other workloads' objects that the "
+                         "single-layer decode line carries")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference kernel for the HBM byte counters)")
@@ -87,9 +102,29 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def kernel_digest() -> str:
+def built_digest() -> str:
+    """The build stamp written next to libgdn.so when it was compiled: the
+    digest of the sources and flags it was built from."""
     from linear_attention_recurrence_forward_amd import build
-    return build.source_digest()
+    path = os.path.join(build.LIBDIR, "libgdn.digest")
+    if not os.path.exists(path):
+        return ""
+    with open(path) as f:
+        return f.read().strip()
+
+
+def check_build() -> str:
+    """Digest of the library that will be timed; exits (status 3) when its build
+    stamp is missing or differs from the current sources, so that a figure is
+    never reported under a build it was not measured on."""
+    from linear_attention_recurrence_forward_amd import build
+    stamp, current = built_digest(), build.source_digest()
+    if stamp != current:
+        print(f"bench.py: lib/libgdn.so was built from other sources (stamp "
+              f"{stamp or 'missing'}, sources {current}); rebuild it with "
+              "`python -m linear_attention_recurrence_forward_amd.build`", file=sys.stderr)
+        raise SystemExit(3)
+    return stamp
 
 
 def traffic_from_profiles(workload: str, digest: str, kernel: str = KERNEL_NAME,
@@ -209,55 +244,96 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict,
     return md
 
 
-def cpu_baseline(w, budget_s: float):
+def host_cpu() -> dict:
+    """The host CPU: model name, logical CPUs, the CPUs this process may run
+    on, and the worker threads the all-core baseline uses (at most the CPU
+    share of one GPU)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (
+        os.cpu_count() or 1)
+    return dict(model=model, nproc=os.cpu_count() or 1, usable=usable,
+                threads=max(1, min(usable, MAX_WORKER_THREADS)))
+
+
+def _timed_calls(fn, budget_s: float):
+    """Call fn until budget_s has passed (at least once); (calls, seconds)."""
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            return calls, dt
+
+
+def cpu_baseline(w, budget_s: float, rollback: bool = False):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    whole calls for small workloads, a prefix of the sequences for large ones.
-    Returns the rate in the benchmark's unit and a description of the sample."""
-    import oracle
-    x = make_inputs(w)
-    bits = x["q_scale_bits"]
-    args = {n: x[n] for n in NAMES}
-    t0 = time.perf_counter()
-    oracle.reference(**{n: a[:1] for n, a in args.items()}, q_scale_bits=bits,
-                     capture=w.capture)
-    per_seq = time.perf_counter() - t0
-    seqs = max(1, min(w.n_seqs, int(budget_s / max(per_seq, 1e-9))))
-    calls = 1 if seqs < w.n_seqs else max(1, int(budget_s / (per_seq * w.n_seqs)))
-    t0 = time.perf_counter()
-    for _ in range(calls):
-        oracle.reference(**{n: a[:seqs] for n, a in args.items()}, q_scale_bits=bits,
-                         capture=w.capture)
-    dt = time.perf_counter() - t0
-    frac = seqs / w.n_seqs
-    if w.name == "prefill":
-        value = calls * frac * w.n_seqs * w.n_tokens / dt
-        unit = "tokens/s"
-    else:
-        value = calls * frac * w.algorithmic_bytes() / dt / 1e9
-        unit = "GB/s"
-    sample = (f"{calls} oracle call(s) over {seqs} of {w.n_seqs} sequence(s) of the "
-              f"{w.name} workload, {dt:.1f} s, single thread")
-    return dict(value=value, unit=unit, cores=1, kind="oracle", sample=sample)
-
-
-def cpu_baseline_rollback(w, budget_s: float):
-    """The oracle's rollback copy, timed on the host like cpu_baseline."""
+    on one thread (whole calls, or a prefix of the sequences when one call
+    would exceed half the budget), then on all the host's cores (the same
+    oracle loop over disjoint ranges of (sequence, value head) pairs, one range
+    per thread, whole calls). Rates in the benchmark's unit: tokens/s for the
+    prefill, algorithmic GB/s otherwise. rollback: the oracle's rollback copy
+    on the spec_verify shape."""
     import numpy as np
     import oracle
-    rng = np.random.default_rng(w.seed)
-    cap = rng.standard_normal((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
-                              dtype=np.float32)
-    state = np.zeros((w.n_seqs, w.n_v_heads, w.d_v, w.d_k), np.float32)
-    acc = rng.integers(0, w.n_tokens, size=w.n_seqs).astype(np.uint32)
-    calls, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        oracle.rollback(cap, acc, state)
-        calls += 1
-    dt = time.perf_counter() - t0
-    return dict(value=calls * (w.state_bytes() + 4 * w.n_seqs) / dt / 1e9, unit="GB/s",
-                cores=1, kind="oracle",
-                sample=f"{calls} oracle rollback calls on the spec_verify shape, "
-                       f"{dt:.1f} s, single thread")
+    cpu = host_cpu()
+    half = budget_s / 2
+    if rollback:
+        rng = np.random.default_rng(w.seed)
+        cap = rng.standard_normal((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
+                                  dtype=np.float32)
+        state = np.zeros((w.n_seqs, w.n_v_heads, w.d_v, w.d_k), np.float32)
+        acc = rng.integers(0, w.n_tokens, size=w.n_seqs).astype(np.uint32)
+        per_call = w.state_bytes() + 4 * w.n_seqs
+        c1, d1 = _timed_calls(lambda: oracle.rollback(cap, acc, state), half)
+        cn, dn = _timed_calls(lambda: oracle.rollback_threads(cap, acc, state,
+                                                              threads=cpu["threads"]), half)
+        one = c1 * per_call / d1 / 1e9
+        alln = cn * per_call / dn / 1e9
+        unit = "GB/s"
+        s1 = f"{c1} oracle rollback calls on the spec_verify shape, {d1:.1f} s, 1 thread"
+        sn = (f"{cn} oracle rollback calls on the spec_verify shape, {dn:.1f} s, "
+              f"{min(cpu['threads'], w.n_seqs)} threads over the sequences")
+        used = min(cpu["threads"], w.n_seqs)
+    else:
+        x = make_inputs(w)
+        bits = x["q_scale_bits"]
+        args = {n: x[n] for n in NAMES}
+        t0 = time.perf_counter()
+        oracle.reference(**{n: a[:1] for n, a in args.items()}, q_scale_bits=bits,
+                         capture=w.capture)
+        per_seq = time.perf_counter() - t0
+        seqs = max(1, min(w.n_seqs, int(half / max(per_seq, 1e-9))))
+        part = {n: a[:seqs] for n, a in args.items()}
+        c1, d1 = _timed_calls(lambda: oracle.reference(**part, q_scale_bits=bits,
+                                                       capture=w.capture), half)
+        pairs = w.n_seqs * w.n_v_heads
+        used = min(cpu["threads"], pairs)
+        cn, dn = _timed_calls(lambda: oracle.reference_threads(
+            **args, q_scale_bits=bits, capture=w.capture, threads=used), half)
+        if w.name == "prefill":
+            unit = "tokens/s"
+            one = c1 * seqs * w.n_tokens / d1
+            alln = cn * w.n_seqs * w.n_tokens / dn
+        else:
+            unit = "GB/s"
+            one = c1 * (seqs / w.n_seqs) * w.algorithmic_bytes() / d1 / 1e9
+            alln = cn * w.algorithmic_bytes() / dn / 1e9
+        s1 = (f"{c1} oracle call(s) over {seqs} of {w.n_seqs} sequence(s) of the {w.name} "
+              f"workload, {d1:.1f} s, 1 thread")
+        sn = (f"{cn} whole oracle call(s) of the {w.name} workload, {dn:.1f} s, {used} "
+              f"threads over its {pairs} (sequence, value head) pairs")
+    return dict(value=alln, unit=unit, cores=used, kind="oracle", sample=sn,
+                single_core=dict(value=one, unit=unit, cores=1, sample=s1),
+                cpu_model=cpu["model"], nproc=cpu["nproc"], usable_cpus=cpu["usable"])
 
 
 VALU_PASSES = (
@@ -346,6 +422,205 @@ def summarize_valu_counters(src: str, out_dir: str | None = None) -> str:
     return path
 
 
+def measure(name: str, *, steps: int, warmup: int, launch: str = "graph", io: str = "f32",
+            normalize_k: bool = False, layers: int = 0, calibrate_copy_mib: int = 0,
+            digest: str = ""):
+    """One workload's timed run on cuda:0 (see the module doc). Returns the
+    measurement as a dict (without CPU baseline)."""
+    import torch
+    import linear_attention_recurrence_forward_amd as gdn
+
+    dev = torch.device("cuda:0")
+    rollback = name == "rollback"
+    if (io == "bf16" or normalize_k) and rollback:
+        raise SystemExit("bench.py: --io bf16 and --normalize-k apply to forward workloads")
+    bf16 = io == "bf16"
+    w, kernel_name, alg_bytes, description = workload_info(name, io)
+    x = make_inputs(w)
+    bits = x["q_scale_bits"]
+    layers = layers or max(2, math.ceil(RESIDENT_TARGET_BYTES / max(alg_bytes, 1)))
+    layers = min(layers, 4096)
+
+    # Resident input sets: same values, distinct memory (state updated in place).
+    host = {n: torch.from_numpy(x[n]) for n in NAMES}
+    if bf16:
+        for n in ("q", "k", "v"):
+            host[n] = host[n].to(torch.bfloat16)
+    sets = []
+    for _ in range(layers):
+        d = {n: host[n].to(dev) for n in NAMES}
+        d["output"] = torch.empty(x["v"].shape, device=dev,
+                                  dtype=torch.bfloat16 if bf16 else torch.float32)
+        d["capture"] = (torch.empty((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
+                                    device=dev) if w.capture else None)
+        sets.append(d)
+    params = gdn.params_for(sets[0]["q"], sets[0]["v"], bits)
+    if rollback:
+        # Fill every set's capture with a real forward call, then pick per
+        # sequence a token to roll back to (all inside the call).
+        rng = torch.Generator().manual_seed(w.seed)
+        for d in sets:
+            gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                    d["state_in"], d["output"], d["state_in"],
+                                    d["capture"], params)
+            d["accepted"] = torch.randint(0, w.n_tokens, (w.n_seqs,), generator=rng,
+                                          dtype=torch.int32).to(dev)
+        torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream(dev)
+
+    def launch_one(i):
+        d = sets[i % layers]
+        if rollback:
+            gdn.gdn_rollback(d["capture"], d["accepted"], d["state_in"], params, stream)
+        elif normalize_k:
+            gdn.gdn_forward_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                               d["output"], d["state_in"], d["capture"], params,
+                               gdn.OPT_NORMALIZE_K | (gdn.OPT_BF16_IO if bf16 else 0),
+                               stream)
+        elif bf16:
+            gdn.gdn_forward_bf16(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                 d["output"], d["state_in"], d["capture"], params, stream)
+        elif w.capture:
+            gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                    d["state_in"], d["output"], d["state_in"],
+                                    d["capture"], params, stream)
+        else:
+            gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                            d["output"], d["state_in"], params, stream)
+
+    torch.cuda.synchronize()
+
+    def enqueue(n, offset):
+        if launch == "graph":
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(graph, stream=stream):
+                    for i in range(n):
+                        launch_one(offset + i)
+            torch.cuda.synchronize()
+            return graph.replay
+        return lambda: [launch_one(offset + i) for i in range(n)]
+
+    def events(run):
+        """Seconds between HIP events recorded on the launch stream around run()."""
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            run()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3
+
+    run_warm = enqueue(warmup, 0) if warmup > 0 else (lambda: None)
+    run_timed = enqueue(steps, warmup)
+    with torch.cuda.stream(stream):
+        run_warm()
+    torch.cuda.synchronize()
+
+    # The timed region: exactly `steps` steps, synchronised on both sides.
+    torch.cuda.synchronize()  # barrier: one rank only
+    t0 = time.perf_counter()
+    event_s = events(run_timed)
+    wall = time.perf_counter() - t0
+
+    # Per-launch kernel duration: graph replays of 2K and K steps, differenced.
+    # Each pair has its own two graphs, which continue the walk through the
+    # ring of input sets where the timed region left it. All graphs are
+    # replayed once untimed (a graph's first launch carries set-up costs that
+    # grow with its length), then again in the same order under events: the
+    # walk is at least as long as the ring, so every call still finds its
+    # state evicted from the caches, as in the timed region.
+    if launch == "graph":
+        per_rep = 3 * event_s
+        reps = max(3, min(25, int(1.0 / max(per_rep, 1e-9)), 30000 // (3 * steps)))
+        reps = max(reps, math.ceil(layers / (3 * steps)))
+        pairs, offset = [], warmup + steps
+        for _ in range(reps):
+            pairs.append((enqueue(steps, offset), enqueue(2 * steps, offset + steps)))
+            offset += 3 * steps
+        for run_k, run_2k in pairs:
+            events(run_k)
+            events(run_2k)
+        diffs = []
+        for run_k, run_2k in pairs:
+            e1 = events(run_k)
+            e2 = events(run_2k)
+            diffs.append((e2 - e1) / steps)
+        del pairs
+        kernel_s = statistics.median(diffs)
+        method = (f"median over {reps} pairs of (events({2 * steps}-step replay) - "
+                  f"events({steps}-step replay)) / {steps}; every replay repeated, each "
+                  f"call's input set last used {reps * 3 * steps} calls before")
+    else:
+        kernel_s = event_s / steps
+        method = f"events around the {steps} timed launches / {steps}"
+
+    if calibrate_copy_mib:
+        n = calibrate_copy_mib << 18  # floats
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    ms_per_step = wall * 1e3 / steps
+    if w.name == "prefill" and not rollback:
+        value = w.n_seqs * w.n_tokens * steps / wall
+        unit = "tokens/s"
+        achieved = w.flops() / kernel_s / 1e12
+        roofline = dict(bound="alu", achieved=achieved, peak=FP32_VECTOR_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=achieved / FP32_VECTOR_PEAK_TFLOPS)
+    else:
+        value = alg_bytes * steps / wall / 1e9
+        unit = "GB/s"
+        achieved = alg_bytes / kernel_s / 1e9
+        roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=achieved / HBM_PEAK_GBPS)
+    roofline["traffic"] = (None if bf16 or normalize_k else
+                           traffic_from_profiles(name, digest, kernel_name))
+    roofline["kernel"] = kernel_name
+    roofline["kernel_us"] = kernel_s * 1e6
+    roofline["kernel_us_method"] = method
+    return dict(
+        name=name, w=w, bf16=bf16, rollback=rollback, value=value, unit=unit, steps=steps,
+        warmup=warmup, ms_per_step=ms_per_step, event_us_per_step=event_s * 1e6 / steps,
+        kernel_us=kernel_s * 1e6, roofline=roofline, description=description,
+        bits=bits, layers=layers, alg_bytes=alg_bytes,
+        state_gbps=w.state_bytes() / kernel_s / 1e9)
+
+
+def progress(m: dict) -> None:
+    """One progress line on stderr per measured workload."""
+    r = m["roofline"]
+    print(f"bench: {m['name']}: {m['ms_per_step'] * 1e3:.2f} us per step (host clock), "
+          f"kernel {m['kernel_us']:.3f} us, {r['achieved']:.1f} {r['unit']} = "
+          f"{r['frac']:.3f} of peak", file=sys.stderr, flush=True)
+
+
+def extra_object(m: dict, cpu: dict | None) -> dict:
+    """A non-headline workload's measurement as an object of the bench line."""
+    w = m["w"]
+    obj = {"metric": ("prefill tokens/s at n_tokens=512" if m["unit"] == "tokens/s" else
+                      "µs per call + algorithmic HBM GB/s (%peak)"),
+           "value": m["value"], "unit": m["unit"], "steps": m["steps"],
+           "warmup": m["warmup"], "ms_per_step": m["ms_per_step"],
+           "us_per_call": m["ms_per_step"] * 1e3, "kernel_us": m["kernel_us"],
+           "workload": m["description"],
+           "shape": {"d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads,
+                     "n_v_heads": w.n_v_heads, "n_tokens": w.n_tokens,
+                     "n_seqs": w.n_seqs, "q_scale_bits": m["bits"], "capture": w.capture},
+           "algorithmic_bytes_per_step": m["alg_bytes"],
+           "roofline": m["roofline"]}
+    if m["unit"] == "GB/s":
+        obj["state_gbps"] = m["state_gbps"]
+    if cpu is not None:
+        obj["cpu_baseline"] = cpu
+    return obj
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.summarize_valu_counters:
@@ -354,10 +629,10 @@ def main(argv=None):
     if args.summarize_rocprof:
         cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt_{w} -o run "
                "-- python3 bench.py --workload {w} --steps 200 --warmup 20 --no-cpu-baseline "
-               "--no-prefill")
+               "--no-extra")
         pmc = ("rocprofv3 --pmc {c} --output-format csv -d <dir>/pmc_{c}_{w} -o run -- "
                "python3 bench.py --workload {w} --steps 10 --warmup 2 --layers 4 "
-               "--no-cpu-baseline --no-prefill --launch direct --calibrate-copy-mib 1024")
+               "--no-cpu-baseline --no-extra --launch direct --calibrate-copy-mib 1024")
         for wl in sorted(WORKLOADS) + ["rollback"]:
             if os.path.isdir(os.path.join(args.summarize_rocprof, f"kt_{wl}")):
                 print(summarize_rocprof(args.summarize_rocprof, wl, 1024, dict(
@@ -370,180 +645,65 @@ def main(argv=None):
               "so a multi-GPU figure would be N independent copies of this one.",
               file=sys.stderr)
         return 2
+    digest = check_build()
 
     import torch
-    import linear_attention_recurrence_forward_amd as gdn
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    def measure(args):
-        """One workload's timed run; returns (line without cpu_baseline,
-        workload, bf16, rollback)."""
-        rollback = args.workload == "rollback"
-        if (args.io == "bf16" or args.normalize_k) and args.workload == "rollback":
-            raise SystemExit("bench.py: --io bf16 and --normalize-k apply to forward workloads")
-        bf16 = args.io == "bf16"
-        w, kernel_name, alg_bytes, description = workload_info(args.workload, args.io)
-        x = make_inputs(w)
-        bits = x["q_scale_bits"]
-        layers = args.layers or max(2, math.ceil(RESIDENT_TARGET_BYTES / max(alg_bytes, 1)))
-        layers = min(layers, 4096)
+    torch.cuda.set_device(torch.device("cuda:0"))
 
-        # Resident input sets: same values, distinct memory (state updated in place).
-        host = {n: torch.from_numpy(x[n]) for n in NAMES}
-        if bf16:
-            for n in ("q", "k", "v"):
-                host[n] = host[n].to(torch.bfloat16)
-        sets = []
-        for _ in range(layers):
-            d = {n: host[n].to(dev) for n in NAMES}
-            d["output"] = torch.empty(x["v"].shape, device=dev,
-                                      dtype=torch.bfloat16 if bf16 else torch.float32)
-            d["capture"] = (torch.empty((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
-                                        device=dev) if w.capture else None)
-            sets.append(d)
-        params = gdn.params_for(sets[0]["q"], sets[0]["v"], bits)
-        if rollback:
-            # Fill every set's capture with a real forward call, then pick per
-            # sequence a token to roll back to (all inside the call).
-            rng = torch.Generator().manual_seed(w.seed)
-            for d in sets:
-                gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                        d["state_in"], d["output"], d["state_in"],
-                                        d["capture"], params)
-                d["accepted"] = torch.randint(0, w.n_tokens, (w.n_seqs,), generator=rng,
-                                              dtype=torch.int32).to(dev)
-            torch.cuda.synchronize()
-
-        def launch(i, stream):
-            d = sets[i % layers]
-            if rollback:
-                gdn.gdn_rollback(d["capture"], d["accepted"], d["state_in"], params, stream)
-            elif args.normalize_k:
-                gdn.gdn_forward_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
-                                   d["output"], d["state_in"], d["capture"], params,
-                                   gdn.OPT_NORMALIZE_K | (gdn.OPT_BF16_IO if bf16 else 0),
-                                   stream)
-            elif bf16:
-                gdn.gdn_forward_bf16(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
-                                     d["output"], d["state_in"], d["capture"], params, stream)
-            elif w.capture:
-                gdn.gdn_forward_capture(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                        d["state_in"], d["output"], d["state_in"],
-                                        d["capture"], params, stream)
-            else:
-                gdn.gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
-                                d["output"], d["state_in"], params, stream)
-
-        stream = torch.cuda.Stream(dev)
-        torch.cuda.synchronize()
-
-        def enqueue(n, offset):
-            if args.launch == "graph":
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.stream(stream):
-                    with torch.cuda.graph(graph, stream=stream):
-                        for i in range(n):
-                            launch(offset + i, stream)
-                torch.cuda.synchronize()
-                return graph.replay
-            return lambda: [launch(offset + i, stream) for i in range(n)]
-
-        run_warm = enqueue(args.warmup, 0) if args.warmup > 0 else (lambda: None)
-        run_timed = enqueue(args.steps, args.warmup)
-        with torch.cuda.stream(stream):
-            run_warm()
-        torch.cuda.synchronize()
-
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()  # barrier: one rank only
-        t0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            run_timed()
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
-
-        if args.calibrate_copy_mib:
-            n = args.calibrate_copy_mib << 18  # floats
-            a = torch.ones(n, device=dev)
-            b = torch.empty_like(a)
-            torch.cuda.synchronize()
-            b.copy_(a)
-            torch.cuda.synchronize()
-            del a, b
-
-        ms_per_step = wall * 1e3 / args.steps
-        digest = kernel_digest()
-        if w.name == "prefill" and not rollback:
-            metric_value = w.n_seqs * w.n_tokens * args.steps / wall
-            unit = "tokens/s"
-            achieved = w.flops() / kernel_s / 1e12
-            roofline = dict(bound="alu", achieved=achieved, peak=FP32_VECTOR_PEAK_TFLOPS,
-                            unit="TFLOP/s", frac=achieved / FP32_VECTOR_PEAK_TFLOPS)
-        else:
-            metric_value = alg_bytes * args.steps / wall / 1e9
-            unit = "GB/s"
-            achieved = alg_bytes / kernel_s / 1e9
-            roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
-                            frac=achieved / HBM_PEAK_GBPS)
-        roofline["traffic"] = (None if bf16 or args.normalize_k else
-                               traffic_from_profiles(args.workload, digest, kernel_name))
-        roofline["kernel"] = kernel_name
-        roofline["kernel_us"] = kernel_s * 1e6
-
-        line = {
-            "metric": METRIC,
-            "value": metric_value,
-            "unit": unit,
-            "n_gpus": 1,
-            "steps": args.steps,
-            "warmup": args.warmup,
-            "ms_per_step": ms_per_step,
-            "higher_is_better": True,
-            "scaling": "weak",
-            "vs_baseline": None,
-            "dtype": "f32" if not bf16 else "bf16 q/k/v/output, f32 state and arithmetic",
-            "data": "synthetic",
-            "config": {
-                "workload": description,
-                "d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads, "n_v_heads": w.n_v_heads,
-                "n_tokens": w.n_tokens, "n_seqs": w.n_seqs, "q_scale_bits": bits,
-                "capture": w.capture, "normalize_k": args.normalize_k,
-                "launch": args.launch, "resident_sets": layers,
-                "algorithmic_bytes_per_step": alg_bytes,
-                "flops_per_step": 0 if rollback else w.flops(),
-            },
-            "us_per_layer": ms_per_step * 1e3,
-            "state_gbps": w.state_bytes() / kernel_s / 1e9,
-            "roofline": roofline,
-            "kernel_digest": digest,
-        }
-        return line, w, bf16, rollback
-
-    line, w, bf16, rollback = measure(args)
-    if (args.workload == "decode" and not bf16 and not args.normalize_k
-            and not args.no_prefill):
-        # The metric's other half: prefill tokens/s at n_tokens = 512, measured
-        # the same way (resident inputs, graph replay, events on the stream).
-        pargs = argparse.Namespace(**vars(args))
-        pargs.workload, pargs.steps, pargs.warmup = "prefill", args.prefill_steps, 200
-        pargs.layers, pargs.calibrate_copy_mib = 0, 0
-        p, *_ = measure(pargs)
-        line["prefill"] = {
-            "metric": "prefill tokens/s at n_tokens=512", "value": p["value"],
-            "unit": p["unit"], "steps": p["steps"], "warmup": p["warmup"],
-            "ms_per_step": p["ms_per_step"], "workload": p["config"]["workload"],
-            "roofline": p["roofline"]}
-    if not args.no_cpu_baseline and not bf16 and not args.normalize_k:
-        line["cpu_baseline"] = (cpu_baseline_rollback(w, args.cpu_seconds) if rollback
-                                else cpu_baseline(w, args.cpu_seconds))
+    plain = args.io == "f32" and not args.normalize_k
+    m = measure(args.workload, steps=args.steps, warmup=args.warmup, launch=args.launch,
+                io=args.io, normalize_k=args.normalize_k, layers=args.layers,
+                calibrate_copy_mib=args.calibrate_copy_mib, digest=digest)
+    progress(m)
+    w = m["w"]
+    line = {
+        "metric": METRIC,
+        "value": m["value"],
+        "unit": m["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if not m["bf16"] else "bf16 q/k/v/output, f32 state and arithmetic",
+        "data": "synthetic",
+        "config": {
+            "workload": m["description"],
+            "d_k": w.d_k, "d_v": w.d_v, "n_k_heads": w.n_k_heads, "n_v_heads": w.n_v_heads,
+            "n_tokens": w.n_tokens, "n_seqs": w.n_seqs, "q_scale_bits": m["bits"],
+            "capture": w.capture, "normalize_k": args.normalize_k,
+            "launch": args.launch, "resident_sets": m["layers"],
+            "algorithmic_bytes_per_step": m["alg_bytes"],
+            "flops_per_step": 0 if m["rollback"] else w.flops(),
+        },
+        "us_per_layer": m["ms_per_step"] * 1e3,
+        "kernel_us": m["kernel_us"],
+        "event_us_per_step": m["event_us_per_step"],
+        "state_gbps": m["state_gbps"],
+        "roofline": m["roofline"],
+        "kernel_digest": digest,
+    }
+    extras = []
+    if args.workload == "decode" and plain and not args.no_extra:
+        # The metric's other workloads, measured the same way in the same process.
+        for name, steps, warmup in EXTRA:
+            extras.append(measure(name, steps=steps, warmup=warmup, launch=args.launch,
+                                  digest=digest))
+            progress(extras[-1])
+            torch.cuda.empty_cache()
+    # CPU baselines after all GPU work (they share nothing with it).
+    if not args.no_cpu_baseline and plain:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, rollback=m["rollback"])
+    for e in extras:
+        cpu = (None if args.no_cpu_baseline else
+               cpu_baseline(e["w"], args.cpu_seconds, rollback=e["rollback"]))
+        line[e["name"]] = extra_object(e, cpu)
     print(json.dumps(line), flush=True)
     return 0
 

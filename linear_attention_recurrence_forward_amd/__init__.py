@@ -13,7 +13,7 @@ _BINDING_NAMES = (
     "gdn_check_params", "gdn_forward", "gdn_forward_bf16", "gdn_forward_capture",
     "gdn_forward_ex", "gdn_rollback", "OPT_BF16_IO", "OPT_NORMALIZE_K",
     "gdn_status_string",
-    "library_path", "make_params", "params_for",
+    "library_path", "make_params", "params_for", "scale_bits",
 )
 
 __all__ = list(_BINDING_NAMES) + ["workloads"]

@@ -285,17 +285,34 @@ def gdn_rollback(state_capture, accepted, state, params: GdnParams, stream=None)
         raise GdnError(st, "gdn_rollback")
 
 
-def forward(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0, capture: bool = False,
-            normalize_k: bool = False, output=None, state_out=None, state_capture=None,
-            stream=None):
+def scale_bits(q_scale=None, q_scale_bits=None) -> int:
+    """Params word 8 from a q_scale value or its bits (at most one of them):
+    None for both means q is pre-scaled (bits 0). A value is stored as its
+    binary32 bits; +0.0 has bits 0, which the params block reads as "no
+    scale", so it is refused (mlx-native 0.21.1 src/ops/gated_delta_net_decode.rs,
+    module doc "Buffer / params contract")."""
+    if q_scale is not None and q_scale_bits is not None:
+        raise ValueError("pass q_scale or q_scale_bits, not both")
+    if q_scale is None:
+        return 0 if q_scale_bits is None else int(q_scale_bits) & 0xFFFFFFFF
+    bits = f32_bits(float(q_scale))
+    if bits == 0:
+        raise ValueError("q_scale=+0.0 cannot be expressed: bits 0 mean q is pre-scaled")
+    return bits
+
+
+def forward(q, k, v, g, beta, state_in, *, q_scale=None, q_scale_bits=None,
+            capture: bool = False, normalize_k: bool = False, output=None, state_out=None,
+            state_capture=None, stream=None):
     """Convenience wrapper on torch-shaped tensors:
     q, k (S, T, H_k, D_k); v (S, T, H_v, D_v); g, beta (S, T, H_v);
     state_in (S, H_v, D_v, D_k). q, k, v in f32, or all three in bf16 (then the
-    output is bf16 too; the state is f32 either way). normalize_k: use every
-    key row as k / sqrt(sum k^2 + 1e-6) (gdn_forward_ex). Allocates missing
-    outputs and returns (output, state_out) or (output, state_out,
-    state_capture)."""
-    params = params_for(q, v, q_scale_bits)
+    output is bf16 too; the state is f32 either way). q_scale (a float) or
+    q_scale_bits (its binary32 bits) folds a scale into every output; neither
+    means q is pre-scaled. normalize_k: use every key row as
+    k / sqrt(sum k^2 + 1e-6) (gdn_forward_ex). Allocates missing outputs and
+    returns (output, state_out) or (output, state_out, state_capture)."""
+    params = params_for(q, v, scale_bits(q_scale, q_scale_bits))
     S, T, Hv, Dv = v.shape
     Dk = q.shape[3]
     bf16 = q.dtype == torch.bfloat16

@@ -818,8 +818,11 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     // In a ring group that runs lazily, c is the product of the alphas of the
     // group's tokens 1 .. u (1 at u = 0) and b = beta / c. A group runs
     // eagerly (every token decays; c = 1, b = beta) if any of its c or
-    // beta / c would leave [2^-64, 2^64] or is not finite (strong decay or
-    // growth, special values), and always when the state is captured. The
+    // beta / c, or the alpha of its first token, would leave [2^-63, 2^63]
+    // or is not finite (strong decay or growth, special values), and always
+    // when the state is captured. A lazy group's first token decays by
+    // kappa * alpha (kappa: the previous group's last c, or 1), so both
+    // factors within [2^-63, 2^63] keep that product a normal number. The
     // raw g/beta of the next chunk are requested a chunk ahead into registers
     // that nothing else reads.
     float g_raw, b_raw;
@@ -842,8 +845,9 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
             c = i <= u ? c * ai : c;
           }
           const float bc = be / c;
-          const bool lazy_ok = c >= 0x1p-64f && c <= 0x1p64f &&
-                               __builtin_fabsf(bc) <= 0x1p64f;
+          const bool lazy_ok = c >= 0x1p-63f && c <= 0x1p63f &&
+                               __builtin_fabsf(bc) <= 0x1p63f &&
+                               (u != 0 || (al >= 0x1p-63f && al <= 0x1p63f));
           const uint64_t bad = __builtin_amdgcn_ballot_w64(!lazy_ok);
           eager_mask =
               (uint64_t)uniform((uint32_t)(bad >> 32)) << 32 | uniform((uint32_t)bad);
@@ -916,6 +920,16 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       // into a VGPR and back for every branch.
       const uint32_t eager =
           CAPTURE ? 1u : uniform((uint32_t)(eager_mask >> (t & 63u)) & ((1u << NB) - 1u));
+      if (!CAPTURE && eager != 0 && uniform(__builtin_bit_cast(uint32_t, kappa)) != 0x3F800000u) {
+        // An eager group after a lazy one: back to the plain state first, so
+        // that the first token's alpha (possibly extreme: that is one reason
+        // to run eagerly) is not multiplied into kappa.
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int m = 0; m < NV; ++m) st[r][m] *= kappa;
+        kappa = 1.f;
+      }
       park_vgroup(v_raw, vg);
       v_raw = load_vgroup(t + NB);
       if constexpr (GNORM) {

@@ -264,6 +264,18 @@ int oracle_gdn_forward_range_f32(const float *q, const float *k, const float *v,
                            state_out, state_capture, pair_begin, pair_end);
 }
 
+// The binary64 shadow over a range of pairs, as above.
+int oracle_gdn_forward_range_f64(const float *q, const float *k, const float *v,
+                                 const float *g, const float *beta,
+                                 const float *state_in,
+                                 const oracle_gdn_shape *p, int head_map,
+                                 uint64_t pair_begin, uint64_t pair_end,
+                                 double *output, double *state_out,
+                                 double *state_capture) {
+  return run<double, float>(q, k, v, g, beta, state_in, p, head_map, output,
+                            state_out, state_capture, pair_begin, pair_end);
+}
+
 // As the two above, with option bits: 2 = normalise every key row first
 // (normalized_keys). Other bits are an error (5).
 int oracle_gdn_forward_ex_f32(const float *q, const float *k, const float *v,

@@ -45,7 +45,7 @@ int oracle_gdn_forward_f64(const float *q, const float *k, const float *v,
                            int head_map, double *output, double *state_out,
                            double *state_capture);
 
-/* oracle_gdn_forward_f32 over the (sequence, value head) pairs
+/* oracle_gdn_forward_f32 (and _f64) over the (sequence, value head) pairs
  * [pair_begin, pair_end) only, numbered s * n_v_heads + vh (the end is clamped
  * to n_seqs * n_v_heads). Disjoint ranges may run concurrently on the same
  * arrays; together they write what one whole call writes, bit for bit. */
@@ -56,6 +56,14 @@ int oracle_gdn_forward_range_f32(const float *q, const float *k, const float *v,
                                  uint64_t pair_begin, uint64_t pair_end,
                                  float *output, float *state_out,
                                  float *state_capture);
+
+int oracle_gdn_forward_range_f64(const float *q, const float *k, const float *v,
+                                 const float *g, const float *beta,
+                                 const float *state_in,
+                                 const oracle_gdn_shape *p, int head_map,
+                                 uint64_t pair_begin, uint64_t pair_end,
+                                 double *output, double *state_out,
+                                 double *state_capture);
 
 /* bf16 q, k, v and output (raw 16-bit patterns); g, beta, state and capture
  * f32. Inputs widened exactly, f32 recurrence, output rounded to nearest-even

@@ -96,12 +96,15 @@ def _load(path: str | None = None):
                 lib.oracle_f32_to_bf16.argtypes = [ctypes.POINTER(ctypes.c_float), u16,
                                                    ctypes.c_uint64]
                 lib.oracle_f32_to_bf16.restype = None
-            if hasattr(lib, "oracle_gdn_forward_range_f32"):
-                fn = lib.oracle_gdn_forward_range_f32
-                fp = ctypes.POINTER(ctypes.c_float)
-                fn.argtypes = [fp] * 6 + [ctypes.POINTER(_Shape), ctypes.c_int,
-                                          ctypes.c_uint64, ctypes.c_uint64, fp, fp, fp]
-                fn.restype = ctypes.c_int
+            for name, real in (("oracle_gdn_forward_range_f32", ctypes.c_float),
+                               ("oracle_gdn_forward_range_f64", ctypes.c_double)):
+                if hasattr(lib, name):
+                    fn = getattr(lib, name)
+                    fp = ctypes.POINTER(ctypes.c_float)
+                    rp = ctypes.POINTER(real)
+                    fn.argtypes = [fp] * 6 + [ctypes.POINTER(_Shape), ctypes.c_int,
+                                              ctypes.c_uint64, ctypes.c_uint64, rp, rp, rp]
+                    fn.restype = ctypes.c_int
             if hasattr(lib, "oracle_gdn_rollback"):
                 fn = lib.oracle_gdn_rollback
                 fn.argtypes = [ctypes.POINTER(ctypes.c_float),
@@ -170,6 +173,19 @@ def reference(q, k, v, g, beta, state_in, *, q_scale_bits: int = 0,
     return (out, st, cap) if capture else (out, st)
 
 
+_pools: dict = {}
+
+
+def _pool(threads: int):
+    """A thread pool of the given size, kept for later calls (creating one per
+    call would cost more than a short oracle call)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with _lock:
+        if threads not in _pools:
+            _pools[threads] = ThreadPoolExecutor(max_workers=threads)
+        return _pools[threads]
+
+
 def _ranges(n: int, parts: int):
     """[begin, end) bounds of `parts` contiguous, nearly equal slices of n items."""
     parts = max(1, min(parts, n))
@@ -177,32 +193,33 @@ def _ranges(n: int, parts: int):
 
 
 def reference_threads(q, k, v, g, beta, state_in, *, threads: int, q_scale_bits: int = 0,
-                      head_map: int = HEAD_MAP_MOD, capture: bool = False):
-    """The f32 oracle with its independent (sequence, value head) pairs split
-    into `threads` contiguous ranges that run concurrently (each range is one
-    call of the same loop body; ctypes releases the GIL during a call). The
-    result is reference(...)'s bit for bit. Used to time the oracle on all of a
-    host's cores."""
-    from concurrent.futures import ThreadPoolExecutor
+                      head_map: int = HEAD_MAP_MOD, capture: bool = False,
+                      precision: str = "f32"):
+    """The oracle (or its f64 shadow) with its independent (sequence, value
+    head) pairs split into `threads` contiguous ranges that run concurrently
+    (each range is one call of the same loop body; ctypes releases the GIL
+    during a call). The result is reference(...)'s bit for bit. Used to time
+    the oracle on all of a host's cores, and to check large GPU cases."""
     q, k, v, g, beta, state_in = (_f32(a) for a in (q, k, v, g, beta, state_in))
     S, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     if k.shape != q.shape or v.shape[:2] != (S, T) or g.shape != (S, T, Hv) or \
             beta.shape != (S, T, Hv) or state_in.shape != (S, Hv, Dv, Dk):
         raise ValueError("inconsistent shapes (see reference)")
-    out = np.empty((S, T, Hv, Dv), np.float32)
-    st = np.empty((S, Hv, Dv, Dk), np.float32)
-    cap = np.empty((S, T, Hv, Dv, Dk), np.float32) if capture else None
+    real, dtype = {"f32": (ctypes.c_float, np.float32),
+                   "f64": (ctypes.c_double, np.float64)}[precision]
+    out = np.empty((S, T, Hv, Dv), dtype)
+    st = np.empty((S, Hv, Dv, Dk), dtype)
+    cap = np.empty((S, T, Hv, Dv, Dk), dtype) if capture else None
     shape = _Shape(Dk, Dv, Hk, Hv, T, S, q_scale_bits & 0xFFFFFFFF)
     fp = ctypes.c_float
-    fn = _load().oracle_gdn_forward_range_f32
+    fn = getattr(_load(), f"oracle_gdn_forward_range_{precision}")
     args = (_ptr(q, fp), _ptr(k, fp), _ptr(v, fp), _ptr(g, fp), _ptr(beta, fp),
             _ptr(state_in, fp), ctypes.byref(shape), head_map)
-    outs = (_ptr(out, fp), _ptr(st, fp), _ptr(cap, fp) if cap is not None else
-            ctypes.POINTER(fp)())
+    outs = (_ptr(out, real), _ptr(st, real), _ptr(cap, real) if cap is not None else
+            ctypes.POINTER(real)())
     ranges = _ranges(S * Hv, threads)
-    with ThreadPoolExecutor(max_workers=len(ranges)) as ex:
-        rcs = list(ex.map(lambda r: fn(*args, r[0], r[1], *outs), ranges))
+    rcs = list(_pool(len(ranges)).map(lambda r: fn(*args, r[0], r[1], *outs), ranges))
     if any(rcs):
         raise ValueError(f"oracle rejected the inputs (codes {rcs})")
     return (out, st, cap) if capture else (out, st)
@@ -211,7 +228,6 @@ def reference_threads(q, k, v, g, beta, state_in, *, threads: int, q_scale_bits:
 def rollback_threads(state_capture, accepted, state, *, threads: int):
     """rollback(...) with the sequences split into `threads` contiguous ranges
     copied concurrently; the same result bit for bit."""
-    from concurrent.futures import ThreadPoolExecutor
     cap = _f32(state_capture)
     S, T, Hv, Dv, Dk = cap.shape
     out = np.array(state, dtype=np.float32, copy=True, order="C")
@@ -227,8 +243,8 @@ def rollback_threads(state_capture, accepted, state, *, threads: int):
         return lib.oracle_gdn_rollback(_ptr(cap[s0:s1], ctypes.c_float),
                                        acc[s0:s1].ctypes.data_as(u32), ctypes.byref(shape),
                                        _ptr(out[s0:s1], ctypes.c_float))
-    with ThreadPoolExecutor(max_workers=max(1, min(threads, S))) as ex:
-        rcs = list(ex.map(part, _ranges(S, threads)))
+    ranges = _ranges(S, threads)
+    rcs = list(_pool(len(ranges)).map(part, ranges))
     if any(rcs):
         raise ValueError(f"oracle rejected the inputs (codes {rcs})")
     return out

@@ -259,3 +259,23 @@ def test_forward_ex_options(lib):
     # f32 rule (16-byte q) without the bf16 bit, 8-byte with it
     assert ex(_binding.OPT_NORMALIZE_K, q=8) == "GDN_ERR_MISALIGNED"
     assert ex(_binding.OPT_NORMALIZE_K | _binding.OPT_BF16_IO, k=4) == "GDN_ERR_MISALIGNED"
+
+
+def test_q_scale_value_or_bits():
+    """forward(q_scale=<float>) stores the value's binary32 bits in params word
+    8; q_scale_bits passes them as they are; neither means q is pre-scaled
+    (bits 0). +0.0 has bits 0, which read as "no scale", so it is refused;
+    -0.0 is a literal scale. The checks run before any tensor is touched."""
+    from linear_attention_recurrence_forward_amd import _binding as b
+    assert b.scale_bits() == 0
+    assert b.scale_bits(q_scale=1 / 128 ** 0.5) == 0x3DB504F3
+    assert b.scale_bits(q_scale_bits=0x3E3504F3) == 0x3E3504F3
+    assert b.scale_bits(q_scale=-0.0) == 0x80000000
+    with pytest.raises(ValueError, match="cannot be expressed"):
+        b.scale_bits(q_scale=0.0)
+    with pytest.raises(ValueError, match="not both"):
+        b.scale_bits(q_scale=0.5, q_scale_bits=0x3F000000)
+    torch = pytest.importorskip("torch")
+    z = torch.zeros(1, 1, 1, 32)
+    with pytest.raises(ValueError, match="cannot be expressed"):
+        b.forward(z, z, z, z[..., 0], z[..., 0], torch.zeros(1, 1, 32, 32), q_scale=0.0)

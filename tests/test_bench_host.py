@@ -177,3 +177,41 @@ def test_summarize_valu_counters(bench, tmp_path):
     assert "11.00 GFLOP per call" in text
     for cmd in bench.VALU_PASSES:
         assert cmd in text
+
+
+def test_stale_build_is_refused(bench, monkeypatch, tmp_path):
+    """The bench times the library it loads: when the build stamp next to
+    libgdn.so differs from the current sources (or is missing) it exits with
+    status 3 before touching the GPU; a matching stamp is returned as the
+    digest the line reports."""
+    from linear_attention_recurrence_forward_amd import build
+    monkeypatch.setattr(build, "LIBDIR", str(tmp_path))
+    monkeypatch.setattr(build, "source_digest", lambda: "current-sources")
+    with pytest.raises(SystemExit) as e:
+        bench.check_build()  # no stamp at all
+    assert e.value.code == 3
+    (tmp_path / "libgdn.digest").write_text("older-sources\n")
+    with pytest.raises(SystemExit) as e:
+        bench.check_build()
+    assert e.value.code == 3
+    (tmp_path / "libgdn.digest").write_text("current-sources\n")
+    assert bench.check_build() == "current-sources"
+
+
+def test_host_cpu(bench):
+    cpu = bench.host_cpu()
+    assert cpu["nproc"] >= 1 and 1 <= cpu["threads"] <= bench.MAX_WORKER_THREADS
+    assert cpu["threads"] <= cpu["usable"] and isinstance(cpu["model"], str)
+
+
+def test_cpu_baseline_fields(bench):
+    """Every CPU baseline names the CPU and carries a one-core and an all-core
+    rate of the oracle in the workload's unit."""
+    w = WORKLOADS["tiny"]
+    cpu = bench.cpu_baseline(w, 0.2)
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s"
+    assert cpu["single_core"]["cores"] == 1 and cpu["single_core"]["value"] > 0
+    assert cpu["value"] > 0 and cpu["cores"] == min(bench.host_cpu()["threads"], 2)
+    assert cpu["cpu_model"] and cpu["nproc"] >= 1
+    rb = bench.cpu_baseline(WORKLOADS["spec_verify"].with_(n_seqs=2), 0.2, rollback=True)
+    assert rb["unit"] == "GB/s" and rb["single_core"]["value"] > 0

@@ -25,6 +25,37 @@ pytestmark = pytest.mark.gpu
 
 RTOL, ATOL = 1e-4, 1e-5
 NAMES = ("q", "k", "v", "g", "beta", "state_in")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Parity margins of the runs below: max |gpu - ref| / (ATOL + RTOL |ref|) per
+# case and array (below 1 passes), written to a JSON file when the module ends
+# ($GDN_PARITY_MARGINS, else gpurun_out/parity_margins.json under the repo).
+MARGINS: dict = {}
+
+
+def tol_used(a, e):
+    """Fraction of the tolerance used: max |a - e| / (ATOL + RTOL |e|)."""
+    e = np.asarray(e, np.float64)
+    return float(np.max(np.abs(np.asarray(a, np.float64) - e) / (ATOL + RTOL * np.abs(e))))
+
+
+def record(case, what, **margins):
+    MARGINS.setdefault(case, {})[what] = margins
+
+
+@pytest.fixture(scope="module", autouse=True)
+def margins_file():
+    yield
+    if not MARGINS:
+        return
+    path = os.environ.get("GDN_PARITY_MARGINS") or os.path.join(
+        ROOT, "gpurun_out", "parity_margins.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    import json
+    with open(path, "w") as f:
+        json.dump({"tolerance": {"rtol": RTOL, "atol": ATOL},
+                   "margin": "max |gpu - ref| / (atol + rtol |ref|)", "cases": MARGINS},
+                  f, indent=1, sort_keys=True)
 
 
 @pytest.fixture(autouse=True)
@@ -67,11 +98,6 @@ def close(gpu, expected, what):
                   what)
 
 
-def max_rel(a, e):
-    e = np.asarray(e, np.float64)
-    return float(np.max(np.abs(a - e) / (ATOL / RTOL + np.abs(e))))
-
-
 # ------------------------------------------------------------------ native
 
 def test_native_library_is_loaded():
@@ -95,10 +121,10 @@ def test_workload_parity(name):
     exp = ref(x, capture=w.capture)
     shadow = ref(x, capture=w.capture, precision="f64")
     for g_, e, s, what in zip(got, exp, shadow, ("output", "state_out", "capture")):
+        record(name, what, gpu_vs_oracle=tol_used(g_, e), gpu_vs_f64=tol_used(g_, s),
+               oracle_vs_f64=tol_used(e, s))
         close(g_, e, f"{name} {what} vs oracle")
         close(g_, s, f"{name} {what} vs f64 shadow")
-        sys.__stderr__.write(f"  {name} {what}: max scaled err vs oracle "
-                             f"{max_rel(g_, e):.2e}, vs f64 {max_rel(g_, s):.2e}\n")
     if w.capture:
         assert_equal(got[2][:, -1], got[1], f"{name} capture[T-1] == state_out")
 
@@ -149,6 +175,12 @@ SHAPES = [
     (128, 128, 2, 4, 8, 1),
     (128, 40, 1, 2, 72, 2),
     (64, 64, 1, 2, 68, 1),
+    # multi-token D_k = 128 grids of 256 two-row workgroups or more (the
+    # paired kernel the prefill takes): nonzero state, partial row blocks,
+    # tokens left after the last ring group, 64-token chunk boundaries
+    (128, 72, 8, 96, 13, 1),
+    (128, 40, 4, 64, 70, 2),
+    (128, 128, 16, 64, 3, 1),
 ]
 
 
@@ -250,13 +282,23 @@ def test_decay_extremes():
                  "zero state, beta = 0: zero outputs through the growth tokens")
 
 
-def test_long_run_drift():
+@pytest.mark.parametrize("shape", [(128, 128, 2, 4, 2048, 1), (128, 32, 2, 256, 2048, 1)],
+                         ids=["one_row_kernel", "two_row_kernel"])
+def test_long_run_drift(shape):
     """A long run (T = 2048) stays within tolerance of the oracle and the f64
-    shadow: no drift from the exp or the reduction order."""
-    w = Workload("long", 0, 128, 128, 2, 4, 2048, 1, fold_q_scale=True, g_high=0.5)
+    shadow: no drift from the exp, the lazy decay's reassociation or the
+    reduction order; on the one-row and the two-row (256 workgroups)
+    D_k = 128 multi-token kernels."""
+    w = Workload("long", 0, *shape, fold_q_scale=True, g_high=0.5)
     x = make_inputs(w, seed=5)
     got = run(x)
-    for e, what in ((ref(x), "oracle"), (ref(x, precision="f64"), "f64 shadow")):
+    kw = dict(q_scale_bits=x["q_scale_bits"], threads=16)
+    args = {n: x[n] for n in NAMES}
+    for e, what in ((oracle.reference_threads(**args, **kw), "oracle"),
+                    (oracle.reference_threads(**args, **kw, precision="f64"), "f64 shadow")):
+        for g_, e_, arr in zip(got, e, ("output", "state_out")):
+            MARGINS.setdefault(f"drift_T2048_{shape[1]}x{shape[3]}", {}).setdefault(
+                arr, {})[f"gpu_vs_{'oracle' if what == 'oracle' else 'f64'}"] = tol_used(g_, e_)
         close(got[0], e[0], f"long-run output vs {what}")
         close(got[1], e[1], f"long-run state vs {what}")
 
@@ -570,6 +612,10 @@ NORM_SHAPES = [
     # lane) and a call of exactly 16 tokens
     (32, 24, 1, 2, 40, 1),
     (128, 32, 1, 2, 16, 1),
+    # the two-row D_k = 128 multi-token kernel, per-token and group-ahead
+    # factors
+    (128, 40, 4, 64, 13, 2),
+    (128, 72, 8, 96, 20, 1),
 ]
 
 
@@ -725,3 +771,206 @@ def test_errors_on_device_tensors():
         gdn.gdn_forward(*(d[n] for n in NAMES), out, st, bad)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+# ------------------------------------------------------------------ special values
+
+def close_special(gpu, expected, what):
+    """NaN-aware parity: NaN where the oracle has NaN, the same infinity where
+    it has one, and every finite element within tolerance."""
+    g_, e = np.asarray(gpu), np.asarray(expected)
+    nan_g, nan_e = np.isnan(g_), np.isnan(e)
+    assert np.array_equal(nan_g, nan_e), (
+        f"{what}: NaN positions differ ({int(nan_g.sum())} on the GPU, {int(nan_e.sum())} "
+        f"in the oracle, {int((nan_g != nan_e).sum())} mismatched)")
+    inf_e = np.isinf(e)
+    assert np.array_equal(np.isinf(g_), inf_e), f"{what}: infinite positions differ"
+    assert np.array_equal(g_[inf_e], e[inf_e]), f"{what}: infinities of another sign"
+    fin = np.isfinite(e)
+    close(g_[fin], e[fin], f"{what} (finite elements)")
+
+
+SPECIAL_SHAPES = [
+    # d_k, d_v, n_k, n_v, T, S: one-token and multi-token geometries, one row
+    # per lane (small grids) and two (256 workgroups or more), all D_k
+    (128, 72, 2, 8, 1, 2),
+    (128, 96, 8, 96, 1, 1),
+    (128, 72, 2, 8, 40, 2),
+    (128, 96, 8, 96, 40, 1),
+    (64, 40, 2, 8, 40, 2),
+    (32, 24, 1, 4, 40, 3),
+]
+
+
+def plant_specials(x, seed):
+    """NaN and +-inf in v, g, beta and the state, each on its own (sequence,
+    value head), and beta outside (0, 1) on a quarter of the tokens of the
+    other heads. Returns the modified inputs and the heads left finite."""
+    rng = np.random.default_rng(seed)
+    v, g, beta, st = (x[n].copy() for n in ("v", "g", "beta", "state_in"))
+    S, T, Hv, Dv = v.shape
+    Dk = st.shape[-1]
+    heads = [(s_, h) for s_ in range(S) for h in range(Hv)]
+    pick = [heads[i] for i in rng.permutation(len(heads))]
+    tok = lambda: int(rng.integers(0, T))  # noqa: E731
+    row = lambda: int(rng.integers(0, Dv))  # noqa: E731
+    col = lambda: int(rng.integers(0, Dk))  # noqa: E731
+    for (a, b), val in zip(pick[0:3], (np.nan, np.inf, -np.inf)):
+        v[a, tok(), b, row()] = val
+    for (a, b), val in zip(pick[3:6], (np.nan, -np.inf, np.inf)):  # alpha NaN, +inf, 0
+        g[a, tok(), b] = val
+    for (a, b), val in zip(pick[6:8], (np.nan, np.inf)):
+        beta[a, tok(), b] = val
+    for (a, b), val in zip(pick[8:11], (np.nan, np.inf, -np.inf)):
+        st[a, b, row(), col()] = val
+    rest = pick[11:]
+    for a, b in rest:
+        sel = rng.random(T) < 0.25
+        beta[a, sel, b] = rng.choice([-1.0, -0.5, 1.5, 2.0, 3.0], size=int(sel.sum()))
+    return dict(x, v=v, g=g, beta=beta, state_in=st), rest
+
+
+@pytest.mark.parametrize("capture", [False, True], ids=["plain", "capture"])
+@pytest.mark.parametrize("shape", SPECIAL_SHAPES, ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
+def test_special_values(shape, capture):
+    """No clamps anywhere: NaN and infinities in v, g, beta and the state
+    propagate as in the oracle's IEEE arithmetic, beta outside (0, 1) is an
+    ordinary value. The lazy decay of multi-token calls falls back to the
+    written order for such groups."""
+    dk, dv, hk, hv, t, s_ = shape
+    w = Workload("special", 0, dk, dv, hk, hv, t, s_)
+    x, rest = plant_specials(make_inputs(w, seed=50 + t), seed=51 + t + dk)
+    for bits in (0, q_scale_bits_for(dk)):
+        got = run(x, q_scale_bits=bits, capture=capture)
+        exp = ref(x, q_scale_bits=bits, capture=capture)
+        for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
+            close_special(g_, e, f"{shape} bits={bits:#x} {what}")
+        assert np.isnan(exp[1]).any() and np.isfinite(exp[1]).mean() > 0.5
+        # the heads without planted values stay finite
+        for a, b in rest:
+            assert np.all(np.isfinite(got[0][a, :, b])), f"head {(a, b)} output finite"
+        if capture:
+            assert np.array_equal(got[2][:, -1].view(np.uint32), got[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(128, 64, 2, 4, 24, 1), (128, 72, 8, 96, 24, 1),
+                                   (64, 40, 2, 4, 24, 1), (32, 24, 1, 4, 24, 1)],
+                         ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
+def test_lazy_decay_extreme_products(shape):
+    """Strong growth, then decay, across ring-group boundaries: a group whose
+    running decay product ends near 2^60 followed by a token with alpha ~
+    2^70 (and the mirror case, ~2^-60 followed by alpha ~ 2^-87), on states
+    scaled so that the true results stay normal numbers. The product of the
+    two factors leaves the binary32 range; the result must not."""
+    dk, dv, hk, hv, t, s_ = shape
+    w = Workload("kappa", 0, dk, dv, hk, hv, t, s_)
+    x = make_inputs(w, seed=61)
+    g, beta, st = x["g"].copy(), x["beta"].copy(), x["state_in"].copy()
+    nb = 8 if dk >= 64 else 4  # ring group of the multi-token kernel
+    # value head 1: growth, then a huge alpha on the next group's first token
+    beta[0, :, 1] = 0.0
+    st[0, 1] *= np.float32(1e-20)
+    g[0, 1:nb, 1] = -59.6 / (nb - 1) * np.log(2.0)
+    g[0, nb, 1] = -70.0 * np.log(2.0)
+    # value head 2: decay, then a tiny alpha on the next group's first token
+    beta[0, :, 2] = 0.0
+    st[0, 2] *= np.float32(1e20)
+    g[0, 1:nb, 2] = 59.6 / (nb - 1) * np.log(2.0)
+    g[0, nb, 2] = 87.0 * np.log(2.0)
+    x = dict(x, g=g.astype(np.float32), beta=beta, state_in=st)
+    got = run(x)
+    exp = ref(x)
+    shadow = ref(x, precision="f64")
+    for g_, e, what in zip(got, exp, ("output", "state_out")):
+        assert np.all(np.isfinite(e)), f"{what}: the oracle stays finite"
+        assert np.all(np.isfinite(g_)), f"{what}: the GPU stays finite"
+    # The outputs of heads 1 and 2 span ~2^-95 to ~2^60, where a dot product's
+    # rounding is relative to the size of its terms rather than of its sum:
+    # each output is held to the tolerance relative to the largest output of
+    # its (token, head) as well as to itself. A product that overflowed or
+    # underflowed fails by far.
+    for e, what in ((exp, "oracle"), (shadow, "f64 shadow")):
+        out = e[0].astype(np.float64)
+        scale = np.max(np.abs(out), axis=-1, keepdims=True)
+        assert np.all(scale > 0)
+        assert_within(got[0], out, ATOL + RTOL * (scale + np.abs(out)),
+                      f"{shape} output vs {what}")
+        close(got[1], e[1], f"{shape} state_out vs {what}")
+    # Value head 2's state ends near 2^-95, far below the absolute tolerance:
+    # relative agreement there.
+    st2 = exp[1][0, 2].astype(np.float64)
+    assert np.all(np.abs(st2) > 0)
+    assert_within(got[1][0, 2], st2, RTOL * np.abs(st2), f"{shape} head 2 state_out")
+
+
+# ------------------------------------------------------------------ addresses
+
+def test_addresses_with_bit31_of_the_low_word_set():
+    """Every array at an address whose low 32 bits have bit 31 set (views into
+    one allocation of 4 GiB + 128 MiB): wave-uniform pointers are rebuilt from
+    two 32-bit halves in the kernels, and a sign-extended low half would
+    corrupt the high word exactly there. One-token, multi-token (both D_k =
+    128 kernels, with capture) and rollback calls against the oracle."""
+    buf = torch.empty((1 << 32) + (128 << 20), dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr()
+    cursor = [((1 << 31) - (base & 0xFFFFFFFF)) % (1 << 32)]
+
+    def carve(shape, dtype=torch.float32):
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        off = (cursor[0] + 255) & ~255
+        cursor[0] = off + n
+        t = buf[off:off + n].view(dtype).view(shape)
+        lo = t.data_ptr() & 0xFFFFFFFF
+        assert lo >= 1 << 31 and lo + n <= 1 << 32, hex(t.data_ptr())
+        return t
+
+    for shape in ((128, 72, 2, 8, 1, 2), (128, 96, 8, 96, 1, 1), (128, 72, 2, 4, 13, 2),
+                  (128, 72, 8, 96, 13, 1)):
+        cursor[0] = ((1 << 31) - (base & 0xFFFFFFFF)) % (1 << 32)
+        dk, dv, hk, hv, t, s_ = shape
+        x = make_inputs(Workload("addr", 0, dk, dv, hk, hv, t, s_, fold_q_scale=True),
+                        seed=71 + t)
+        d = {}
+        for n in NAMES:
+            d[n] = carve(x[n].shape)
+            d[n].copy_(torch.from_numpy(x[n]))
+        out = carve(x["v"].shape)
+        st = carve(x["state_in"].shape)
+        cap = carve((s_, t, hv, dv, dk))
+        gdn.forward(*(d[n] for n in NAMES), q_scale_bits=x["q_scale_bits"], capture=True,
+                    output=out, state_out=st, state_capture=cap)
+        torch.cuda.synchronize()
+        exp = ref(x, capture=True)
+        for g_, e, what in zip((out, st, cap), exp, ("output", "state_out", "capture")):
+            close(g_.cpu().numpy(), e, f"{shape} high addresses {what}")
+        o2, s2 = carve(x["v"].shape), carve(x["state_in"].shape)
+        gdn.forward(*(d[n] for n in NAMES), q_scale_bits=x["q_scale_bits"], output=o2,
+                    state_out=s2)
+        torch.cuda.synchronize()
+        close(o2.cpu().numpy(), exp[0], f"{shape} high addresses output, no capture")
+        close(s2.cpu().numpy(), exp[1], f"{shape} high addresses state, no capture")
+        acc = carve((s_,), torch.int32)
+        acc_np = (np.arange(s_) % t).astype(np.int32)
+        acc.copy_(torch.from_numpy(acc_np))
+        slot = carve(x["state_in"].shape)
+        slot.fill_(5.0)
+        gdn.gdn_rollback(cap, acc, slot, gdn.params_for(d["q"], d["v"]))
+        torch.cuda.synchronize()
+        want = oracle.rollback(cap.cpu().numpy(), acc_np.astype(np.uint32),
+                               np.full(x["state_in"].shape, 5.0, np.float32))
+        assert np.array_equal(slot.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    del buf
+    torch.cuda.empty_cache()
+
+
+def test_q_scale_value():
+    """forward(q_scale=<float>) equals forward(q_scale_bits=<its bits>) bit for
+    bit."""
+    w = WORKLOADS["decode"].with_(n_tokens=3)
+    x = make_inputs(w, seed=81)
+    d = dev(x)
+    a = gdn.forward(*(d[n] for n in NAMES), q_scale=0.25)
+    b = gdn.forward(*(d[n] for n in NAMES), q_scale_bits=f32_bits(0.25))
+    torch.cuda.synchronize()
+    for u, v_ in zip(a, b):
+        assert torch.equal(u, v_)

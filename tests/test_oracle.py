@@ -77,6 +77,11 @@ def test_threaded_oracle_is_bit_identical(threads):
                                        capture=capture, threads=threads)
         for a, b in zip(one, par):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    one = oracle.reference(**{n: x[n] for n in names}, precision="f64")
+    par = oracle.reference_threads(**{n: x[n] for n in names}, precision="f64",
+                                   threads=threads)
+    for a, b in zip(one, par):
+        assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
     _, _, cap = oracle.reference(**{n: x[n] for n in names}, capture=True)
     acc = np.array([0, w.n_tokens, 2], np.uint32)
     base = np.full(x["state_in"].shape, 3.0, np.float32)
