@@ -464,9 +464,13 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
   // token's instruction stream.
   constexpr bool DEFER = PAIRED;
   static_assert(!DEFER || NB % TB == 0, "ring groups hold whole output batches");
-  float yp[DEFER ? TB : 1];
+  // yp keeps the lane's A-row partial and yq its B-row partial of each token
+  // slot; the flush pairs them (a + partner's b), so the pairing adds of a
+  // batch are independent of each other instead of one per token on that
+  // token's dependent chain.
+  float yp[DEFER ? TB : 1], yq[DEFER ? TB : 1];
 #pragma unroll
-  for (uint32_t j = 0; j < (DEFER ? TB : 1); ++j) yp[j] = 0.f;
+  for (uint32_t j = 0; j < (DEFER ? TB : 1); ++j) yp[j] = yq[j] = 0.f;
   float yk[NY];
   uint32_t yoff[NY];  // lane's output address: row r of token t0 + slot_t
 #pragma unroll
@@ -544,11 +548,14 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
   kq_ext = a.kq_ext0;
   v_ext = a.v_ext0;
 
-  auto load_token = [&](uint32_t t, Tok &x) {
-    const uint32_t kq_off = uniform((t - base_t) * kq_bytes);
+  // Token rows at byte offset kq_off from base_t's row.
+  auto load_token_at = [&](uint32_t kq_off, Tok &x) {
     const rsrc_t k_rs = buffer(k_b, kq_ext), q_rs = buffer(q_b, kq_ext);
     x.kr = Raw<RB>::load(k_rs, slane * RB, kq_off);
     x.qr = Raw<RB>::load(q_rs, slane * RB, kq_off);
+  };
+  auto load_token = [&](uint32_t t, Tok &x) {
+    load_token_at(uniform((t - base_t) * kq_bytes), x);
   };
 
   // Multi-token calls read v once per ring group: the wave's ROWS_PER_WAVE
@@ -688,14 +695,14 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
   // last token (in a ring group only the last token can be, and it then ends
   // an output batch anyway).
   auto step = [&](uint32_t t, uint32_t j, bool may_end, const KQ &kq, const float (&v)[NY],
-                  uint32_t decay, float alpha, float b, float c) {
+                  uint32_t decay, float alpha, float b, float c, bool raise) {
     // The sk chain (decay, dot products, butterfly, delta) is what the rest
     // of the token, and the next token, wait for; the rank-1 write and y are
     // throughput work the other waves of the SIMD can interleave with. The
     // wave's issue priority is raised for the chain and dropped after delta
     // (512-token prefill 183.5 -> 178.5 us; dropping it after the write
-    // instead: 185.4 us).
-    __builtin_amdgcn_s_setprio(1);
+    // instead: 185.4 us). raise: not raised yet by the caller.
+    if (raise) __builtin_amdgcn_s_setprio(1);
     // Normalised keys (NK): sk = c * inv * (cells . k) and the write adds
     // delta * inv along the raw k, the same as using k * inv throughout.
     float cs = c, bs = b;
@@ -759,10 +766,13 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       // from sinking the token's dot product there, which would hold every
       // token's cells live until the end of the batch. The partial is kept
       // without the token's c: the flush applies c once to the lane's sum.
-      float y = pair_part<L>(part[0], part[1]);
-      asm volatile("" : "+v"(y));
+      float ya = part[0], yb = part[1];
+      asm volatile("" : "+v"(ya), "+v"(yb));
 #pragma unroll
-      for (uint32_t i = 0; i < TB; ++i) yp[i] = i == j ? y : yp[i];
+      for (uint32_t i = 0; i < TB; ++i) {
+        yp[i] = i == j ? ya : yp[i];
+        yq[i] = i == j ? yb : yq[i];
+      }
     } else if constexpr (PAIRED) {
       const float y = c * pair_sum<L>(part[0], part[1]);
       yk[0] = mine ? y : yk[0];
@@ -788,7 +798,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       if constexpr (DEFER) {
         float w[TB];
 #pragma unroll
-        for (uint32_t i = 0; i < TB; ++i) w[i] = yp[i];
+        for (uint32_t i = 0; i < TB; ++i) w[i] = pair_part<L>(yp[i], yq[i]);
         scatter_sum<TB / 2>(w, slot_t);
         // Token t0 + slot_t's c: from the factor table in a ring group (1
         // when the group ran eagerly); tokens after the last whole group run
@@ -863,7 +873,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     auto run = [&](uint32_t t, uint32_t j, const KQ &kq, const float (&v)[NY]) {
       next_chunk(t);
       const float4 f = ab[t & 63u];
-      step(t, j, true, kq, v, true, f.x, f.w, 1.f);
+      step(t, j, true, kq, v, true, f.x, f.w, 1.f, true);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -936,6 +946,15 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         read_krow(invg);
         load_krow(t + NB, 0, kn);
       }
+      // The group's prefetch requests (tokens t + NB - 1 .. t + 2 NB - 2),
+      // each clamped to the last token, at byte offsets from base_t's row: a
+      // running offset and one minimum per token. Requests reach at most
+      // 63 + 2 NB - 2 tokens past base_t, so clamping the last token's
+      // distance to 96 changes no request and keeps the products below 2^32
+      // (the host bounds the row stride below 2^25 bytes).
+      const uint32_t last_rel = T - 1 - base_t;
+      const uint32_t kq_last = uniform((last_rel < 96u ? last_rel : 96u) * kq_bytes);
+      uint32_t kq_next = uniform((t + NB - 1 - base_t) * kq_bytes);
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         float vu[NY];
@@ -953,15 +972,15 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         // the prefetch request and the next token's staging are issued
         // ahead of the other waves' throughput work (-1%).
         __builtin_amdgcn_s_setprio(1);
-        const uint32_t ahead = t + NB - 1;
-        load_token(ahead < T ? ahead : T - 1, buf[(u + NB - 1) % NB]);
+        load_token_at(kq_next < kq_last ? kq_next : kq_last, buf[(u + NB - 1) % NB]);
+        kq_next += kq_bytes;
         // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
         // last token when t is the last one.
         const KQ nxt = columns(buf[AHEAD ? (u + 1) % NB : u]);
         KQ cur = AHEAD ? kq : nxt;
         if constexpr (GNORM) cur.inv = invg[u];
         step(t, u % TB, false, cur, vu, u == 0 ? 1u : eager,
-             u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z);
+             u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z, false);
         kq = nxt;
         ++t;
       }
