@@ -143,7 +143,12 @@ def traffic_from_profiles(workload: str, digest: str, kernel: str = KERNEL_NAME,
 
 
 def _csv(path):
+    """Rows of a CSV file (or of its gzip-compressed copy path + '.gz')."""
     import csv
+    import gzip
+    if not os.path.exists(path) and os.path.exists(path + ".gz"):
+        with gzip.open(path + ".gz", "rt") as f:
+            return list(csv.DictReader(f))
     with open(path) as f:
         return list(csv.DictReader(f))
 
@@ -187,7 +192,7 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict,
     # under the profiler, which pull the average up).
     durations = {}
     trace = os.path.join(src, f"kt_{workload}", "run_kernel_trace.csv")
-    if os.path.exists(trace):
+    if os.path.exists(trace) or os.path.exists(trace + ".gz"):
         for r in _csv(trace):
             durations.setdefault(r["Kernel_Name"], []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -242,6 +247,51 @@ def summarize_rocprof(src: str, workload: str, calib_mib: int, commands: dict,
     with open(os.path.join(out_dir, f"{kernel}_{workload}_hbm_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     return md
+
+
+def summarize_default_trace(src: str, command: str, out_dir: str | None = None) -> str:
+    """Kernel-trace summary of the default bench command (every workload of
+    the headline line in one process) from rocprofv3 CSV output in
+    src/kt_default, next to the per-launch kernel times the same run's bench
+    line reports (those are event timings under the profiler, which
+    serialises dispatches, so they are not the unprofiled figures)."""
+    stats = _csv(os.path.join(src, "kt_default", "run_kernel_stats.csv"))
+    durations = {}
+    for r in _csv(os.path.join(src, "kt_default", "run_kernel_trace.csv")):
+        durations.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    line = None
+    with open(os.path.join(src, "kt_default.log")) as f:
+        for ln in f:
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    lines = ["# All kernels of the default bench line (decode, prefill, batched decode, "
+             "spec verify, rollback)", "",
+             f"kernel digest (sha256 of sources + flags) of the profiled build: "
+             f"`{line['kernel_digest']}`", "", "```", command, "```", "",
+             "| kernel | calls | average µs | median µs | min µs | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        d = sorted(durations.get(r["Name"], []))
+        med = f"{(d[(len(d) - 1) // 2] + d[len(d) // 2]) / 2:.2f}" if d else "—"
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {med} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    lines += ["", "Per-launch kernel time reported by the same (profiled) run's bench line:", "",
+              "| workload | kernel_us under the profiler |", "|---|---|",
+              f"| decode | {line['kernel_us']:.3f} |"]
+    for k in ("prefill", "batched_decode", "spec_verify", "rollback"):
+        if k in line:
+            lines.append(f"| {k} | {line[k]['kernel_us']:.3f} |")
+    lines.append("")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, "all_kernels_default_bench_line.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
 
 
 def host_cpu() -> dict:
@@ -638,6 +688,11 @@ def main(argv=None):
                 print(summarize_rocprof(args.summarize_rocprof, wl, 1024, dict(
                     kt=cmd.format(w=wl), fetch=pmc.format(c="FETCH_SIZE", w=wl),
                     write=pmc.format(c="WRITE_SIZE", w=wl))))
+        if os.path.isdir(os.path.join(args.summarize_rocprof, "kt_default")):
+            print(summarize_default_trace(
+                args.summarize_rocprof,
+                "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt_default -o run "
+                "-- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline"))
         return 0
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "

@@ -215,3 +215,27 @@ def test_cpu_baseline_fields(bench):
     assert cpu["cpu_model"] and cpu["nproc"] >= 1
     rb = bench.cpu_baseline(WORKLOADS["spec_verify"].with_(n_seqs=2), 0.2, rollback=True)
     assert rb["unit"] == "GB/s" and rb["single_core"]["value"] > 0
+
+
+def test_summarize_default_trace(bench, tmp_path):
+    """The default bench line's kernel trace: per-kernel statistics, the
+    profiled build's digest and the bench line's kernel times, read from a
+    gzip-compressed trace."""
+    import gzip
+    src, out = tmp_path / "prof", tmp_path / "profiles"
+    write_csv(str(src / "kt_default" / "run_kernel_stats.csv"),
+              ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+              [["void gdn::gdn_decode<128>", 3, 3000.0, 2000.0, 4000.0, 60.0]])
+    rows = [["void gdn::gdn_decode<128>", 0, d] for d in (2000, 3000, 4000)]
+    with gzip.open(src / "kt_default" / "run_kernel_trace.csv.gz", "wt") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for r in rows:
+            f.write(",".join(f'"{v}"' for v in r) + "\n")
+    line = {"kernel_digest": "cafe", "kernel_us": 2.8,
+            "prefill": {"kernel_us": 180.0}, "rollback": {"kernel_us": 2.9}}
+    with open(src / "kt_default.log", "w") as f:
+        f.write("bench: progress\n" + json.dumps(line) + "\n")
+    text = open(bench.summarize_default_trace(str(src), "the-command", str(out))).read()
+    assert "`cafe`" in text and "the-command" in text
+    assert "| 3 | 3.00 | 3.00 | 2.00 | 60.0 |" in text
+    assert "| decode | 2.800 |" in text and "| prefill | 180.000 |" in text
