@@ -552,10 +552,11 @@ def measure(name: str, *, steps: int, warmup: int, launch: str = "graph", io: st
             return graph.replay
         return lambda: [launch_one(offset + i) for i in range(n)]
 
-    def events(run):
-        """Seconds between HIP events recorded on the launch stream around run()."""
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
+    def events(run, ev0=None, ev1=None):
+        """Seconds between HIP events recorded on the launch stream around run()
+        (events created here unless given)."""
+        ev0 = ev0 or torch.cuda.Event(enable_timing=True)
+        ev1 = ev1 or torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
             ev0.record(stream)
             run()
@@ -570,9 +571,10 @@ def measure(name: str, *, steps: int, warmup: int, launch: str = "graph", io: st
     torch.cuda.synchronize()
 
     # The timed region: exactly `steps` steps, synchronised on both sides.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()  # barrier: one rank only
     t0 = time.perf_counter()
-    event_s = events(run_timed)
+    event_s = events(run_timed, ev0, ev1)
     wall = time.perf_counter() - t0
 
     # Per-launch kernel duration: graph replays of 2K and K steps, differenced.
