@@ -26,7 +26,9 @@ cost cancels, and the figure does not depend on K.
 Prints one JSON line. The single-layer decode line (the default) also carries
 one object per other workload of the headline metric: "prefill" (512-token
 prefill, tokens/s), "batched_decode", "spec_verify" and "rollback", each with
-its own roofline and CPU baseline (--no-extra leaves them out). Every CPU
+its own roofline and CPU baseline, and "state_copy", the library's copy kernel
+moving exactly the decode call's state bytes, measured the same way: the floor
+beside the decode figure (--no-extra leaves them out). Every CPU
 baseline times the oracle on one core and on all the host's cores (threads
 over the independent (sequence, value head) pairs) and names the CPU.
 """
@@ -60,7 +62,7 @@ NAMES = ("q", "k", "v", "g", "beta", "state_in")
 # timed region covers tens of milliseconds of GPU work whatever --steps is
 # (the 512-token prefill needs a longer warm-up to reach its loaded clock).
 EXTRA = (("prefill", 500, 200), ("batched_decode", 500, 50), ("spec_verify", 2000, 200),
-         ("rollback", 2000, 200))
+         ("rollback", 2000, 200), ("state_copy", 2000, 200))
 MAX_WORKER_THREADS = 16  # the host CPU share of one GPU on the GPU machines
 
 
@@ -70,9 +72,11 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["rollback"],
+    ap.add_argument("--workload", default="decode",
+                    choices=sorted(WORKLOADS) + ["rollback", "state_copy"],
                     help="forward workload, or 'rollback': accepted-prefix rollback "
-                         "on the spec_verify shape")
+                         "on the spec_verify shape, or 'state_copy': the rollback "
+                         "kernel on the single-layer decode shape")
     ap.add_argument("--launch", default="graph", choices=("graph", "direct"))
     ap.add_argument("--io", default="f32", choices=("f32", "bf16"),
                     help="element type of q, k, v and output (state stays f32)")
@@ -157,11 +161,19 @@ def workload_info(name: str, io: str = "f32"):
     """(forward workload, kernel name, algorithmic bytes per launch, description)
     of a bench workload name; 'rollback' is the rollback copy on the
     spec_verify shape (one state slice read and written per sequence, plus the
-    index array)."""
+    index array); 'state_copy' is the same copy kernel on the single-layer
+    decode shape (one token, index 0): it reads and writes exactly that call's
+    state bytes and nothing else, the floor the decode call is measured
+    against (the HIP runtime's own device-to-device copy of those bytes is
+    slower)."""
     if name == "rollback":
         w = WORKLOADS["spec_verify"]
         return (w, "gdn_rollback_kernel", w.state_bytes() + 4 * w.n_seqs,
                 "accepted-prefix rollback after " + w.description)
+    if name == "state_copy":
+        w = WORKLOADS["decode"]
+        return (w, "gdn_rollback_kernel", w.state_bytes() + 4 * w.n_seqs,
+                "state copy (rollback kernel, index 0) on the " + w.description)
     w = WORKLOADS[name]
     kernel = DECODE_KERNEL_NAME if w.n_tokens == 1 else KERNEL_NAME
     if io == "bf16":
@@ -282,7 +294,7 @@ def summarize_default_trace(src: str, command: str, out_dir: str | None = None) 
     lines += ["", "Per-launch kernel time reported by the same (profiled) run's bench line:", "",
               "| workload | kernel_us under the profiler |", "|---|---|",
               f"| decode | {line['kernel_us']:.3f} |"]
-    for k in ("prefill", "batched_decode", "spec_verify", "rollback"):
+    for k in ("prefill", "batched_decode", "spec_verify", "rollback", "state_copy"):
         if k in line:
             lines.append(f"| {k} | {line[k]['kernel_us']:.3f} |")
     lines.append("")
@@ -349,8 +361,8 @@ def cpu_baseline(w, budget_s: float, rollback: bool = False):
         one = c1 * per_call / d1 / 1e9
         alln = cn * per_call / dn / 1e9
         unit = "GB/s"
-        s1 = f"{c1} oracle rollback calls on the spec_verify shape, {d1:.1f} s, 1 thread"
-        sn = (f"{cn} oracle rollback calls on the spec_verify shape, {dn:.1f} s, "
+        s1 = f"{c1} oracle rollback calls on the {w.name} shape, {d1:.1f} s, 1 thread"
+        sn = (f"{cn} oracle rollback calls on the {w.name} shape, {dn:.1f} s, "
               f"{min(cpu['threads'], w.n_seqs)} threads over the sequences")
         used = min(cpu["threads"], w.n_seqs)
     else:
@@ -481,7 +493,7 @@ def measure(name: str, *, steps: int, warmup: int, launch: str = "graph", io: st
     import linear_attention_recurrence_forward_amd as gdn
 
     dev = torch.device("cuda:0")
-    rollback = name == "rollback"
+    rollback = name in ("rollback", "state_copy")
     if (io == "bf16" or normalize_k) and rollback:
         raise SystemExit("bench.py: --io bf16 and --normalize-k apply to forward workloads")
     bf16 = io == "bf16"
@@ -502,7 +514,7 @@ def measure(name: str, *, steps: int, warmup: int, launch: str = "graph", io: st
         d["output"] = torch.empty(x["v"].shape, device=dev,
                                   dtype=torch.bfloat16 if bf16 else torch.float32)
         d["capture"] = (torch.empty((w.n_seqs, w.n_tokens, w.n_v_heads, w.d_v, w.d_k),
-                                    device=dev) if w.capture else None)
+                                    device=dev) if w.capture or rollback else None)
         sets.append(d)
     params = gdn.params_for(sets[0]["q"], sets[0]["v"], bits)
     if rollback:
@@ -737,7 +749,7 @@ def main(argv=None):
             "capture": w.capture, "normalize_k": args.normalize_k,
             "launch": args.launch, "resident_sets": m["layers"],
             "algorithmic_bytes_per_step": m["alg_bytes"],
-            "flops_per_step": 0 if m["rollback"] else w.flops(),
+            "flops_per_step": 0 if m["rollback"] or m["name"] == "state_copy" else w.flops(),
         },
         "us_per_layer": m["ms_per_step"] * 1e3,
         "kernel_us": m["kernel_us"],
@@ -758,7 +770,8 @@ def main(argv=None):
     if not args.no_cpu_baseline and plain:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, rollback=m["rollback"])
     for e in extras:
-        cpu = (None if args.no_cpu_baseline else
+        # The copy floor is a reference point, not a workload of the metric.
+        cpu = (None if args.no_cpu_baseline or e["name"] == "state_copy" else
                cpu_baseline(e["w"], args.cpu_seconds, rollback=e["rollback"]))
         line[e["name"]] = extra_object(e, cpu)
     print(json.dumps(line), flush=True)

@@ -6,7 +6,9 @@
 // sequence's state slot. An index at or past n_tokens leaves the slot as is.
 //
 // The copy is HBM-bound: every byte of the slice is read once and written
-// once, as 16-byte vectors, four per lane in flight, with non-temporal stores.
+// once, as 16-byte vectors, non-temporal, four per lane in flight when the copy
+// is large and one per lane (four times the workgroups) when four per lane
+// would leave fewer than four workgroups per compute unit.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -19,11 +21,12 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kVecsPerThread = 4;  // float4s per lane per pass
 
 // Grid: x = block within a sequence (blocks_per_seq of them), y = sequence
 // within the launch (the host moves every base to the launch's first
-// sequence), so the index read needs no division.
+// sequence), so the index read needs no division. kVecsPerThread: float4s per
+// lane per pass.
+template <int kVecsPerThread>
 __global__ __launch_bounds__(kThreads) void gdn_rollback_kernel(
     const float *capture, const uint32_t *accepted, float *state,
     uint32_t n_tokens, uint64_t seq_vecs, uint32_t blocks_per_seq) {
@@ -60,7 +63,15 @@ hipError_t enqueue_rollback(const float *capture, const uint32_t *accepted,
   // One sequence's state: n_v_heads * d_v * d_k floats, a multiple of 4
   // because d_k is 32, 64 or 128.
   const uint64_t seq_vecs = (uint64_t)n_v_heads * d_v * d_k / 4;
-  const uint64_t per_block = (uint64_t)kThreads * kVecsPerThread;
+  // Four float4s per lane, unless that leaves fewer than 4 workgroups per
+  // compute unit of an MI355X (256 of them): 3 MiB (one dense-shape layer)
+  // and 4 MiB (the 8-sequence verify) copies then run one per lane.
+  constexpr uint64_t kMinBlocks = 4 * 256;
+  const uint64_t blocks4 = ((seq_vecs + kThreads * 4 - 1) / (kThreads * 4)) * n_seqs;
+  const int vpt = blocks4 >= kMinBlocks ? 4 : 1;
+  const void *kernel = vpt == 4 ? reinterpret_cast<const void *>(&gdn_rollback_kernel<4>)
+                                : reinterpret_cast<const void *>(&gdn_rollback_kernel<1>);
+  const uint64_t per_block = (uint64_t)kThreads * vpt;
   uint64_t blocks_per_seq = (seq_vecs + per_block - 1) / per_block;
   if (blocks_per_seq > 1024) blocks_per_seq = 1024;  // the loop covers the rest
   const uint64_t blocks = blocks_per_seq * n_seqs;
@@ -74,9 +85,7 @@ hipError_t enqueue_rollback(const float *capture, const uint32_t *accepted,
     const uint32_t *acc = accepted + s0;
     float *st = state + (uint64_t)s0 * seq_vecs * 4;
     void *args[] = {&cap, &acc, &st, &n_tokens, const_cast<uint64_t *>(&seq_vecs), &bps};
-    const hipError_t e =
-        hipLaunchKernel(reinterpret_cast<const void *>(&gdn_rollback_kernel), dim3(bps, ny),
-                        dim3(kThreads), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(kernel, dim3(bps, ny), dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -239,3 +239,12 @@ def test_summarize_default_trace(bench, tmp_path):
     assert "`cafe`" in text and "the-command" in text
     assert "| 3 | 3.00 | 3.00 | 2.00 | 60.0 |" in text
     assert "| decode | 2.800 |" in text and "| prefill | 180.000 |" in text
+
+
+def test_state_copy_bytes(bench):
+    """The decode call's floor: the rollback kernel on the decode shape moves
+    the state once each way (and reads one index)."""
+    w, kernel, alg, _ = bench.workload_info("state_copy")
+    assert (w.d_k, w.d_v, w.n_v_heads, w.n_tokens, w.n_seqs) == (128, 128, 48, 1, 1)
+    assert kernel == "gdn_rollback_kernel"
+    assert alg == 2 * 4 * 128 * 128 * 48 + 4
