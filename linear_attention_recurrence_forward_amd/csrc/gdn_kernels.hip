@@ -678,6 +678,48 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     return c;
   };
 
+  // Shared staging (multi-token calls without capture, and without the
+  // per-token key normalisation, which sums each key row in the wave that
+  // loads it). All waves of a workgroup need the same k and q rows, so
+  // instead of every wave loading every token's rows, each wave loads NB /
+  // WAVES tokens of the next ring group and stages them, widened to f32, in
+  // a workgroup LDS block (two of them, one per alternate group); one
+  // workgroup barrier per group publishes the block. Every wave of a
+  // workgroup runs the same token loop, so every wave reaches every barrier.
+  // Four times fewer row requests, and no staging write per token: the
+  // 512-token prefill went from 177 to 169 us, its key-normalised form from
+  // 204 to 187 us. Not at D_k = 32, where a wave's rows are a quarter as
+  // long and the per-group barrier costs more than the loads it saves
+  // (a D_k = 32 prefill ran 106 us without it, 118 us with it).
+  constexpr bool SHARE = !CAPTURE && NK != 1 && DK >= 64 && NB % WAVES == 0;
+  constexpr int TPW = SHARE ? NB / WAVES : 1;  // tokens a wave stages per group
+  __shared__ __attribute__((aligned(16)))
+  float grp_lds[SHARE ? 2 : 1][SHARE ? NB : 1][SHARE ? 2 * DK : 1];
+  // This lane's part of a token's rows, widened, into a staged row pair.
+  auto stage_rows = [&](const Tok &x, float *dst) {
+    float kw[EPL], qw[EPL];
+    widen<IO, EPL>(x.kr, kw);
+    widen<IO, EPL>(x.qr, qw);
+    if (SLANES == 64 || lane < SLANES) {
+#pragma unroll
+      for (uint32_t e = 0; e < EPL; ++e) {
+        dst[EPL * lane + e] = kw[e];
+        dst[DK + EPL * lane + e] = qw[e];
+      }
+    }
+  };
+  // This lane's columns of a staged row pair.
+  auto columns_at = [&](const float *rows) {
+    KQ c;
+    c.inv = 1.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      c.k[m] = *reinterpret_cast<const f4 *>(rows + m * 4 * L + 4 * sub);
+      c.q[m] = *reinterpret_cast<const f4 *>(rows + DK + m * 4 * L + 4 * sub);
+    }
+    return c;
+  };
+
   // Factor table of the current 64-token chunk (see next_chunk below).
   __shared__ float4 ab_lds[WAVES][64];
   float4 *const ab = ab_lds[wave];
@@ -887,9 +929,22 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     // v of the group starting at t, requested before the ring so that the
     // first group's wait for it leaves the ring's requests in flight.
     float v_raw = load_vgroup(0);
-    Tok buf[NB];
+    Tok buf[SHARE ? TPW : NB];
+    uint32_t gb = 0;  // SHARE: the staged block of the current group
+    if constexpr (SHARE) {
+      // The first group's rows (this wave's share), staged and published.
 #pragma unroll
-    for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
+      for (int i = 0; i < TPW; ++i) {
+        const uint32_t tk = wave * TPW + i;
+        load_token(tk < T ? tk : T - 1, buf[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[0][wave * TPW + i]);
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
+    }
     float vg[NY][NB];
     uint32_t t = 0;
     // Columns of the current token. Without capture each step stages the next
@@ -899,7 +954,11 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     // step (4-token verify +2% the other way).
     constexpr bool AHEAD = !CAPTURE;
     KQ kq;
-    if constexpr (AHEAD) kq = columns(buf[0]);
+    if constexpr (SHARE) {
+      kq = columns_at(grp_lds[0][0]);
+    } else if constexpr (AHEAD) {
+      kq = columns(buf[0]);
+    }
     KRow kn;
     float kss = 0.f;  // sum of squares of the parts already received
     float invg[GNORM ? NB : 1];
@@ -946,6 +1005,15 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         read_krow(invg);
         load_krow(t + NB, 0, kn);
       }
+      if constexpr (SHARE) {
+        // This wave's share of the next group's rows (clamped to the last
+        // token; at most 2 NB - 1 tokens past t, within 64 + 2 NB of base_t).
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const uint32_t tk = t + NB + wave * TPW + i;
+          load_token(tk < T ? tk : T - 1, buf[i]);
+        }
+      }
       // The group's prefetch requests (tokens t + NB - 1 .. t + 2 NB - 2),
       // each clamped to the last token, at byte offsets from base_t's row: a
       // running offset and one minimum per token. Requests reach at most
@@ -972,17 +1040,33 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         // the prefetch request and the next token's staging are issued
         // ahead of the other waves' throughput work (-1%).
         __builtin_amdgcn_s_setprio(1);
-        load_token_at(kq_next < kq_last ? kq_next : kq_last, buf[(u + NB - 1) % NB]);
-        kq_next += kq_bytes;
-        // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
-        // last token when t is the last one.
-        const KQ nxt = columns(buf[AHEAD ? (u + 1) % NB : u]);
-        KQ cur = AHEAD ? kq : nxt;
+        KQ nxt, cur;
+        if constexpr (SHARE) {
+          // The next token's columns, from this group's block; the next
+          // group's first token is read after the barrier.
+          nxt = u + 1 < NB ? columns_at(grp_lds[gb][u + 1]) : kq;
+          cur = kq;
+        } else {
+          load_token_at(kq_next < kq_last ? kq_next : kq_last, buf[(u + NB - 1) % NB]);
+          kq_next += kq_bytes;
+          // buf[(u + 1) % NB] holds token t + 1, or a clamped repeat of the
+          // last token when t is the last one.
+          nxt = columns(buf[AHEAD ? (u + 1) % NB : u]);
+          cur = AHEAD ? kq : nxt;
+        }
         if constexpr (GNORM) cur.inv = invg[u];
         step(t, u % TB, false, cur, vu, u == 0 ? 1u : eager,
              u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z, false);
         kq = nxt;
         ++t;
+      }
+      if constexpr (SHARE) {
+        // Stage this wave's share of the next group, publish, switch blocks.
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[gb ^ 1][wave * TPW + i]);
+        __syncthreads();
+        gb ^= 1;
+        kq = columns_at(grp_lds[gb][0]);
       }
       kappa = f[NB - 1].z;  // 1 after an eager group
     }
@@ -1002,7 +1086,14 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         float vu[NY];
 #pragma unroll
         for (int r = 0; r < NY; ++r) vu[r] = vg[r][u];
-        if constexpr (AHEAD) {
+        if constexpr (SHARE) {
+          KQ nxt = kq;
+          if (t + 1 < T) nxt = columns_at(grp_lds[gb][u + 1]);
+          KQ cur = kq;
+          if constexpr (GNORM) cur.inv = invg[u];
+          run(t, u % TB, cur, vu);
+          kq = nxt;
+        } else if constexpr (AHEAD) {
           KQ nxt = kq;
           if (t + 1 < T) nxt = columns(buf[u + 1]);
           KQ cur = kq;
