@@ -160,6 +160,11 @@ constexpr int kBufferWord3 = 0x00020000;
 // accesses.
 constexpr int kNonTemporal = 2;
 
+// s_waitcnt operand (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8) that waits for every outstanding vector-memory
+// request and for nothing else.
+constexpr int kWaitVmAll = 0x0F70;
+
 // Descriptor over `bytes` bytes from `base` (bytes < 2^32).
 __device__ __forceinline__ rsrc_t buffer(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes,
@@ -736,8 +741,11 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
   // batches (NB % TB == 0), a constant after unrolling. may_end: t may be the
   // last token (in a ring group only the last token can be, and it then ends
   // an output batch anyway).
+  // hold: a batch that this token ends is not stored here but by
+  // store_held(), after the ring group's staging wait (see there).
+  uint32_t held = 0, held_soff = 0;  // wave-uniform
   auto step = [&](uint32_t t, uint32_t j, bool may_end, const KQ &kq, const float (&v)[NY],
-                  uint32_t decay, float alpha, float b, float c, bool raise) {
+                  uint32_t decay, float alpha, float b, float c, bool raise, bool hold) {
     // The sk chain (decay, dot products, butterfly, delta) is what the rest
     // of the token, and the next token, wait for; the rank-1 write and y are
     // throughput work the other waves of the SIMD can interleave with. The
@@ -847,11 +855,31 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         // with c = 1.
         yk[0] = may_end ? w[0] : w[0] * ab[(t0 & 63u) + slot_t].z;
       }
-      if (slot_t <= (t & (TB - 1)))
+      if (hold) {
+        held = 1;
+        held_soff = soff;
+      } else if (slot_t <= (t & (TB - 1))) {
 #pragma unroll
         for (int r = 0; r < NY; ++r)
           if (ok[r]) Io<IO>::store1(o_rs, yoff[r], soff, yk[r] * a.q_scale);
+      }
       __builtin_amdgcn_s_setprio(0);
+    }
+  };
+  // The held batch (it ended a ring group, so every token slot is filled).
+  // The memory counter runs in issue order, so a wait for the rows that
+  // were requested at the group's start also waits for every store issued
+  // after them; and when a store is issued on some paths only, the
+  // compiler's bookkeeping waits as if it were (for its write
+  // acknowledgement). Issued after that wait, the store is not waited for
+  // until the next group's end, long after it has completed.
+  auto store_held = [&]() {
+    if (held != 0) {
+      const rsrc_t o_rs = buffer(o_b, v_ext);
+#pragma unroll
+      for (int r = 0; r < NY; ++r)
+        if (ok[r]) Io<IO>::store1(o_rs, yoff[r], held_soff, yk[r] * a.q_scale);
+      held = 0;
     }
   };
 
@@ -915,7 +943,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     auto run = [&](uint32_t t, uint32_t j, const KQ &kq, const float (&v)[NY]) {
       next_chunk(t);
       const float4 f = ab[t & 63u];
-      step(t, j, true, kq, v, true, f.x, f.w, 1.f, true);
+      step(t, j, true, kq, v, true, f.x, f.w, 1.f, true, false);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -941,6 +969,13 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
 #pragma unroll
       for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[0][wave * TPW + i]);
       __syncthreads();
+      // Every request so far (state, the first chunk's g and beta, the first
+      // group's v) completes before the loop. The compiler orders these
+      // requests freely; one of them still in flight on entry would make its
+      // bookkeeping at the loop's first wait for v (every group) cover the
+      // requests issued after it in the loop, such as the next chunk's g and
+      // beta or the held output store.
+      __builtin_amdgcn_s_waitcnt(kWaitVmAll);
     } else {
 #pragma unroll
       for (int u = 0; u < NB - 1; ++u) load_token(u < T ? u : T - 1, buf[u]);
@@ -1056,7 +1091,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         }
         if constexpr (GNORM) cur.inv = invg[u];
         step(t, u % TB, false, cur, vu, u == 0 ? 1u : eager,
-             u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z, false);
+             u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z, false, SHARE && u == NB - 1);
         kq = nxt;
         ++t;
       }
@@ -1064,6 +1099,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         // Stage this wave's share of the next group, publish, switch blocks.
 #pragma unroll
         for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[gb ^ 1][wave * TPW + i]);
+        store_held();
         __syncthreads();
         gb ^= 1;
         kq = columns_at(grp_lds[gb][0]);
