@@ -963,6 +963,53 @@ def test_addresses_with_bit31_of_the_low_word_set():
     torch.cuda.empty_cache()
 
 
+
+@pytest.mark.parametrize("shape", [(128, 72, 2, 8, 1, 2), (128, 72, 8, 96, 1, 1),
+                                   (64, 40, 4, 64, 1, 2), (32, 70, 1, 3, 1, 2)],
+                         ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
+def test_one_token_arrays_more_than_4gib_apart(shape):
+    """One-token calls pass their arrays as 32-bit offsets from the lowest one
+    when all lie within 4 GiB of it, and as full pointers otherwise (output and
+    state_out here sit past 4 GiB from the inputs). Both forms against the
+    oracle, and against each other bit for bit (they share the token's
+    arithmetic); f32 and bf16 I/O, with and without key normalisation."""
+    dk, dv, hk, hv, t, s_ = shape
+    x = make_inputs(Workload("far", 0, dk, dv, hk, hv, t, s_, fold_q_scale=True), seed=91 + dk)
+    buf = torch.empty((1 << 32) + (64 << 20), dtype=torch.uint8, device="cuda")
+    cursor = [0]
+
+    def carve(shape_, dtype=torch.float32, at=None):
+        n = int(np.prod(shape_)) * torch.tensor([], dtype=dtype).element_size()
+        off = (cursor[0] if at is None else at) + 255 & ~255
+        cursor[0] = off + n
+        return buf[off:off + n].view(dtype).view(shape_)
+
+    for io in (torch.float32, torch.bfloat16):
+        for nk in (False, True):
+            cursor[0] = 0
+            d = {}
+            for n in NAMES:
+                dt = io if n in ("q", "k", "v") else torch.float32
+                d[n] = carve(x[n].shape, dt)
+                d[n].copy_(torch.from_numpy(x[n]).to(dt))
+            io_out = io
+            near = (carve(x["v"].shape, io_out), carve(x["state_in"].shape))
+            far_at = (1 << 32) + (1 << 20)
+            far = (carve(x["v"].shape, io_out, at=far_at), carve(x["state_in"].shape))
+            assert far[0].data_ptr() - d["state_in"].data_ptr() > 1 << 32
+            for o_, s2 in (near, far):
+                gdn.forward(*(d[n] for n in NAMES), q_scale_bits=x["q_scale_bits"],
+                            normalize_k=nk, output=o_, state_out=s2)
+            torch.cuda.synchronize()
+            what = f"{shape} {io} normalize_k={nk}"
+            assert torch.equal(near[0], far[0]) and torch.equal(near[1], far[1]), what
+            if io == torch.float32:
+                exp = ref(x, q_scale_bits=x["q_scale_bits"], normalize_k=nk)
+                close(far[0].cpu().numpy(), exp[0], f"{what} output, arrays far apart")
+                close(far[1].cpu().numpy(), exp[1], f"{what} state, arrays far apart")
+    del buf
+    torch.cuda.empty_cache()
+
 def test_q_scale_value():
     """forward(q_scale=<float>) equals forward(q_scale_bits=<its bits>) bit for
     bit."""
