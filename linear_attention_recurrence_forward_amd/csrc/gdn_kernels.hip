@@ -1225,13 +1225,9 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
     for (int m = 0; m < NV; ++m) st[r][m] = load4_stream(s_in, cell[r] + m * 16 * L);
   const uint64_t kq = ((uint64_t)s * n_k_heads + kh) * DK * IB;
   const rsrc_t k_rs = buffer(static_cast<const char *>(p.k) + kq, DK * IB);
-  const rsrc_t q_rs = buffer(static_cast<const char *>(p.q) + kq, DK * IB);
   f4 kc[NV], qc[NV];
 #pragma unroll
-  for (int m = 0; m < NV; ++m) {
-    kc[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, 0);
-    qc[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, 0);
-  }
+  for (int m = 0; m < NV; ++m) kc[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, 0);
   const float g = load1(buffer(p.g + hs, 4), 0);
 
   const rsrc_t v_rs = buffer(static_cast<const char *>(p.v) + (uint64_t)hs * d_v * IB, d_v * IB);
@@ -1239,6 +1235,18 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
 #pragma unroll
   for (int r = 0; r < NY; ++r) v[r] = Io<IO>::load1(v_rs, row[r] * IB, 0);
   const float beta = load1(buffer(p.beta + hs, 4), 0);
+  const rsrc_t q_rs = buffer(static_cast<const char *>(p.q) + kq, DK * IB);
+#pragma unroll
+  for (int m = 0; m < NV; ++m) qc[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, 0);
+  // Then the arguments that may come from kernel-argument memory (the store
+  // addresses and q_scale): requested here, after every load, and waited
+  // for once (the empty asm takes them as operands, so that no read is
+  // left for its first use, after the arithmetic).
+  __builtin_amdgcn_sched_barrier(0);
+  void *const out = p.output;
+  float *const s_out_p = p.state_out, *const cap_p = p.capture;
+  const float qsc = q_scale;
+  asm volatile("" ::"s"(out), "s"(s_out_p), "s"(cap_p), "s"(qsc));
 
   // Normalised keys (NK): the L lanes of a row group hold the whole key row;
   // 1 / sqrt(sum k^2 + kNormEps) is folded into sk and delta.
@@ -1299,14 +1307,14 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
 #pragma unroll
   for (int r = 0; r < R; ++r) asm volatile("" : "+v"(part[r]));
   if constexpr (CAPTURE) {
-    const rsrc_t ct = buffer(p.capture + head, head_bytes);
+    const rsrc_t ct = buffer(cap_p + head, head_bytes);
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (ok[r])
 #pragma unroll
         for (int m = 0; m < NV; ++m) store4_stream(ct, cell[r] + m * 16 * L, st[r][m]);
   }
-  const rsrc_t s_out = buffer(p.state_out + head, head_bytes);
+  const rsrc_t s_out = buffer(s_out_p + head, head_bytes);
 #pragma unroll
   for (int r = 0; r < R; ++r)
     if (ok[r])
@@ -1322,78 +1330,75 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
   }
   // Lane 0 of each set of TB lanes writes its rows' outputs, q_scale applied.
   const rsrc_t o_rs =
-      buffer(static_cast<char *>(p.output) + (uint64_t)hs * d_v * IB, d_v * IB);
+      buffer(static_cast<char *>(out) + (uint64_t)hs * d_v * IB, d_v * IB);
   if (sub % TB == 0)
 #pragma unroll
     for (int r = 0; r < NY; ++r)
-      if (ok[r]) Io<IO>::store1(o_rs, row[r] * IB, 0, y[r] * q_scale);
+      if (ok[r]) Io<IO>::store1(o_rs, row[r] * IB, 0, y[r] * qsc);
 }
 
-// Arguments of the general one-token kernel that its first loads do not
-// need. Its leading parameters (the state, k, q and g bases and the sizes
-// that address them) are preloaded into scalar registers at dispatch (the
-// library is built with a kernel-argument preload count that covers them);
-// these fields are read from kernel-argument memory.
-struct DecodeArgs {
-  const float *beta;
-  const void *v;  // IO type
-  void *output;   // IO type
+// Arguments of the one-token kernels that only the stores need: read from
+// kernel-argument memory (the others are preloaded into scalar registers at
+// dispatch, see below) once the loads are issued, a round trip that
+// completes under theirs.
+struct DecodeTail {
+  void *output;  // IO type
   float *state_out, *capture;
   float q_scale;
 };
 
-// The general one-token kernel (capture, or arrays that do not fit the
-// packed form below). Grid: x = (value head << rb_shift) | row block, the
-// row blocks of a head padded to a power of two (padding blocks exit at
-// once); y = sequence within the launch. shifts: kh_shift in bits 0-7,
-// rb_shift in bits 8-15; vh / n_k_heads == (vh * kh_magic) >> kh_shift for
-// every value head (host-computed, exact below 2^23 heads).
+// Sizes of a one-token launch in one 32-bit word: d_v in bits 0-10,
+// rb_shift in 11-14, n_k_heads in 15-24, n_v_heads / n_k_heads in 25-31.
+constexpr uint32_t kPackDv = 11, kPackRb = 4, kPackNk = 10, kPackGroups = 7;
+
+// The one-token kernel. The six arrays that the loads address (state, k,
+// q, g, v, beta) and the size word are the first 13 kernel-argument dwords,
+// which the dispatch preloads into scalar registers (the library is built
+// with that preload count): no load waits for kernel-argument memory.
+// Reading v and beta's bases from it cost single-layer decode 2.75 against
+// 2.69 us; q's, 2.76 (y waits for q). The grid's own sizes would be such a
+// read too (they live in the implicit kernel arguments), hence the size
+// word. Grid: x = (key head kh << rb_shift) | row block, the row blocks of
+// a head padded to a power of two (padding blocks exit at once); y = g, one
+// of the n_v_heads / n_k_heads value heads of a key head; z = sequence
+// within the launch. vh = kh + g * n_k_heads (the modulo GQA map, no
+// division), and the workgroups run in the order of the state in memory
+// (sequence, value head, row block); a key-head-major order measured 44.9
+// against 42.4 us on the 64-sequence batch.
 template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
 __global__ __launch_bounds__(WAVES * 64) void gdn_decode(
     const float *state_in, const void *k_in, const void *q_in, const float *g_in,
-    uint32_t d_v, uint32_t n_v_heads, uint32_t n_k_heads, uint32_t kh_magic,
-    uint32_t shifts, DecodeArgs a) {
+    const void *v_in, const float *beta_in, uint32_t sizes, DecodeTail a) {
+  const uint32_t d_v = sizes & ((1u << kPackDv) - 1u);
+  const uint32_t rb_shift = (sizes >> kPackDv) & ((1u << kPackRb) - 1u);
+  const uint32_t n_k_heads = (sizes >> (kPackDv + kPackRb)) & ((1u << kPackNk) - 1u);
+  const uint32_t n_v_heads = (sizes >> (kPackDv + kPackRb + kPackNk)) * n_k_heads;
+  const uint32_t rb = blockIdx.x & ((1u << rb_shift) - 1u);
+  const uint32_t kh = blockIdx.x >> rb_shift;
+  const uint32_t vh = kh + n_k_heads * blockIdx.y;
+  const DecodePtrs p{state_in, k_in, q_in, g_in, beta_in, v_in, a.output, a.state_out, a.capture};
+  decode_token<DK, C, R, WAVES, CAPTURE, IO, NK>(p, d_v, n_v_heads, n_k_heads, blockIdx.z, vh,
+                                                 kh, rb, a.q_scale);
+}
+
+// The one-token kernel for sizes past the size word's fields (d_v above
+// 2047, more than 1023 key heads or 127 value heads per key head). Grid: x =
+// (value head << rb_shift) | row block, y = sequence within the launch.
+// shifts: kh_shift in bits 0-7, rb_shift in bits 8-15; vh / n_k_heads ==
+// (vh * kh_magic) >> kh_shift for every value head (host-computed, exact
+// below 2^23 heads). Its sizes come from kernel-argument memory.
+template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
+__global__ __launch_bounds__(WAVES * 64) void gdn_decode_wide(
+    const float *state_in, const void *k_in, const void *q_in, const float *g_in,
+    const void *v_in, const float *beta_in, uint32_t d_v, uint32_t n_v_heads,
+    uint32_t n_k_heads, uint32_t kh_magic, uint32_t shifts, DecodeTail a) {
   const uint32_t rb_shift = shifts >> 8, kh_shift = shifts & 0xFFu;
   const uint32_t rb = blockIdx.x & ((1u << rb_shift) - 1u);
   const uint32_t vh = blockIdx.x >> rb_shift;
   const uint32_t kh = vh - n_k_heads * (uint32_t)(((uint64_t)vh * kh_magic) >> kh_shift);
-  const DecodePtrs p{state_in, k_in, q_in, g_in, a.beta, a.v, a.output, a.state_out, a.capture};
+  const DecodePtrs p{state_in, k_in, q_in, g_in, beta_in, v_in, a.output, a.state_out, a.capture};
   decode_token<DK, C, R, WAVES, CAPTURE, IO, NK>(p, d_v, n_v_heads, n_k_heads, blockIdx.y, vh,
                                                  kh, rb, a.q_scale);
-}
-
-// The packed one-token kernel (no capture): every argument fits the 13
-// kernel-argument dwords that are preloaded into scalar registers at
-// dispatch, so the kernel reads no kernel-argument memory. A read of that
-// memory is a round trip ahead of every load and store whose address
-// depends on it: without it, single-layer decode 2.75 -> 2.58 us. The eight
-// arrays are given as 32-bit byte offsets from one base (the host uses this
-// form when they all lie within 4 GiB of the lowest), d_v and n_v_heads in
-// the halves of dv_nv, n_k_heads and rb_shift in the low and high halves of
-// nk_rb (each below 2^16). Grid: x = (key head kh << rb_shift) | row block,
-// y = g, z = sequence within the launch: value head vh = kh + g * n_k_heads
-// (the modulo GQA map, with no division), and workgroups in the order of
-// the state in memory (sequence, value head, row block), which streams it
-// as the general kernel's order does (a key-head-major order measured
-// 44.9 against 42.4 us on the 64-sequence batch). Padding row blocks exit at
-// once.
-template <int DK, int C, int R, int WAVES, typename IO, int NK>
-__global__ __launch_bounds__(WAVES * 64) void gdn_decode_packed(
-    const char *base, uint32_t o_state_in, uint32_t o_k, uint32_t o_q, uint32_t o_g,
-    uint32_t o_beta, uint32_t o_v, uint32_t o_output, uint32_t o_state_out, uint32_t dv_nv,
-    uint32_t nk_rb, float q_scale) {
-  const uint32_t d_v = dv_nv & 0xFFFFu, n_v_heads = dv_nv >> 16;
-  const uint32_t n_k_heads = nk_rb & 0xFFFFu, rb_shift = nk_rb >> 16;
-  const uint32_t rb = blockIdx.x & ((1u << rb_shift) - 1u);
-  const uint32_t kh = blockIdx.x >> rb_shift;
-  const uint32_t vh = kh + n_k_heads * blockIdx.y;
-  char *const w = const_cast<char *>(base);
-  const DecodePtrs p{reinterpret_cast<const float *>(base + o_state_in), base + o_k, base + o_q,
-                     reinterpret_cast<const float *>(base + o_g),
-                     reinterpret_cast<const float *>(base + o_beta), base + o_v, w + o_output,
-                     reinterpret_cast<float *>(w + o_state_out), nullptr};
-  decode_token<DK, C, R, WAVES, false, IO, NK>(p, d_v, n_v_heads, n_k_heads, blockIdx.z, vh, kh,
-                                               rb, q_scale);
 }
 
 // ---------------------------------------------------------------- geometry
@@ -1403,7 +1408,7 @@ struct Geometry {
   int threads;
   const void *kernel;
   bool decode;  // gdn_decode (one token) rather than gdn_recurrent
-  const void *packed = nullptr;  // one token without capture: gdn_decode_packed
+  const void *wide = nullptr;  // one token, GQA ratio above 65535: gdn_decode_wide
 };
 
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
@@ -1416,12 +1421,10 @@ constexpr Geometry make_geometry() {
 
 template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
 constexpr Geometry make_decode_geometry() {
-  const void *packed = nullptr;
-  if constexpr (!CAPTURE)
-    packed = reinterpret_cast<const void *>(&gdn_decode_packed<DK, C, R, WAVES, IO, NK>);
-  return Geometry{WAVES * (64 / (DK / C)) * R, WAVES * 64,
-                  reinterpret_cast<const void *>(&gdn_decode<DK, C, R, WAVES, CAPTURE, IO, NK>),
-                  true, packed};
+  return Geometry{
+      WAVES * (64 / (DK / C)) * R, WAVES * 64,
+      reinterpret_cast<const void *>(&gdn_decode<DK, C, R, WAVES, CAPTURE, IO, NK>), true,
+      reinterpret_cast<const void *>(&gdn_decode_wide<DK, C, R, WAVES, CAPTURE, IO, NK>)};
 }
 
 // Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
@@ -1554,72 +1557,50 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
 
   const uint64_t io = f.bf16 ? 2 : 4;
   if (geo.decode) {
-    // One token: grid x = (value head << rb_shift) | row block, the row
-    // blocks padded to 2^rb_shift; grid y = sequence, one launch per 65535
-    // sequences with every base moved to the launch's first sequence
-    // (sequences are independent and T = 1).
+    // One token: grid x = (key head << rb_shift) | row block, the row blocks
+    // padded to 2^rb_shift; y = value head of the key head; z = sequence,
+    // one launch per 65535 sequences with every base moved to the launch's
+    // first sequence (sequences are independent and T = 1). Sizes past the
+    // size word take gdn_decode_wide: x = (value head << rb_shift) | row
+    // block, y = sequence.
+    constexpr uint32_t kMaxGrid = 65535;
     const uint32_t rb_shift = ceil_log2(row_blocks);
+    const uint32_t groups = f.n_v_heads / f.n_k_heads;
+    const bool wide = f.d_v >> kPackDv != 0 || rb_shift >> kPackRb != 0 ||
+                      f.n_k_heads >> kPackNk != 0 || groups >> kPackGroups != 0;
     const uint32_t kh_shift = 23 + ceil_log2(f.n_k_heads);
     const uint32_t kh_magic =
         (uint32_t)(((uint64_t(1) << kh_shift) + f.n_k_heads - 1) / f.n_k_heads);
-    uint32_t shifts = kh_shift | rb_shift << 8;
-    const uint32_t gx = f.n_v_heads << rb_shift;
     const uint64_t state_seq = (uint64_t)f.n_v_heads * f.d_v * f.d_k;  // floats
     const uint64_t kq_seq = (uint64_t)f.n_k_heads * f.d_k * io;       // bytes
     const uint64_t v_seq = (uint64_t)f.n_v_heads * f.d_v * io;        // bytes
-    constexpr uint32_t kMaxY = 65535;
-    // The packed kernel's grid: x = (key head << rb_shift) | row block, y =
-    // the n_v_heads / n_k_heads value heads of each key head, z = sequence;
-    // its sizes in 16-bit fields.
-    const uint32_t groups = f.n_v_heads / f.n_k_heads;
-    const bool pack_sizes = geo.packed != nullptr && f.d_v < 65536 && f.n_v_heads < 65536 &&
-                            ((uint64_t)f.n_k_heads << rb_shift) * geo.threads <= 0xFFFFFFFFu;
-    for (uint32_t s0 = 0; s0 < f.n_seqs; s0 += kMaxY) {
-      const uint32_t ny = f.n_seqs - s0 < kMaxY ? f.n_seqs - s0 : kMaxY;
+    for (uint32_t s0 = 0; s0 < f.n_seqs; s0 += kMaxGrid) {
+      const uint32_t ns = f.n_seqs - s0 < kMaxGrid ? f.n_seqs - s0 : kMaxGrid;
       const float *state_in = f.state_in + s0 * state_seq;
       const void *k = static_cast<const char *>(f.k) + s0 * kq_seq;
-      const void *q = static_cast<const char *>(f.q) + s0 * kq_seq;
       const float *g = f.g + (uint64_t)s0 * f.n_v_heads;
-      const float *beta = f.beta + (uint64_t)s0 * f.n_v_heads;
       const void *v = static_cast<const char *>(f.v) + s0 * v_seq;
-      void *output = static_cast<char *>(f.output) + s0 * v_seq;
-      float *state_out = f.state_out + s0 * state_seq;
-      if (pack_sizes) {
-        // The eight arrays as offsets from the lowest of them, if all fit.
-        const uintptr_t ptr[8] = {(uintptr_t)state_in, (uintptr_t)k,    (uintptr_t)q,
-                                  (uintptr_t)g,        (uintptr_t)beta, (uintptr_t)v,
-                                  (uintptr_t)output,   (uintptr_t)state_out};
-        uintptr_t lo = ptr[0];
-        for (uintptr_t x : ptr) lo = x < lo ? x : lo;
-        uint32_t off[8];
-        bool fits = true;
-        for (int i = 0; i < 8; ++i) {
-          fits = fits && ptr[i] - lo <= 0xFFFFFFFFu;
-          off[i] = (uint32_t)(ptr[i] - lo);
-        }
-        if (fits) {
-          const char *base = reinterpret_cast<const char *>(lo);
-          uint32_t dv_nv = f.d_v | f.n_v_heads << 16, nk_rb = f.n_k_heads | rb_shift << 16;
-          float q_scale = f.q_scale;
-          void *args[] = {&base,   &off[0], &off[1], &off[2], &off[3], &off[4], &off[5],
-                          &off[6], &off[7], &dv_nv,  &nk_rb,  &q_scale};
-          const hipError_t e = hipLaunchKernel(geo.packed, dim3(f.n_k_heads << rb_shift, groups, ny),
-                                               dim3(geo.threads), args, 0, stream);
-          if (e != hipSuccess) return e;
-          continue;
-        }
+      const float *beta = f.beta + (uint64_t)s0 * f.n_v_heads;
+      const void *q = static_cast<const char *>(f.q) + s0 * kq_seq;
+      DecodeTail t;
+      t.output = static_cast<char *>(f.output) + s0 * v_seq;
+      t.state_out = f.state_out + s0 * state_seq;
+      t.capture = f.capture != nullptr ? f.capture + s0 * state_seq : nullptr;
+      t.q_scale = f.q_scale;
+      hipError_t e;
+      if (!wide) {
+        uint32_t sizes = f.d_v | rb_shift << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
+                         groups << (kPackDv + kPackRb + kPackNk);
+        void *args[] = {&state_in, &k, &q, &g, &v, &beta, &sizes, &t};
+        e = hipLaunchKernel(geo.kernel, dim3(f.n_k_heads << rb_shift, groups, ns),
+                            dim3(geo.threads), args, 0, stream);
+      } else {
+        uint32_t d_v = f.d_v, n_v = f.n_v_heads, n_k = f.n_k_heads, magic = kh_magic;
+        uint32_t shifts = kh_shift | rb_shift << 8;
+        void *args[] = {&state_in, &k, &q, &g, &v, &beta, &d_v, &n_v, &n_k, &magic, &shifts, &t};
+        e = hipLaunchKernel(geo.wide, dim3(f.n_v_heads << rb_shift, ns), dim3(geo.threads), args,
+                            0, stream);
       }
-      uint32_t d_v = f.d_v, n_v = f.n_v_heads, n_k = f.n_k_heads, magic = kh_magic;
-      DecodeArgs d;
-      d.beta = beta;
-      d.v = v;
-      d.output = output;
-      d.state_out = state_out;
-      d.capture = f.capture != nullptr ? f.capture + s0 * state_seq : nullptr;
-      d.q_scale = f.q_scale;
-      void *args[] = {&state_in, &k, &q, &g, &d_v, &n_v, &n_k, &magic, &shifts, &d};
-      const hipError_t e =
-          hipLaunchKernel(geo.kernel, dim3(gx, ny), dim3(geo.threads), args, 0, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

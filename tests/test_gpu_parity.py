@@ -968,11 +968,11 @@ def test_addresses_with_bit31_of_the_low_word_set():
                                    (64, 40, 4, 64, 1, 2), (32, 70, 1, 3, 1, 2)],
                          ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
 def test_one_token_arrays_more_than_4gib_apart(shape):
-    """One-token calls pass their arrays as 32-bit offsets from the lowest one
-    when all lie within 4 GiB of it, and as full pointers otherwise (output and
-    state_out here sit past 4 GiB from the inputs). Both forms against the
-    oracle, and against each other bit for bit (they share the token's
-    arithmetic); f32 and bf16 I/O, with and without key normalisation."""
+    """One-token calls with output and state_out more than 4 GiB from the
+    inputs (the kernel takes some bases preloaded, others from argument
+    memory, all as full 64-bit addresses) give the same bits as with every
+    array together, and match the oracle; f32 and bf16 I/O, with and without
+    key normalisation."""
     dk, dv, hk, hv, t, s_ = shape
     x = make_inputs(Workload("far", 0, dk, dv, hk, hv, t, s_, fold_q_scale=True), seed=91 + dk)
     buf = torch.empty((1 << 32) + (64 << 20), dtype=torch.uint8, device="cuda")
@@ -1009,6 +1009,25 @@ def test_one_token_arrays_more_than_4gib_apart(shape):
                 close(far[1].cpu().numpy(), exp[1], f"{what} state, arrays far apart")
     del buf
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("capture", [False, True], ids=["plain", "capture"])
+@pytest.mark.parametrize("shape", [
+    (32, 2100, 1, 1, 1, 1),     # d_v past 2047
+    (128, 2050, 1, 2, 1, 1),
+    (32, 3, 1030, 1030, 1, 2),  # more than 1023 key heads
+    (32, 2, 1, 130, 1, 2),      # more than 127 value heads per key head
+], ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
+def test_one_token_sizes_past_the_size_word(shape, capture):
+    """One-token calls whose sizes do not fit the one-token kernel's 32-bit
+    size word take the kernel with full-width sizes: against the oracle."""
+    dk, dv, hk, hv, t, s_ = shape
+    x = make_inputs(Workload("wide", 0, dk, dv, hk, hv, t, s_, fold_q_scale=True),
+                    seed=101 + dv)
+    got = run(x, capture=capture)
+    exp = ref(x, capture=capture)
+    for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
+        close(g_, e, f"{shape} {what}")
 
 def test_q_scale_value():
     """forward(q_scale=<float>) equals forward(q_scale_bits=<its bits>) bit for
