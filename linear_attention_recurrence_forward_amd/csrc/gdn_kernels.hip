@@ -26,19 +26,22 @@
 //     two rows per lane y needs no butterfly per token: the partials of a
 //     batch of tokens are reduced together by one reduce-scatter that leaves
 //     token t0+j's y in lane j (see scatter_sum()).
-//   * In multi-token calls every row group of a wave needs the same k and q
-//     columns; the wave loads each token's k and q rows once and hands them
-//     out through a per-wave LDS slot, so the vector memory unit sees each
-//     byte once per wave instead of once per row group.
+//   * In multi-token calls every row group of a wave, and every wave of a
+//     workgroup, needs the same k and q columns; each token's k and q rows
+//     are loaded once per workgroup (each wave a share of a ring group's
+//     tokens; once per wave at D_k = 32 and with capture) and handed out
+//     through LDS, so the vector memory unit sees each byte once per
+//     workgroup instead of once per row group.
 //   * A workgroup covers rows of one (sequence, value head), so g and beta are
 //     uniform: the per-token factors of 64 tokens are computed once per wave
 //     (lane j holds token t0+j), parked in LDS and read per ring group.
 //   * Multi-token calls without capture carry the state divided by a running
 //     product of alphas inside each ring group (the lazy form of step()): one
 //     multiply per cell and token fewer, the same recurrence reassociated.
-//   * Token t+NB-1's k and q rows are requested while token t computes (a
-//     ring of NB register sets); v is requested once per ring group, a group
-//     ahead, for all rows of the wave.
+//   * The next ring group's k and q rows are requested at the start of a
+//     group (or, per wave, token t+NB-1's while token t computes: a ring of
+//     NB register sets); v is requested once per ring group, a group ahead,
+//     for all rows of the wave.
 //   * Every access goes through a buffer resource (a 128-bit scalar
 //     descriptor: base address and size in bytes) plus a 32-bit per-lane byte
 //     offset that is fixed for the whole loop; per-token bases advance with
@@ -47,10 +50,11 @@
 //   * Optionally (NK) every key row is used L2-normalised, its factor folded
 //     into sk and delta: computed per token, or a ring group ahead in calls of
 //     16 tokens or more.
-// Two kernels: gdn_decode for a single decode token (HBM-bound on the state
-// read and write; straight-line code, its leading arguments preloaded into
-// scalar registers) and gdn_recurrent for multi-token calls (bound by VALU
-// issue; two rows per lane share each k/q register).
+// Kernels: gdn_decode for a single decode token (HBM-bound on the state read
+// and write; straight-line code, every input base and its sizes preloaded
+// into scalar registers), gdn_decode_wide for one-token calls with sizes
+// past gdn_decode's size word, and gdn_recurrent for multi-token calls
+// (bound by VALU issue; two rows per lane share each k/q register).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1209,8 +1213,8 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
     row[r] = ok[r] ? i : d_v - 1;
   }
 
-  // The loads that need only preloaded arguments: state rows, the k and q
-  // columns of this lane, g. Then v and beta.
+  // The loads, all addressed from preloaded arguments in gdn_decode: state
+  // rows, this lane's k columns, g, v, beta, then the q columns.
   const uint32_t head_bytes = d_v * ROW_BYTES;  // host-checked < 2^32
   const uint64_t head = (uint64_t)hs * d_v * DK;
   const uint32_t col = 16 * sub, col_io = 4 * IB * sub;
