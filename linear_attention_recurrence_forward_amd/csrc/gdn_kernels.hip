@@ -361,7 +361,7 @@ constexpr float kNormEps = 1e-6f;
 // values outside the token loop instead).
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
 __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(KernelArgs a) {
-  static_assert(NB >= 2, "a ring of two or more tokens");
+  static_assert(NB >= 4 && NB % 4 == 0, "a ring of a multiple of four tokens");
   constexpr bool NORMK = NK != 0;
   constexpr int L = DK / C;      // lanes sharing one state row
   constexpr int G = 64 / L;      // row groups per wave
@@ -729,9 +729,12 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     return c;
   };
 
-  // Factor table of the current 64-token chunk (see next_chunk below).
-  __shared__ float4 ab_lds[WAVES][64];
-  float4 *const ab = ab_lds[wave];
+  // Factor table of the current 64-token chunk (see next_chunk below): alpha,
+  // b, c and beta of its tokens, each in its own array, so that a ring group
+  // reads each factor of its NB tokens with NB / 4 16-byte reads.
+  __shared__ __attribute__((aligned(16))) float ab_lds[WAVES][4][64];
+  float *const fa = ab_lds[wave][0], *const fb = ab_lds[wave][1];
+  float *const fc = ab_lds[wave][2], *const fbeta = ab_lds[wave][3];
 
   // One token. With decay set (c = 1, b = beta): the cells are multiplied by
   // alpha, then sk, delta = (v - sk) * beta, the rank-1 write and y, as the
@@ -857,7 +860,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         // Token t0 + slot_t's c: from the factor table in a ring group (1
         // when the group ran eagerly); tokens after the last whole group run
         // with c = 1.
-        yk[0] = may_end ? w[0] : w[0] * ab[(t0 & 63u) + slot_t].z;
+        yk[0] = may_end ? w[0] : w[0] * fc[(t0 & 63u) + slot_t];
       }
       if (hold) {
         held = 1;
@@ -897,8 +900,9 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     };
 
     // Per-token factors of the current 64-token chunk live in a small
-    // per-wave LDS slot (ab), computed once per chunk (lane j: token t0 + j)
-    // and read per ring group as broadcasts: {alpha = exp(-g), b, c, beta}.
+    // per-wave LDS slot (fa, fb, fc, fbeta), computed once per chunk (lane j:
+    // token t0 + j) and read per ring group as broadcasts: alpha = exp(-g),
+    // b, c and beta.
     // In a ring group that runs lazily, c is the product of the alphas of the
     // group's tokens 1 .. u (1 at u = 0) and b = beta / c. A group runs
     // eagerly (every token decays; c = 1, b = beta) if any of its c or
@@ -917,15 +921,18 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       if ((t & 63u) == 0) {
         const float al = expf(-g_raw), be = b_raw;
         if constexpr (CAPTURE) {
-          ab[lane] = make_float4(al, be, 1.f, be);
+          fa[lane] = al;
+          fb[lane] = be;
+          fc[lane] = 1.f;
+          fbeta[lane] = be;
         } else {
-          ab[lane].x = al;
+          fa[lane] = al;
           __builtin_amdgcn_wave_barrier();
           const uint32_t q0 = lane & ~(NB - 1u), u = lane & (NB - 1u);
           float c = 1.f;
 #pragma unroll
           for (uint32_t i = 1; i < NB; ++i) {
-            const float ai = ab[q0 + i].x;
+            const float ai = fa[q0 + i];
             c = i <= u ? c * ai : c;
           }
           const float bc = be / c;
@@ -936,7 +943,9 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
           eager_mask =
               (uint64_t)uniform((uint32_t)(bad >> 32)) << 32 | uniform((uint32_t)bad);
           const bool eager = (eager_mask >> q0) & ((1ull << NB) - 1u);
-          ab[lane] = eager ? make_float4(al, be, 1.f, be) : make_float4(al, bc, c, be);
+          fb[lane] = eager ? be : bc;
+          fc[lane] = eager ? 1.f : c;
+          fbeta[lane] = be;
         }
         // After the last use of this chunk's raw values, so that the requests
         // can land in the same registers without a copy (and a wait).
@@ -946,8 +955,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     };
     auto run = [&](uint32_t t, uint32_t j, const KQ &kq, const float (&v)[NY]) {
       next_chunk(t);
-      const float4 f = ab[t & 63u];
-      step(t, j, true, kq, v, true, f.x, f.w, 1.f, true, false);
+      step(t, j, true, kq, v, true, fa[t & 63u], fbeta[t & 63u], 1.f, true, false);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -1020,9 +1028,20 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       // on its first token; the factors of the group's NB tokens are read
       // from LDS together, one wait per group.
       next_chunk(t);
-      float4 f[NB];
+      float fal[NB], fbl[NB], fcl[NB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) f[u] = ab[(t & 63u) + u];
+      for (int v4 = 0; v4 < NB / 4; ++v4) {
+        const uint32_t at = (t & 63u) + 4 * v4;
+        const f4 a4 = *reinterpret_cast<const f4 *>(fa + at);
+        const f4 b4 = *reinterpret_cast<const f4 *>(fb + at);
+        const f4 c4 = *reinterpret_cast<const f4 *>(fc + at);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          fal[4 * v4 + e] = a4[e];
+          fbl[4 * v4 + e] = b4[e];
+          fcl[4 * v4 + e] = c4[e];
+        }
+      }
       // Nonzero: the group runs eagerly. An integer, not a bool: a bool live
       // across the group's token branches is kept as a lane mask and turned
       // into a VGPR and back for every branch.
@@ -1095,7 +1114,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         }
         if constexpr (GNORM) cur.inv = invg[u];
         step(t, u % TB, false, cur, vu, u == 0 ? 1u : eager,
-             u == 0 ? kappa * f[u].x : f[u].x, f[u].y, f[u].z, false, SHARE && u == NB - 1);
+             u == 0 ? kappa * fal[u] : fal[u], fbl[u], fcl[u], false, SHARE && u == NB - 1);
         kq = nxt;
         ++t;
       }
@@ -1108,7 +1127,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         gb ^= 1;
         kq = columns_at(grp_lds[gb][0]);
       }
-      kappa = f[NB - 1].z;  // 1 after an eager group
+      kappa = fcl[NB - 1];  // 1 after an eager group
     }
     // Back to the plain state for the remaining tokens and the final store.
 #pragma unroll
