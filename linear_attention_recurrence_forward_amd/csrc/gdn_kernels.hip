@@ -73,6 +73,9 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm:[2,3,0,1]  lane ^ 2
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane -> 7 - lane (per 8)
 constexpr int kDppMirror = 0x140;     // row_mirror: lane -> 15 - lane (per 16)
 constexpr int kDppRor8 = 0x128;       // row_ror:8: lane -> lane ^ 8 (per 16)
+constexpr int kDppShr1 = 0x111;       // row_shr:1: lane - 1 (per 16)
+constexpr int kDppShr2 = 0x112;       // row_shr:2: lane - 2 (per 16)
+constexpr int kDppShr4 = 0x114;       // row_shr:4: lane - 4 (per 16)
 // ds_swizzle bit mode (offset bit 15 = 0): and_mask 0x1f, or_mask 0,
 // xor_mask 0x10 -> lane ^ 16 within each group of 32.
 constexpr int kSwizzleXor16 = 0x1F | (0x10 << 10);
@@ -927,13 +930,25 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
           fbeta[lane] = be;
         } else {
           fa[lane] = al;
-          __builtin_amdgcn_wave_barrier();
           const uint32_t q0 = lane & ~(NB - 1u), u = lane & (NB - 1u);
-          float c = 1.f;
-#pragma unroll
-          for (uint32_t i = 1; i < NB; ++i) {
-            const float ai = fa[q0 + i];
-            c = i <= u ? c * ai : c;
+          // c: the product of the alphas of the group's tokens 1 .. u, as an
+          // inclusive prefix product over the group's lanes (lane u holds 1
+          // at u = 0, its alpha otherwise; the step of span S multiplies in
+          // the partial product of the lane S below, which lies in the same
+          // NB-lane-aligned group when u >= S). Every lane reads its
+          // neighbour (the DPP moves stand outside the selects, so no lane
+          // reads from a disabled one).
+          static_assert(NB <= 8, "prefix product within a 16-lane DPP row");
+          float c = u == 0 ? 1.f : al;
+          const float p1 = dpp<kDppShr1>(c);
+          c = u >= 1 ? c * p1 : c;
+          if constexpr (NB >= 4) {
+            const float p2 = dpp<kDppShr2>(c);
+            c = u >= 2 ? c * p2 : c;
+          }
+          if constexpr (NB >= 8) {
+            const float p4 = dpp<kDppShr4>(c);
+            c = u >= 4 ? c * p4 : c;
           }
           const float bc = be / c;
           const bool lazy_ok = c >= 0x1p-63f && c <= 0x1p63f &&
