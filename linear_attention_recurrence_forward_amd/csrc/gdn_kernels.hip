@@ -754,8 +754,12 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
   // hold: a batch that this token ends is not stored here but by
   // store_held(), after the ring group's staging wait (see there).
   uint32_t held = 0, held_soff = 0;  // wave-uniform
+  // alpha_at: read the token's alpha from the factor table at index t & 63
+  // when it decays (a lazy group's tokens after its first do not decay, and
+  // then read nothing), instead of the alpha argument.
   auto step = [&](uint32_t t, uint32_t j, bool may_end, const KQ &kq, const float (&v)[NY],
-                  uint32_t decay, float alpha, float b, float c, bool raise, bool hold) {
+                  uint32_t decay, float alpha, bool alpha_at, float b, float c, bool raise,
+                  bool hold) {
     // The sk chain (decay, dot products, butterfly, delta) is what the rest
     // of the token, and the next token, wait for; the rank-1 write and y are
     // throughput work the other waves of the SIMD can interleave with. The
@@ -770,11 +774,13 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       cs = c * kq.inv;
       bs = b * kq.inv;
     }
-    if (decay != 0)
+    if (decay != 0) {
+      const float a = alpha_at ? fa[t & 63u] : alpha;
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int m = 0; m < NV; ++m) st[r][m] *= alpha;
+        for (int m = 0; m < NV; ++m) st[r][m] *= a;
+    }
     float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -970,7 +976,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     };
     auto run = [&](uint32_t t, uint32_t j, const KQ &kq, const float (&v)[NY]) {
       next_chunk(t);
-      step(t, j, true, kq, v, true, fa[t & 63u], fbeta[t & 63u], 1.f, true, false);
+      step(t, j, true, kq, v, true, fa[t & 63u], false, fbeta[t & 63u], 1.f, true, false);
     };
 
     // base_t moves in steps of 64 only if every group starts on a multiple
@@ -1043,16 +1049,17 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       // on its first token; the factors of the group's NB tokens are read
       // from LDS together, one wait per group.
       next_chunk(t);
-      float fal[NB], fbl[NB], fcl[NB];
+      // b and c of the group's tokens, and its first token's alpha (the
+      // others' are read only by tokens that decay, in an eager group).
+      const float alpha0 = fa[t & 63u];
+      float fbl[NB], fcl[NB];
 #pragma unroll
       for (int v4 = 0; v4 < NB / 4; ++v4) {
         const uint32_t at = (t & 63u) + 4 * v4;
-        const f4 a4 = *reinterpret_cast<const f4 *>(fa + at);
         const f4 b4 = *reinterpret_cast<const f4 *>(fb + at);
         const f4 c4 = *reinterpret_cast<const f4 *>(fc + at);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          fal[4 * v4 + e] = a4[e];
           fbl[4 * v4 + e] = b4[e];
           fcl[4 * v4 + e] = c4[e];
         }
@@ -1129,7 +1136,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
         }
         if constexpr (GNORM) cur.inv = invg[u];
         step(t, u % TB, false, cur, vu, u == 0 ? 1u : eager,
-             u == 0 ? kappa * fal[u] : fal[u], fbl[u], fcl[u], false, SHARE && u == NB - 1);
+             kappa * alpha0, u != 0, fbl[u], fcl[u], false, SHARE && u == NB - 1);
         kq = nxt;
         ++t;
       }
