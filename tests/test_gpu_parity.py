@@ -235,6 +235,52 @@ def test_random_shapes(case):
         assert_equal(got[2][:, -1], got[1], "capture[T-1] == state_out")
 
 
+def random_wide_shapes(n, seed):
+    """n shapes from a fixed seed over wider ranges than random_shapes: up to
+    32 key heads and 6 value heads per key head, D_v up to 160, T up to 200
+    (around the ring groups and the 64-token chunks), 1-3 sequences; every
+    third case has (value heads x sequences x row blocks of 32) >= 256, so it
+    takes the two-row multi-token kernel with shared staging at D_k = 64 and
+    128. g up to 3, keys scaled when normalised in the kernel. T is cut so
+    that no case asks the oracle for more than 2^29 cell updates."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        dk = int(rng.choice([32, 64, 128]))
+        if c % 3 == 0:
+            hk, ratio, dv, s = int(rng.choice([16, 32])), int(rng.choice([3, 4, 6])), \
+                int(rng.choice([96, 128, 160])), int(rng.integers(1, 3))
+        else:
+            hk, ratio, dv, s = int(rng.choice([1, 2, 4, 8, 16])), int(rng.choice([1, 2, 3, 4])), \
+                int(rng.choice([8, 17, 32, 40, 64, 72, 96, 128, 160])), int(rng.integers(1, 4))
+        t = int(rng.choice([1, 2, 3, 5, 8, 9, 16, 17, 33, 63, 64, 65, 100, 129, 200]))
+        while t > 1 and s * t * hk * ratio * dv * dk > 1 << 29:
+            t = max(1, t // 2 + 1) if t > 2 else 1
+        out.append(dict(shape=(dk, dv, hk, hk * ratio, t, s),
+                        g_high=float(rng.choice([0.05, 0.5, 1.0, 3.0])),
+                        capture=bool(rng.random() < 0.3), fold=bool(rng.random() < 0.5),
+                        normalize_k=bool(rng.random() < 0.25),
+                        k_scale=float(rng.uniform(0.5, 3.0))))
+    return out
+
+
+@pytest.mark.parametrize("case", random_wide_shapes(48, 2027),
+                         ids=lambda c: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % c["shape"])
+def test_random_wide_shapes(case):
+    """Wider shapes drawn once from a fixed seed, against the oracle on every
+    element."""
+    dk, dv, hk, hv, t, s = case["shape"]
+    w = Workload("wide", 0, dk, dv, hk, hv, t, s, g_high=case["g_high"])
+    x = make_inputs(w, seed=sum(case["shape"]) + 7)
+    if case["normalize_k"]:
+        x["k"] = (x["k"] * np.float32(case["k_scale"])).astype(np.float32)
+    bits = q_scale_bits_for(dk) if case["fold"] else 0
+    got = run(x, q_scale_bits=bits, capture=case["capture"], normalize_k=case["normalize_k"])
+    exp = ref(x, q_scale_bits=bits, capture=case["capture"], normalize_k=case["normalize_k"])
+    for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
+        close(g_, e, f"{case} {what}")
+
+
 @pytest.mark.parametrize("shape", [
     (32, 1, 1, 1, 1, 70000),      # sequences past one launch's 65535
     (32, 1, 1, 65540, 1, 1),      # value heads past 65535 (GQA ratio 65540)
