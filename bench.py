@@ -26,9 +26,11 @@ cost cancels, and the figure does not depend on K.
 Prints one JSON line. The single-layer decode line (the default) also carries
 one object per other workload of the headline metric: "prefill" (512-token
 prefill, tokens/s), "batched_decode", "spec_verify" and "rollback", each with
-its own roofline and CPU baseline, and "state_copy", the library's copy kernel
+its own roofline and CPU baseline, "state_copy", the library's copy kernel
 moving exactly the decode call's state bytes, measured the same way: the floor
-beside the decode figure (--no-extra leaves them out). Every CPU
+beside the decode figure, and "tiny", the smallest configuration (D_k = D_v =
+32, 8 tokens, 2 value heads), whose call is all launch and latency
+(--no-extra leaves them out). Every CPU
 baseline times the oracle on one core and on all the host's cores (threads
 over the independent (sequence, value head) pairs) and names the CPU.
 """
@@ -62,7 +64,7 @@ NAMES = ("q", "k", "v", "g", "beta", "state_in")
 # timed region covers tens of milliseconds of GPU work whatever --steps is
 # (the 512-token prefill needs a longer warm-up to reach its loaded clock).
 EXTRA = (("prefill", 500, 200), ("batched_decode", 500, 50), ("spec_verify", 2000, 200),
-         ("rollback", 2000, 200), ("state_copy", 2000, 200))
+         ("rollback", 2000, 200), ("state_copy", 2000, 200), ("tiny", 2000, 200))
 MAX_WORKER_THREADS = 16  # the host CPU share of one GPU on the GPU machines
 
 
@@ -278,7 +280,7 @@ def summarize_default_trace(src: str, command: str, out_dir: str | None = None) 
             if ln.startswith("{"):
                 line = json.loads(ln)
     lines = ["# All kernels of the default bench line (decode, prefill, batched decode, "
-             "spec verify, rollback)", "",
+             "spec verify, rollback, state copy, tiny)", "",
              f"kernel digest (sha256 of sources + flags) of the profiled build: "
              f"`{line['kernel_digest']}`", "", "```", command, "```", "",
              "| kernel | calls | average µs | median µs | min µs | share % |",
@@ -294,7 +296,7 @@ def summarize_default_trace(src: str, command: str, out_dir: str | None = None) 
     lines += ["", "Per-launch kernel time reported by the same (profiled) run's bench line:", "",
               "| workload | kernel_us under the profiler |", "|---|---|",
               f"| decode | {line['kernel_us']:.3f} |"]
-    for k in ("prefill", "batched_decode", "spec_verify", "rollback", "state_copy"):
+    for k in ("prefill", "batched_decode", "spec_verify", "rollback", "state_copy", "tiny"):
         if k in line:
             lines.append(f"| {k} | {line[k]['kernel_us']:.3f} |")
     lines.append("")
