@@ -1059,14 +1059,18 @@ def test_one_token_arrays_more_than_4gib_apart(shape):
 
 @pytest.mark.parametrize("capture", [False, True], ids=["plain", "capture"])
 @pytest.mark.parametrize("shape", [
+    (32, 2047, 1, 1, 1, 1),     # the size word's largest d_v
     (32, 2100, 1, 1, 1, 1),     # d_v past 2047
     (128, 2050, 1, 2, 1, 1),
+    (32, 3, 1023, 1023, 1, 2),  # its largest key-head count
     (32, 3, 1030, 1030, 1, 2),  # more than 1023 key heads
+    (32, 2, 1, 127, 1, 2),      # its largest value-head count per key head
     (32, 2, 1, 130, 1, 2),      # more than 127 value heads per key head
 ], ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
 def test_one_token_sizes_past_the_size_word(shape, capture):
-    """One-token calls whose sizes do not fit the one-token kernel's 32-bit
-    size word take the kernel with full-width sizes: against the oracle."""
+    """One-token calls at the largest sizes the one-token kernel's 32-bit size
+    word holds, and past them (those take the kernel with full-width sizes):
+    against the oracle."""
     dk, dv, hk, hv, t, s_ = shape
     x = make_inputs(Workload("wide", 0, dk, dv, hk, hv, t, s_, fold_q_scale=True),
                     seed=101 + dv)
