@@ -330,22 +330,20 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (lane_value(0) + lane_value(16)) + (lane_value(32) + lane_value(48));
 }
 
+// The multi-token kernel's arguments that its workgroup-index split and its
+// state loads do not need; those come first, as scalar parameters, so that
+// they are among the 13 kernel-argument dwords the dispatch preloads into
+// scalar registers (a by-value struct is not preloaded), and the split and
+// the state requests wait for no kernel-argument memory.
 struct KernelArgs {
   const void *q, *k, *v;  // IO type
-  const float *g, *beta, *state_in;
+  const float *g, *beta;
   void *output;           // IO type
   float *state_out, *capture;
-  uint32_t d_v, n_k_heads, n_v_heads, n_tokens;
-  uint32_t row_blocks;  // workgroups per (sequence, value head)
   float q_scale;
   // Descriptor sizes of the k/q and v rows of a whole sequence (the first
   // rebase), the same for every workgroup.
   uint32_t kq_ext0, v_ext0;
-  // Value heads per key head, and host-computed reciprocals for the
-  // workgroup index split: x / d == (x * magic) >> shift for every x < 2^24
-  // (the grid size), d = row_blocks, groups, n_k_heads; shifts holds the
-  // three shifts in bits 0-7, 8-15 and 16-23.
-  uint32_t groups, rb_magic, g_magic, kh_magic, shifts;
 };
 
 // Epsilon of the key-normalisation option (binary32 value of 1e-6).
@@ -362,8 +360,18 @@ constexpr float kNormEps = 1e-6f;
 // the next group's key rows would otherwise take the D_k = 128 instance one
 // register past the 168 that 3 waves allow (the compiler then spills two
 // values outside the token loop instead).
+// Leading parameters (preloaded): the state base; d_v, n_k_heads, n_v_heads,
+// n_tokens; row_blocks (workgroups per (sequence, value head)) and groups
+// (value heads per key head) with host-computed reciprocals for the
+// workgroup index split, x / d == (x * magic) >> shift for every x < 2^24
+// (the grid size), d = row_blocks, groups, n_k_heads, the three shifts in
+// bits 0-7, 8-15 and 16-23 of shifts; and n_blocks, the grid size (the
+// grid's own size lives in kernel-argument memory).
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
-__global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(KernelArgs a) {
+__global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
+    const float *state_in, uint32_t d_v, uint32_t n_k_heads, uint32_t n_v_heads,
+    uint32_t n_tokens, uint32_t row_blocks, uint32_t groups, uint32_t rb_magic,
+    uint32_t g_magic, uint32_t kh_magic, uint32_t shifts, uint32_t n_blocks, KernelArgs a) {
   static_assert(NB >= 4 && NB % 4 == 0, "a ring of a multiple of four tokens");
   constexpr bool NORMK = NK != 0;
   constexpr int L = DK / C;      // lanes sharing one state row
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
   // then fetched into one L2 instead of several.
   uint32_t s, vh, rb, kh;
   {
-    const uint32_t n = gridDim.x, xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
+    const uint32_t n = n_blocks, xcd = blockIdx.x % 8u, local = blockIdx.x / 8u;
     const uint32_t per = n / 8u, extra = n % 8u;
     const uint32_t bid = xcd * per + (xcd < extra ? xcd : extra) + local;
     // bid = ((s * n_k_heads + kh) * groups + g) * row_blocks + rb, split by
@@ -400,23 +408,23 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
       return q;
     };
     uint32_t g, khead;
-    uint32_t rest = divmod(bid, a.row_blocks, a.rb_magic, a.shifts & 0xFFu, rb);
-    rest = divmod(rest, a.groups, a.g_magic, (a.shifts >> 8) & 0xFFu, g);
-    s = divmod(rest, a.n_k_heads, a.kh_magic, a.shifts >> 16, khead);
-    vh = khead + g * a.n_k_heads;
+    uint32_t rest = divmod(bid, row_blocks, rb_magic, shifts & 0xFFu, rb);
+    rest = divmod(rest, groups, g_magic, (shifts >> 8) & 0xFFu, g);
+    s = divmod(rest, n_k_heads, kh_magic, shifts >> 16, khead);
+    vh = khead + g * n_k_heads;
     kh = khead;  // vh % n_k_heads
   }
   // s * n_v_heads + vh is below the grid size (host-checked < 2^24).
-  const uint32_t hs = s * a.n_v_heads + vh;
+  const uint32_t hs = s * n_v_heads + vh;
 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t grp = lane / L;
   const uint32_t sub = lane % L;
 
-  const uint32_t Dv = a.d_v;
-  const uint32_t T = a.n_tokens;
-  const uint64_t Hv = a.n_v_heads, Hk = a.n_k_heads;
+  const uint32_t Dv = d_v;
+  const uint32_t T = n_tokens;
+  const uint64_t Hv = n_v_heads, Hk = n_k_heads;
 
   // This lane's rows. Rows past D_v compute on a clamped (valid) row and
   // store nothing; all lanes stay active for the cross-lane sums. The high
@@ -431,6 +439,24 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     ok[r] = i < Dv;
     row[r] = ok[r] ? i : Dv - 1;
   }
+
+  // The state rows first: their requests need only preloaded arguments, and
+  // the scheduling barrier keeps every read of kernel-argument memory (the
+  // other arrays' bases) behind them. Per-lane byte offsets, fixed for the
+  // whole call: vector m of row r starts at column m*4L + 4*sub (state: 16
+  // bytes per vector; k/q: 4*IB bytes).
+  const uint32_t head_bytes = Dv * ROW_BYTES;
+  const rsrc_t s_in = buffer(state_in + (uint64_t)hs * Dv * DK, head_bytes);
+  const uint32_t col = 16 * sub;
+  uint32_t cell[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) cell[r] = row[r] * ROW_BYTES + col;
+  f4 st[R][NV];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NV; ++m) st[r][m] = load4_stream(s_in, cell[r] + m * 16 * L);
+  __builtin_amdgcn_sched_barrier(0);
 
   // Wave-uniform bases of this (s, vh): token-0 addresses and per-token
   // strides, in elements. The k/q/v descriptors start at a token's row and
@@ -448,16 +474,8 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
   const float *b_tok = a.beta + tok0 * Hv + vh;
   float *c_tok = CAPTURE ? a.capture + (tok0 * Hv + vh) * (uint64_t)Dv * DK : nullptr;
   const uint64_t cap_step = Hv * Dv * DK;
-  const uint32_t head_bytes = Dv * ROW_BYTES;
-  const rsrc_t s_in = buffer(a.state_in + (uint64_t)hs * Dv * DK, head_bytes);
   const rsrc_t s_out = buffer(a.state_out + (uint64_t)hs * Dv * DK, head_bytes);
 
-  // Per-lane byte offsets, fixed for the whole call: vector m of row r starts
-  // at column m*4L + 4*sub (state: 16 bytes per vector; k/q: 4*IB bytes).
-  const uint32_t col = 16 * sub;
-  uint32_t cell[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) cell[r] = row[r] * ROW_BYTES + col;
   uint32_t vrow[NY];
 #pragma unroll
   for (int r = 0; r < NY; ++r) vrow[r] = row[r] * IB;
@@ -491,11 +509,6 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(Ker
     yoff[r] = vrow[r] + slot_t * (uint32_t)(Hv * Dv * IB);
   }
 
-  f4 st[R][NV];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < NV; ++m) st[r][m] = load4_stream(s_in, cell[r] + m * 16 * L);
   // Register element e of a cell vector holds column (e + ROT) % 4 of its four
   // columns. The k/q column vectors arrive in aligned register quads, as the
   // state does, so with ROT = 0 every multiply-add would read cell and key (or
@@ -1657,15 +1670,9 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   a.v = f.v;
   a.g = f.g;
   a.beta = f.beta;
-  a.state_in = f.state_in;
   a.output = f.output;
   a.state_out = f.state_out;
   a.capture = f.capture;
-  a.d_v = f.d_v;
-  a.n_k_heads = f.n_k_heads;
-  a.n_v_heads = f.n_v_heads;
-  a.n_tokens = f.n_tokens;
-  a.row_blocks = row_blocks;
   a.q_scale = f.q_scale;
   const uint64_t kq_row = (uint64_t)f.n_k_heads * f.d_k, v_row = (uint64_t)f.n_v_heads * f.d_v;
   const uint64_t last = f.n_tokens - 1u;
@@ -1677,16 +1684,21 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   // ceil(2^shift / d) <= 2^25, exact because x * (magic * d - 2^shift) <
   // 2^24 * d <= 2^shift.
   if (blocks >= (uint64_t(1) << 24)) return hipErrorInvalidValue;
-  a.groups = f.n_v_heads / f.n_k_heads;
   auto recip = [](uint32_t d, uint32_t &magic) {
     const uint32_t shift = 24 + ceil_log2(d);
     magic = (uint32_t)(((uint64_t(1) << shift) + d - 1) / d);
     return shift;
   };
-  a.shifts = recip(row_blocks, a.rb_magic) | recip(a.groups, a.g_magic) << 8 |
-             recip(f.n_k_heads, a.kh_magic) << 16;
-  void *args[] = {&a};
-  return hipLaunchKernel(geo.kernel, dim3((uint32_t)blocks), dim3(geo.threads), args, 0, stream);
+  const float *state_in = f.state_in;
+  uint32_t d_v = f.d_v, n_k = f.n_k_heads, n_v = f.n_v_heads, n_tok = f.n_tokens;
+  uint32_t rbs = row_blocks, groups = f.n_v_heads / f.n_k_heads;
+  uint32_t rb_magic, g_magic, kh_magic;
+  uint32_t shifts = recip(row_blocks, rb_magic) | recip(groups, g_magic) << 8 |
+                    recip(f.n_k_heads, kh_magic) << 16;
+  uint32_t n_blocks = (uint32_t)blocks;
+  void *args[] = {&state_in, &d_v,     &n_k,      &n_v,    &n_tok,    &rbs,      &groups,
+                  &rb_magic, &g_magic, &kh_magic, &shifts, &n_blocks, &a};
+  return hipLaunchKernel(geo.kernel, dim3(n_blocks), dim3(geo.threads), args, 0, stream);
 }
 
 }  // namespace gdn
