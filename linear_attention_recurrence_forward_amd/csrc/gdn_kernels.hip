@@ -1267,9 +1267,18 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
     row[r] = ok[r] ? i : d_v - 1;
   }
 
-  // The loads, all addressed from preloaded arguments in gdn_decode: state
-  // rows, this lane's k columns, g, v, beta, then the q columns.
-  const uint32_t head_bytes = d_v * ROW_BYTES;  // host-checked < 2^32
+  // The loads, all addressed from preloaded arguments in gdn_decode: g,
+  // beta and v first, then the state rows and this lane's k and q columns.
+  // Vector-memory loads complete in the order issued, so the decay factor
+  // is computed while the state is still arriving instead of after it.
+  const float g = load1(buffer(p.g + hs, 4), 0);
+  const float beta = load1(buffer(p.beta + hs, 4), 0);
+  const rsrc_t v_rs = buffer(static_cast<const char *>(p.v) + (uint64_t)hs * d_v * IB, d_v * IB);
+  float v[NY];
+#pragma unroll
+  for (int r = 0; r < NY; ++r) v[r] = Io<IO>::load1(v_rs, row[r] * IB, 0);
+  // head_bytes: host-checked < 2^32, and a multiple of ROW_BYTES.
+  const uint32_t head_bytes = d_v * ROW_BYTES;
   const uint64_t head = (uint64_t)hs * d_v * DK;
   const uint32_t col = 16 * sub, col_io = 4 * IB * sub;
   uint32_t cell[R];
@@ -1286,21 +1295,16 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
   f4 kc[NV], qc[NV];
 #pragma unroll
   for (int m = 0; m < NV; ++m) kc[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, 0);
-  const float g = load1(buffer(p.g + hs, 4), 0);
-
-  const rsrc_t v_rs = buffer(static_cast<const char *>(p.v) + (uint64_t)hs * d_v * IB, d_v * IB);
-  float v[NY];
-#pragma unroll
-  for (int r = 0; r < NY; ++r) v[r] = Io<IO>::load1(v_rs, row[r] * IB, 0);
-  const float beta = load1(buffer(p.beta + hs, 4), 0);
   const rsrc_t q_rs = buffer(static_cast<const char *>(p.q) + kq, DK * IB);
 #pragma unroll
   for (int m = 0; m < NV; ++m) qc[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, 0);
-  // Then the arguments that may come from kernel-argument memory (the store
-  // addresses and q_scale): requested here, after every load, and waited
-  // for once (the empty asm takes them as operands, so that no read is
-  // left for its first use, after the arithmetic).
   __builtin_amdgcn_sched_barrier(0);
+  const float alpha = expf(-g);
+  __builtin_amdgcn_sched_barrier(0);
+  // Then the arguments that may come from kernel-argument memory (the store
+  // addresses and q_scale): requested here, and waited for once (the empty
+  // asm takes them as operands, so that no read is left for its first use,
+  // after the arithmetic).
   void *const out = p.output;
   float *const s_out_p = p.state_out, *const cap_p = p.capture;
   const float qsc = q_scale;
@@ -1317,7 +1321,6 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
       for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kc[m][e], kc[m][e], ss);
     inv = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
   }
-  const float alpha = expf(-g);
   const float bs = beta * inv;
 
   // The step as written: decay, sk, delta = (v - sk) * beta, the rank-1
@@ -1344,47 +1347,52 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
     for (int r = 0; r < R; ++r) d[r] = __builtin_fmaf(-inv, group_sum<L>(part[r]), v[r]) * bs;
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    part[r] = 0.f;
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < NV; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        st[r][m][e] = __builtin_fmaf(d[r], kc[m][e], st[r][m][e]);
-        part[r] = __builtin_fmaf(st[r][m][e], qc[m][e], part[r]);
-      }
-  }
+      for (int e = 0; e < 4; ++e) st[r][m][e] = __builtin_fmaf(d[r], kc[m][e], st[r][m][e]);
 
   // The state (and the capture slice, the state after the token) is stored
-  // before y's cross-lane sum: the call ends when its last store completes
-  // and the stores keep program order, so the state's writes run under that
-  // sum instead of after it. y's lane partials come first, so the wait for
-  // the q columns precedes every store (the vector memory counter counts
-  // stores too). An empty asm with each partial as an operand keeps the
-  // compiler from sinking their arithmetic below the stores.
+  // before y is formed: the call ends when its last store completes, so the
+  // state's writes run under y's arithmetic instead of after it. The stores
+  // are unconditional: a row past d_v gets the offset head_bytes, outside
+  // the descriptor's range, and the hardware drops it (no wrap-around: the
+  // largest immediate offset added, (NV - 1) * 16 * L, is below ROW_BYTES,
+  // and head_bytes <= 2^32 - ROW_BYTES). A branch around them would make
+  // the compiler wait for their completion before the loads y needs.
+  uint32_t sc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) asm volatile("" : "+v"(part[r]));
+  for (int r = 0; r < R; ++r) sc[r] = ok[r] ? cell[r] : head_bytes;
   if constexpr (CAPTURE) {
     const rsrc_t ct = buffer(cap_p + head, head_bytes);
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (ok[r])
 #pragma unroll
-        for (int m = 0; m < NV; ++m) store4_stream(ct, cell[r] + m * 16 * L, st[r][m]);
+      for (int m = 0; m < NV; ++m) store4_stream(ct, sc[r] + m * 16 * L, st[r][m]);
   }
   const rsrc_t s_out = buffer(s_out_p + head, head_bytes);
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (ok[r])
 #pragma unroll
-      for (int m = 0; m < NV; ++m) store4_stream(s_out, cell[r] + m * 16 * L, st[r][m]);
+    for (int m = 0; m < NV; ++m) store4_stream(s_out, sc[r] + m * 16 * L, st[r][m]);
+  __builtin_amdgcn_sched_barrier(0);
 
+  float part_y[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    part_y[r] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part_y[r] = __builtin_fmaf(st[r][m][e], qc[m][e], part_y[r]);
+  }
   float y[NY];
   if constexpr (PAIRED) {
-    y[0] = pair_sum<L>(part[0], part[1]);
+    y[0] = pair_sum<L>(part_y[0], part_y[1]);
   } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) y[r] = group_sum<L>(part[r]);
+    for (int r = 0; r < R; ++r) y[r] = group_sum<L>(part_y[r]);
   }
   // Lane 0 of each set of TB lanes writes its rows' outputs, q_scale applied.
   const rsrc_t o_rs =
