@@ -236,9 +236,21 @@ typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 template <typename IO>
 struct Io;
 
+// raw4/raw1 request the bytes and widen4/widen1 turn them into f32, so that
+// a caller can issue every request before any widening waits for its data.
 template <>
 struct Io<float> {
   static constexpr uint32_t bytes = 4;
+  typedef f4 R4;
+  typedef float R1;
+  static __device__ __forceinline__ R4 raw4(rsrc_t r, uint32_t off, uint32_t soff) {
+    return ::gdn::load4(r, off, soff);
+  }
+  static __device__ __forceinline__ f4 widen4(R4 x) { return x; }
+  static __device__ __forceinline__ R1 raw1(rsrc_t r, uint32_t off, uint32_t soff) {
+    return ::gdn::load1(r, off, soff);
+  }
+  static __device__ __forceinline__ float widen1(R1 x) { return x; }
   static __device__ __forceinline__ f4 load4(rsrc_t r, uint32_t off, uint32_t soff) {
     return ::gdn::load4(r, off, soff);
   }
@@ -257,15 +269,26 @@ struct Io<__bf16> {
   static __device__ __forceinline__ float widen(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
   }
-  static __device__ __forceinline__ f4 load4(rsrc_t r, uint32_t off, uint32_t soff) {
-    const u2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  typedef u2 R4;
+  typedef uint32_t R1;
+  static __device__ __forceinline__ R4 raw4(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  }
+  static __device__ __forceinline__ f4 widen4(R4 w) {
     return f4{__builtin_bit_cast(float, w.x << 16),
               __builtin_bit_cast(float, w.x & 0xFFFF0000u),
               __builtin_bit_cast(float, w.y << 16),
               __builtin_bit_cast(float, w.y & 0xFFFF0000u)};
   }
+  static __device__ __forceinline__ R1 raw1(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+  }
+  static __device__ __forceinline__ float widen1(R1 x) { return widen(x); }
+  static __device__ __forceinline__ f4 load4(rsrc_t r, uint32_t off, uint32_t soff) {
+    return widen4(raw4(r, off, soff));
+  }
   static __device__ __forceinline__ float load1(rsrc_t r, uint32_t off, uint32_t soff) {
-    return widen(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
+    return widen1(raw1(r, off, soff));
   }
   static __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, uint32_t soff,
                                                 float x) {
@@ -1274,9 +1297,9 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
   const float g = load1(buffer(p.g + hs, 4), 0);
   const float beta = load1(buffer(p.beta + hs, 4), 0);
   const rsrc_t v_rs = buffer(static_cast<const char *>(p.v) + (uint64_t)hs * d_v * IB, d_v * IB);
-  float v[NY];
+  typename Io<IO>::R1 v_raw[NY];
 #pragma unroll
-  for (int r = 0; r < NY; ++r) v[r] = Io<IO>::load1(v_rs, row[r] * IB, 0);
+  for (int r = 0; r < NY; ++r) v_raw[r] = Io<IO>::raw1(v_rs, row[r] * IB, 0);
   // head_bytes: host-checked < 2^32, and a multiple of ROW_BYTES.
   const uint32_t head_bytes = d_v * ROW_BYTES;
   const uint64_t head = (uint64_t)hs * d_v * DK;
@@ -1290,17 +1313,28 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < NV; ++m) st[r][m] = load4_stream(s_in, cell[r] + m * 16 * L);
+  // (Kept ahead of the k and q requests, which the scheduler would otherwise
+  // hoist above them.) Every value is requested as raw bytes and widened
+  // (bf16 I/O) only after the decay factor: a widening placed among the
+  // requests would wait for its data before issuing the rest.
+  __builtin_amdgcn_sched_barrier(0);
   const uint64_t kq = ((uint64_t)s * n_k_heads + kh) * DK * IB;
   const rsrc_t k_rs = buffer(static_cast<const char *>(p.k) + kq, DK * IB);
-  f4 kc[NV], qc[NV];
+  typename Io<IO>::R4 k_raw[NV], q_raw[NV];
 #pragma unroll
-  for (int m = 0; m < NV; ++m) kc[m] = Io<IO>::load4(k_rs, col_io + m * 4 * IB * L, 0);
+  for (int m = 0; m < NV; ++m) k_raw[m] = Io<IO>::raw4(k_rs, col_io + m * 4 * IB * L, 0);
   const rsrc_t q_rs = buffer(static_cast<const char *>(p.q) + kq, DK * IB);
 #pragma unroll
-  for (int m = 0; m < NV; ++m) qc[m] = Io<IO>::load4(q_rs, col_io + m * 4 * IB * L, 0);
+  for (int m = 0; m < NV; ++m) q_raw[m] = Io<IO>::raw4(q_rs, col_io + m * 4 * IB * L, 0);
   __builtin_amdgcn_sched_barrier(0);
   const float alpha = expf(-g);
   __builtin_amdgcn_sched_barrier(0);
+  f4 kc[NV];
+  float v[NY];
+#pragma unroll
+  for (int m = 0; m < NV; ++m) kc[m] = Io<IO>::widen4(k_raw[m]);
+#pragma unroll
+  for (int r = 0; r < NY; ++r) v[r] = Io<IO>::widen1(v_raw[r]);
   // Then the arguments that may come from kernel-argument memory (the store
   // addresses and q_scale): requested here, and waited for once (the empty
   // asm takes them as operands, so that no read is left for its first use,
@@ -1378,6 +1412,9 @@ __device__ __forceinline__ void decode_token(const DecodePtrs &p, uint32_t d_v,
     for (int m = 0; m < NV; ++m) store4_stream(s_out, sc[r] + m * 16 * L, st[r][m]);
   __builtin_amdgcn_sched_barrier(0);
 
+  f4 qc[NV];
+#pragma unroll
+  for (int m = 0; m < NV; ++m) qc[m] = Io<IO>::widen4(q_raw[m]);
   float part_y[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
