@@ -59,6 +59,7 @@ RESIDENT_TARGET_BYTES = 1 << 30  # input sets cycled per run: >= 4x the cache
 METRIC = "GDN decode µs/layer + state HBM GB/s (%peak); prefill tokens/s at n_tokens=512"
 KERNEL_NAME = "gdn_recurrent"      # multi-token forward calls
 DECODE_KERNEL_NAME = "gdn_decode"  # one-token forward calls
+SHORT_KERNEL_NAME = "gdn_short"    # 2 to 8 tokens at D_k = 128
 NAMES = ("q", "k", "v", "g", "beta", "state_in")
 # The headline line's other workloads: (name, timed steps, warm-up steps). Each
 # timed region covers tens of milliseconds of GPU work whatever --steps is
@@ -177,7 +178,12 @@ def workload_info(name: str, io: str = "f32"):
         return (w, "gdn_rollback_kernel", w.state_bytes() + 4 * w.n_seqs,
                 "state copy (rollback kernel, index 0) on the " + w.description)
     w = WORKLOADS[name]
-    kernel = DECODE_KERNEL_NAME if w.n_tokens == 1 else KERNEL_NAME
+    if w.n_tokens == 1:
+        kernel = DECODE_KERNEL_NAME
+    elif w.n_tokens <= 8 and w.d_k == 128:
+        kernel = SHORT_KERNEL_NAME
+    else:
+        kernel = KERNEL_NAME
     if io == "bf16":
         return (w, kernel, w.algorithmic_bytes(io_bytes=2),
                 w.description + ", bf16 q/k/v/output")

@@ -167,7 +167,7 @@ gdn_status gdn_check_params(const gdn_params *p) {
   // threads per block (at most 256) must stay below 2^32 work-items, for
   // either kernel, with or without capture.
   for (bool cap : {false, true}) {
-    const uint64_t blocks = gdn::grid_blocks(p->d_k, p->d_v, p->n_v_heads,
+    const uint64_t blocks = gdn::grid_blocks(p->d_k, p->d_v, p->n_k_heads, p->n_v_heads,
                                              p->n_seqs, p->n_tokens, cap);
     if (blocks >= (uint64_t(1) << 32) / 256u) return GDN_ERR_SIZE_OVERFLOW;
   }

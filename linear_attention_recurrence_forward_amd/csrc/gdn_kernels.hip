@@ -1504,6 +1504,199 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_decode_wide(
                                                  kh, rb, a.q_scale);
 }
 
+// Sizes of a short multi-token launch in one 32-bit word: d_v in bits 0-10,
+// rb_shift in 11-14, n_k_heads in 15-21, n_v_heads / n_k_heads in 22-28,
+// n_tokens - 1 in 29-31.
+constexpr uint32_t kShortNk = 7, kShortGroups = 7, kShortTok = 3;
+
+// Short multi-token calls (2 <= n_tokens <= NT, D_k = 128; speculative
+// verification): the one-token kernel's layout (grid, preloaded arguments,
+// L lanes per row, one row per lane, straight-line code) extended to NT
+// tokens. Every input is requested before the token loop, in the order it
+// is needed: g and beta (lane t holds token t's), each token's k and q rows
+// (requested once per workgroup, 8 or 4 bytes a lane, the rows spread over
+// the waves, and parked in LDS, from which each lane reads its columns), v,
+// then the state rows last, whose HBM round trip covers the rest; the decay factors
+// are one exp over the lanes and are read back as wave-uniform values. The
+// loop then runs the tokens with nothing to wait for: decay, sk, delta, the
+// rank-1 write, the capture slice (CAPTURE), y. Tokens past n_tokens (up to
+// NT) request clamped, valid addresses and are skipped.
+template <int DK, int C, int WAVES, int NT, bool CAPTURE, typename IO, int NK>
+__global__ __launch_bounds__(WAVES * 64) void gdn_short(
+    const float *state_in, const void *k_in, const void *q_in, const float *g_in,
+    const void *v_in, const float *beta_in, uint32_t sizes, DecodeTail a) {
+  constexpr bool NORMK = NK != 0;
+  constexpr int L = DK / C;  // lanes per row
+  constexpr int G = 64 / L;  // rows per wave
+  constexpr int NV = C / 4;  // float4 per lane and row
+  constexpr uint32_t ROWS = WAVES * G;
+  constexpr uint32_t ROW_BYTES = DK * 4;
+  constexpr uint32_t IB = Io<IO>::bytes;
+  constexpr uint32_t KQ_BYTES = DK * IB;  // one k or q row
+  constexpr uint32_t RB = KQ_BYTES / 64;  // its bytes per lane
+  constexpr uint32_t EPL = RB / IB;       // its elements per lane
+  static_assert(DK == 128 && EPL == 2, "k/q rows of 128 elements, two per lane");
+  static_assert(NT >= 2 && NT <= 8, "2 to 8 tokens");
+  static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
+  // Token t's k row is row 2t of the slot, its q row 2t + 1; wave w requests
+  // rows w, w + WAVES, ... and parks them for the whole workgroup.
+  __shared__ __attribute__((aligned(16))) float kq_lds[NT][2][DK];
+  constexpr int RPW = (2 * NT + WAVES - 1) / WAVES;  // rows per wave
+
+  const uint32_t d_v = sizes & ((1u << kPackDv) - 1u);
+  const uint32_t rb_shift = (sizes >> kPackDv) & ((1u << kPackRb) - 1u);
+  const uint32_t n_k = (sizes >> (kPackDv + kPackRb)) & ((1u << kShortNk) - 1u);
+  const uint32_t groups = (sizes >> (kPackDv + kPackRb + kShortNk)) & ((1u << kShortGroups) - 1u);
+  const uint32_t n_tok = (sizes >> (kPackDv + kPackRb + kShortNk + kShortGroups)) + 1u;
+  const uint32_t n_v = groups * n_k;
+  const uint32_t rb = blockIdx.x & ((1u << rb_shift) - 1u);
+  const uint32_t kh = blockIdx.x >> rb_shift;
+  const uint32_t vh = kh + n_k * blockIdx.y;
+  const uint32_t s = blockIdx.z;
+  if (rb * ROWS >= d_v) return;  // padding of the row blocks: the whole workgroup
+
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t grp = lane / L;
+  const uint32_t sub = lane % L;
+  const uint32_t i = rb * ROWS + wave * G + grp;
+  const bool ok = i < d_v;
+  const uint32_t row = ok ? i : d_v - 1;  // rows past d_v compute on a valid row
+  const uint64_t tok0 = (uint64_t)s * n_tok;  // (s, token 0) in token-major order
+  auto tclamp = [&](uint32_t t) { return t < n_tok ? t : n_tok - 1; };
+
+  // g and beta: lane t requests token t's (clamped).
+  const uint32_t gb_step = n_v * 4;
+  const uint32_t gb_ext = (n_tok - 1) * gb_step + 4;
+  const uint32_t tl = tclamp(lane);
+  const float g_l = load1(buffer(g_in + tok0 * n_v + vh, gb_ext), tl * gb_step);
+  const float b_l = load1(buffer(beta_in + tok0 * n_v + vh, gb_ext), tl * gb_step);
+  // k and q rows: lane l holds elements 2l and 2l + 1 of each.
+  const uint32_t kq_step = n_k * KQ_BYTES;
+  const uint32_t kq_ext = (n_tok - 1) * kq_step + KQ_BYTES;
+  const uint64_t kq0 = (tok0 * n_k + kh) * KQ_BYTES;
+  const rsrc_t k_rs = buffer(static_cast<const char *>(k_in) + kq0, kq_ext);
+  const rsrc_t q_rs = buffer(static_cast<const char *>(q_in) + kq0, kq_ext);
+  typename Raw<RB>::T kr[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const uint32_t r = wave + j * WAVES;
+    const uint32_t rr = r < 2 * NT ? r : 2 * NT - 1;
+    const uint32_t off = uniform(tclamp(rr / 2) * kq_step);
+    kr[j] = (rr & 1) ? Raw<RB>::load(q_rs, lane * RB, off) : Raw<RB>::load(k_rs, lane * RB, off);
+  }
+  // v of this lane's row, every token.
+  const uint32_t v_step = n_v * d_v * IB;
+  const uint32_t v_ext = (n_tok - 1) * v_step + d_v * IB;
+  const uint64_t v0 = (tok0 * n_v + vh) * d_v * IB;
+  const rsrc_t v_rs = buffer(static_cast<const char *>(v_in) + v0, v_ext);
+  typename Io<IO>::R1 vr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) vr[t] = Io<IO>::raw1(v_rs, row * IB, uniform(tclamp(t) * v_step));
+  // The state rows (head_bytes is host-checked < 2^32, a multiple of
+  // ROW_BYTES).
+  const uint32_t head_bytes = d_v * ROW_BYTES;
+  const uint64_t head = ((uint64_t)s * n_v + vh) * d_v * DK;
+  const uint32_t cell = row * ROW_BYTES + 16 * sub;
+  const rsrc_t s_in = buffer(state_in + head, head_bytes);
+  f4 st[NV];
+#pragma unroll
+  for (int m = 0; m < NV; ++m) st[m] = load4_stream(s_in, cell + m * 16 * L);
+  __builtin_amdgcn_sched_barrier(0);
+  const float alpha_l = expf(-g_l);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Park the wave's k and q rows (widened to f32) and, after the workgroup
+  // barrier, read this lane's columns of every token.
+  float(*const slot)[2][DK] = kq_lds;
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const uint32_t r = wave + j * WAVES;
+    if (r < 2 * NT) {
+      float w[EPL];
+      widen<IO, EPL>(kr[j], w);
+#pragma unroll
+      for (uint32_t e = 0; e < EPL; ++e) slot[r / 2][r & 1][EPL * lane + e] = w[e];
+    }
+  }
+  __syncthreads();
+  f4 kc[NT][NV], qc[NT][NV];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      kc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][0][m * 4 * L + 4 * sub]);
+      qc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][1][m * 4 * L + 4 * sub]);
+    }
+  // Per-token factors, wave-uniform: alpha, beta and (NK) the key row's
+  // 1 / sqrt(sum k^2 + kNormEps), folded into sk and delta.
+  float alpha[NT], bs[NT], inv[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    alpha[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_l), t));
+    const float beta = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b_l), t));
+    inv[t] = 1.f;
+    if constexpr (NORMK) {
+      float ss = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kc[t][m][e], kc[t][m][e], ss);
+      inv[t] = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
+    }
+    bs[t] = beta * inv[t];
+  }
+  float v[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) v[t] = Io<IO>::widen1(vr[t]);
+  // The store addresses and q_scale, from kernel-argument memory: requested
+  // here and waited for once.
+  void *const out = a.output;
+  float *const s_out_p = a.state_out, *const cap_p = a.capture;
+  const float qsc = a.q_scale;
+  asm volatile("" ::"s"(out), "s"(s_out_p), "s"(cap_p), "s"(qsc));
+  // Every request has completed before the first store (the loop waits for
+  // no memory, so its stores, inside per-token branches, never delay a
+  // load's wait).
+  __builtin_amdgcn_s_waitcnt(kWaitVmAll);
+
+  // A row past d_v stores at offset head_bytes, outside its descriptor: the
+  // hardware drops it (the immediate offsets added stay below ROW_BYTES).
+  const uint32_t sc = ok ? cell : head_bytes;
+  const rsrc_t o_rs = buffer(static_cast<char *>(out) + v0, v_ext);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t >= (int)n_tok) break;
+#pragma unroll
+    for (int m = 0; m < NV; ++m) st[m] *= alpha[t];
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part = __builtin_fmaf(st[m][e], kc[t][m][e], part);
+    const float d = __builtin_fmaf(-inv[t], group_sum<L>(part), v[t]) * bs[t];
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[m][e] = __builtin_fmaf(d, kc[t][m][e], st[m][e]);
+    if constexpr (CAPTURE) {
+      const rsrc_t ct = buffer(cap_p + ((tok0 + t) * n_v + vh) * d_v * DK, head_bytes);
+#pragma unroll
+      for (int m = 0; m < NV; ++m) store4_stream(ct, sc + m * 16 * L, st[m]);
+    }
+    float py = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) py = __builtin_fmaf(st[m][e], qc[t][m][e], py);
+    const float y = group_sum<L>(py);
+    if (sub == 0 && ok) Io<IO>::store1(o_rs, row * IB, uniform(t * v_step), y * qsc);
+  }
+  const rsrc_t s_out = buffer(s_out_p + head, head_bytes);
+#pragma unroll
+  for (int m = 0; m < NV; ++m) store4_stream(s_out, sc + m * 16 * L, st[m]);
+}
+
 // ---------------------------------------------------------------- geometry
 
 struct Geometry {
@@ -1512,6 +1705,10 @@ struct Geometry {
   const void *kernel;
   bool decode;  // gdn_decode (one token) rather than gdn_recurrent
   const void *wide = nullptr;  // one token, GQA ratio above 65535: gdn_decode_wide
+  // Multi-token calls of at most 8 tokens: gdn_short (short_rows rows per
+  // block) when the sizes fit its size word, else `kernel`.
+  const void *shortk = nullptr;
+  int short_rows = 0, short_threads = 0;
 };
 
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
@@ -1520,6 +1717,15 @@ constexpr Geometry make_geometry() {
                   reinterpret_cast<const void *>(
                       &gdn_recurrent<DK, C, R, WAVES, NB, CAPTURE, IO, NK>),
                   false};
+}
+
+// A multi-token geometry with gdn_short (at most NT tokens) beside it.
+template <int DK, int C, int WAVES, int NT, bool CAPTURE, typename IO, int NK>
+constexpr Geometry with_short(Geometry geo) {
+  geo.shortk = reinterpret_cast<const void *>(&gdn_short<DK, C, WAVES, NT, CAPTURE, IO, NK>);
+  geo.short_rows = WAVES * (64 / (DK / C));
+  geo.short_threads = WAVES * 64;
+  return geo;
 }
 
 template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
@@ -1545,6 +1751,18 @@ constexpr Geometry make_decode_geometry() {
 //                workgroups) runs 3.14 -> 2.93 us with one row per lane and
 //                two waves (768 workgroups); from two sequences on the
 //                two-row grid is faster again (4.05 vs 4.29 us).
+//   2 to 8 tokens at D_k = 128: gdn_short, one row per lane, 16 lanes per
+//                row, 4 waves, every input requested before the token loop
+//                and the k/q rows staged once per workgroup (general kernel
+//                -> gdn_short: 4-token verify with capture 5.21 -> 5.15 us,
+//                without capture 4.77 -> 3.57 us; 2 tokens with capture 4.08
+//                -> 3.71 us; 8 tokens without capture 5.38 -> 4.56 us; one
+//                dense-shape sequence of 4 tokens 4.19 -> 3.19 us; the
+//                64-sequence batch of 4 tokens with capture 150.5 -> 137.9
+//                us). Staging the rows per wave instead of per workgroup put
+//                four times the row requests ahead of the state's in each
+//                compute unit's queue: 4-token verify 5.29 us, 8 tokens
+//                9.12 us.
 //   two or more: two rows per lane (each k/q register feeds two rows, which
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
 //                tokens against one row per lane), 16 lanes per row, 4 waves.
@@ -1581,7 +1799,7 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
         return make_decode_geometry<64, 4, 2, 4, CAPTURE, IO, NK1>();
       }
       return make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
-    case 128:
+    case 128: {
       if (one_token) {
         // A grid of two-row workgroups that leaves compute units idle (one
         // dense-shape layer of one sequence: 192 workgroups) is spread over
@@ -1590,17 +1808,23 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
           return make_decode_geometry<128, 8, 1, 2, CAPTURE, IO, NK1>();
         return make_decode_geometry<128, 8, 2, 4, CAPTURE, IO, NK1>();
       }
+      Geometry geo;
       if constexpr (CAPTURE) {
-        return make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NK>();
+        geo = make_geometry<128, 8, 1, 4, 4, CAPTURE, IO, NK>();
       } else {
         // Below one two-row workgroup per compute unit the waves run their
         // token loops nearly alone: one row per lane (half the work per wave
         // and token) and two waves per workgroup. One dense-shape sequence
         // of 512 tokens: 125.4 -> 116.9 us; of 64 tokens: 19.4 -> 18.9 us.
         if (heads * ((d_v + 31) / 32) < kComputeUnits)
-          return make_geometry<128, 8, 1, 2, 8, CAPTURE, IO, NK>();
-        return make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NK>();
+          geo = make_geometry<128, 8, 1, 2, 8, CAPTURE, IO, NK>();
+        else
+          geo = make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NK>();
       }
+      if (n_tokens <= 4) return with_short<128, 8, 4, 4, CAPTURE, IO, NK1>(geo);
+      if (n_tokens <= 8) return with_short<128, 8, 4, 8, CAPTURE, IO, NK1>(geo);
+      return geo;
+    }
     default:
       return Geometry{0, 0, nullptr, false};
   }
@@ -1638,14 +1862,30 @@ uint32_t ceil_log2(uint64_t x) {
 
 }  // namespace
 
-uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
+namespace {
+
+// Whether a multi-token call takes gdn_short (its sizes fit the size word).
+bool short_fits(const Geometry &geo, uint32_t d_v, uint32_t n_k_heads, uint32_t n_v_heads) {
+  if (geo.shortk == nullptr) return false;
+  const uint32_t groups = n_v_heads / n_k_heads;
+  const uint32_t row_blocks = (d_v + geo.short_rows - 1) / geo.short_rows;
+  return d_v >> kPackDv == 0 && ceil_log2(row_blocks) >> kPackRb == 0 &&
+         n_k_heads >> kShortNk == 0 && groups >> kShortGroups == 0;
+}
+
+}  // namespace
+
+uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_k_heads, uint32_t n_v_heads,
                      uint32_t n_seqs, uint32_t n_tokens, bool capture) {
   const Geometry geo =
       pick_geometry(d_k, d_v, (uint64_t)n_v_heads * n_seqs, n_tokens, capture, false, false);
   if (geo.kernel == nullptr) return 0;
-  const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
-  // One-token grids pad each head's row blocks to a power of two.
-  const uint64_t padded = geo.decode ? uint64_t(1) << ceil_log2(row_blocks) : row_blocks;
+  // One-token and short grids pad each head's row blocks to a power of two.
+  const bool short_grid = short_fits(geo, d_v, n_k_heads, n_v_heads);
+  const int rows = short_grid ? geo.short_rows : geo.rows_per_block;
+  const uint64_t row_blocks = (d_v + rows - 1) / rows;
+  const uint64_t padded =
+      geo.decode || short_grid ? uint64_t(1) << ceil_log2(row_blocks) : row_blocks;
   return padded * n_v_heads * n_seqs;
 }
 
@@ -1704,6 +1944,40 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
         e = hipLaunchKernel(geo.wide, dim3(f.n_v_heads << rb_shift, ns), dim3(geo.threads), args,
                             0, stream);
       }
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+
+  if (short_fits(geo, f.d_v, f.n_k_heads, f.n_v_heads)) {
+    // At most 8 tokens: the one-token grid and argument layout (see above),
+    // the sizes word carrying n_tokens - 1; one launch per 65535 sequences.
+    constexpr uint32_t kMaxGrid = 65535;
+    const uint32_t rb_shift = ceil_log2((f.d_v + geo.short_rows - 1) / geo.short_rows);
+    const uint32_t groups = f.n_v_heads / f.n_k_heads;
+    uint32_t sizes = f.d_v | rb_shift << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
+                     groups << (kPackDv + kPackRb + kShortNk) |
+                     (f.n_tokens - 1) << (kPackDv + kPackRb + kShortNk + kShortGroups);
+    const uint64_t state_seq = (uint64_t)f.n_v_heads * f.d_v * f.d_k;                // floats
+    const uint64_t kq_seq = (uint64_t)f.n_tokens * f.n_k_heads * f.d_k * io;         // bytes
+    const uint64_t v_seq = (uint64_t)f.n_tokens * f.n_v_heads * f.d_v * io;          // bytes
+    const uint64_t gb_seq = (uint64_t)f.n_tokens * f.n_v_heads;                      // floats
+    for (uint32_t s0 = 0; s0 < f.n_seqs; s0 += kMaxGrid) {
+      const uint32_t ns = f.n_seqs - s0 < kMaxGrid ? f.n_seqs - s0 : kMaxGrid;
+      const float *state_in = f.state_in + s0 * state_seq;
+      const void *k = static_cast<const char *>(f.k) + s0 * kq_seq;
+      const float *g = f.g + s0 * gb_seq;
+      const void *v = static_cast<const char *>(f.v) + s0 * v_seq;
+      const float *beta = f.beta + s0 * gb_seq;
+      const void *q = static_cast<const char *>(f.q) + s0 * kq_seq;
+      DecodeTail t;
+      t.output = static_cast<char *>(f.output) + s0 * v_seq;
+      t.state_out = f.state_out + s0 * state_seq;
+      t.capture = f.capture != nullptr ? f.capture + s0 * f.n_tokens * state_seq : nullptr;
+      t.q_scale = f.q_scale;
+      void *args[] = {&state_in, &k, &q, &g, &v, &beta, &sizes, &t};
+      const hipError_t e = hipLaunchKernel(geo.shortk, dim3(f.n_k_heads << rb_shift, groups, ns),
+                                           dim3(geo.short_threads), args, 0, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -23,7 +23,7 @@ struct ForwardArgs {
 
 // Number of workgroups the chosen launch geometry needs (for the host-side
 // overflow check; 0 when d_k is unsupported).
-uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_v_heads,
+uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_k_heads, uint32_t n_v_heads,
                      uint32_t n_seqs, uint32_t n_tokens, bool capture);
 
 // Pick the launch geometry for (d_k, n_tokens, capture) and enqueue the kernel
