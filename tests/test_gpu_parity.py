@@ -1079,6 +1079,32 @@ def test_one_token_sizes_past_the_size_word(shape, capture):
     for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
         close(g_, e, f"{shape} {what}")
 
+@pytest.mark.parametrize("capture", [False, True], ids=["plain", "capture"])
+@pytest.mark.parametrize("shape", [
+    (128, 2047, 1, 1, 3, 1),    # the short kernel's size word: largest d_v
+    (128, 2048, 1, 1, 3, 1),    # d_v past 2047 (the general multi-token kernel)
+    (128, 3, 127, 127, 2, 2),   # its largest key-head count
+    (128, 3, 128, 128, 2, 2),   # more than 127 key heads
+    (128, 2, 1, 127, 8, 2),     # its largest value-head count per key head
+    (128, 2, 1, 128, 8, 2),     # more than 127 value heads per key head
+    (128, 5, 3, 6, 5, 3),       # 5 tokens of an 8-token kernel, ragged rows
+    (128, 1, 1, 1, 2, 70000),   # sequences past one launch's 65535
+], ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
+def test_short_sizes_at_and_past_the_size_word(shape, capture):
+    """Calls of 2 to 8 tokens at D_k = 128 take the short kernel when their
+    sizes fit its size word (d_v, key heads, value heads per key head and
+    n_tokens - 1 in one 32-bit argument) and the general multi-token kernel
+    past it; more than 65535 sequences take several launches. Against the
+    oracle on both sides of each limit."""
+    dk, dv, hk, hv, t, s_ = shape
+    x = make_inputs(Workload("short", 0, dk, dv, hk, hv, t, s_, fold_q_scale=True),
+                    seed=131 + dv + hv)
+    got = run(x, capture=capture)
+    exp = ref(x, capture=capture)
+    for g_, e, what in zip(got, exp, ("output", "state_out", "capture")):
+        close(g_, e, f"{shape} {what}")
+
+
 def test_q_scale_value():
     """forward(q_scale=<float>) equals forward(q_scale_bits=<its bits>) bit for
     bit."""
