@@ -59,7 +59,7 @@ RESIDENT_TARGET_BYTES = 1 << 30  # input sets cycled per run: >= 4x the cache
 METRIC = "GDN decode µs/layer + state HBM GB/s (%peak); prefill tokens/s at n_tokens=512"
 KERNEL_NAME = "gdn_recurrent"      # multi-token forward calls
 DECODE_KERNEL_NAME = "gdn_decode"  # one-token forward calls
-SHORT_KERNEL_NAME = "gdn_short"    # 2 to 8 tokens at D_k = 128
+SHORT_KERNEL_NAME = "gdn_short"    # 2 to 8 tokens
 NAMES = ("q", "k", "v", "g", "beta", "state_in")
 # The headline line's other workloads: (name, timed steps, warm-up steps). Each
 # timed region covers tens of milliseconds of GPU work whatever --steps is
@@ -180,7 +180,7 @@ def workload_info(name: str, io: str = "f32"):
     w = WORKLOADS[name]
     if w.n_tokens == 1:
         kernel = DECODE_KERNEL_NAME
-    elif w.n_tokens <= 8 and w.d_k == 128:
+    elif w.n_tokens <= 8:
         kernel = SHORT_KERNEL_NAME
     else:
         kernel = KERNEL_NAME

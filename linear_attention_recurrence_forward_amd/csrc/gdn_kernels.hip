@@ -1509,12 +1509,12 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_decode_wide(
 // n_tokens - 1 in 29-31.
 constexpr uint32_t kShortNk = 7, kShortGroups = 7, kShortTok = 3;
 
-// Short multi-token calls (2 <= n_tokens <= NT, D_k = 128; speculative
+// Short multi-token calls (2 <= n_tokens <= NT; speculative
 // verification): the one-token kernel's layout (grid, preloaded arguments,
 // L lanes per row, one row per lane, straight-line code) extended to NT
 // tokens. Every input is requested before the token loop, in the order it
 // is needed: g and beta (lane t holds token t's), each token's k and q rows
-// (requested once per workgroup, 8 or 4 bytes a lane, the rows spread over
+// (requested once per workgroup, 2 to 8 bytes a lane, the rows spread over
 // the waves, and parked in LDS, from which each lane reads its columns), v,
 // then the state rows last, whose HBM round trip covers the rest; the decay factors
 // are one exp over the lanes and are read back as wave-uniform values. The
@@ -1532,10 +1532,13 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   constexpr uint32_t ROWS = WAVES * G;
   constexpr uint32_t ROW_BYTES = DK * 4;
   constexpr uint32_t IB = Io<IO>::bytes;
-  constexpr uint32_t KQ_BYTES = DK * IB;  // one k or q row
-  constexpr uint32_t RB = KQ_BYTES / 64;  // its bytes per lane
-  constexpr uint32_t EPL = RB / IB;       // its elements per lane
-  static_assert(DK == 128 && EPL == 2, "k/q rows of 128 elements, two per lane");
+  constexpr uint32_t KQ_BYTES = DK * IB;  // one k or q row (64 to 512 bytes)
+  // It is staged by SL lanes of RB bytes (EPL elements) each: 64 lanes of
+  // 8, 4 or 2 bytes, or 32 lanes of one element for the shortest rows.
+  constexpr uint32_t RB = KQ_BYTES / 64 >= IB ? KQ_BYTES / 64 : IB;
+  constexpr uint32_t SL = KQ_BYTES / RB;
+  constexpr uint32_t EPL = RB / IB;
+  static_assert((EPL == 1 || EPL == 2) && SL <= 64 && SL * RB == KQ_BYTES, "k/q staging");
   static_assert(NT >= 2 && NT <= 8, "2 to 8 tokens");
   static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
   // Token t's k row is row 2t of the slot, its q row 2t + 1; wave w requests
@@ -1571,7 +1574,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   const uint32_t tl = tclamp(lane);
   const float g_l = load1(buffer(g_in + tok0 * n_v + vh, gb_ext), tl * gb_step);
   const float b_l = load1(buffer(beta_in + tok0 * n_v + vh, gb_ext), tl * gb_step);
-  // k and q rows: lane l holds elements 2l and 2l + 1 of each.
+  // k and q rows: staging lane l holds elements EPL * l ... of each.
   const uint32_t kq_step = n_k * KQ_BYTES;
   const uint32_t kq_ext = (n_tok - 1) * kq_step + KQ_BYTES;
   const uint64_t kq0 = (tok0 * n_k + kh) * KQ_BYTES;
@@ -1583,7 +1586,8 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
     const uint32_t r = wave + j * WAVES;
     const uint32_t rr = r < 2 * NT ? r : 2 * NT - 1;
     const uint32_t off = uniform(tclamp(rr / 2) * kq_step);
-    kr[j] = (rr & 1) ? Raw<RB>::load(q_rs, lane * RB, off) : Raw<RB>::load(k_rs, lane * RB, off);
+    const uint32_t lo = (lane % SL) * RB;  // lanes past SL repeat the row
+    kr[j] = (rr & 1) ? Raw<RB>::load(q_rs, lo, off) : Raw<RB>::load(k_rs, lo, off);
   }
   // v of this lane's row, every token.
   const uint32_t v_step = n_v * d_v * IB;
@@ -1612,7 +1616,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
     const uint32_t r = wave + j * WAVES;
-    if (r < 2 * NT) {
+    if (r < 2 * NT && (SL == 64 || lane < SL)) {
       float w[EPL];
       widen<IO, EPL>(kr[j], w);
 #pragma unroll
@@ -1786,10 +1790,14 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
   const bool one_token = n_tokens == 1;
   constexpr int NK1 = NK == 2 ? 1 : NK;  // one-token calls have no ring group
   switch (d_k) {
-    case 32:
-      return one_token ? make_decode_geometry<32, 4, 1, 4, CAPTURE, IO, NK1>()
-                       : make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NK>();
-    case 64:
+    case 32: {
+      if (one_token) return make_decode_geometry<32, 4, 1, 4, CAPTURE, IO, NK1>();
+      const Geometry geo = make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NK>();
+      if (n_tokens <= 4) return with_short<32, 4, 4, 4, CAPTURE, IO, NK1>(geo);
+      if (n_tokens <= 8) return with_short<32, 4, 4, 8, CAPTURE, IO, NK1>(geo);
+      return geo;
+    }
+    case 64: {
       if (one_token) {
         // Two rows per lane once that grid fills the chip (64-sequence
         // batch of the MoE shape at D_k = 64: 12.9 -> 12.4 us); one row per
@@ -1798,7 +1806,11 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
           return make_decode_geometry<64, 4, 1, 4, CAPTURE, IO, NK1>();
         return make_decode_geometry<64, 4, 2, 4, CAPTURE, IO, NK1>();
       }
-      return make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
+      const Geometry geo = make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
+      if (n_tokens <= 4) return with_short<64, 4, 4, 4, CAPTURE, IO, NK1>(geo);
+      if (n_tokens <= 8) return with_short<64, 4, 4, 8, CAPTURE, IO, NK1>(geo);
+      return geo;
+    }
     case 128: {
       if (one_token) {
         // A grid of two-row workgroups that leaves compute units idle (one

@@ -51,7 +51,7 @@ def test_algorithmic_bytes(bench, name, shape, capture, total):
     assert (w.d_k, w.d_v, w.n_k_heads, w.n_v_heads, w.n_tokens, w.n_seqs) == shape
     assert alg == expected_bytes(*shape, capture=capture) == total
     want = ("gdn_decode" if shape[4] == 1 else
-            "gdn_short" if shape[4] <= 8 and shape[0] == 128 else "gdn_recurrent")
+            "gdn_short" if shape[4] <= 8 else "gdn_recurrent")
     assert kernel == want
     _, _, alg16, _ = bench.workload_info(name, "bf16")
     assert alg16 == expected_bytes(*shape, capture=capture, io=2)

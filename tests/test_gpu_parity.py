@@ -455,23 +455,34 @@ def test_capture_prefixes():
     """P5 on the GPU: capture slice t equals the state of the same call cut to
     t+1 tokens, and a call without capture gives the same output and state.
     Bit for bit where the arithmetic is the same: capture[T-1] == state_out of
-    one call (the pages' determinism contract), and capture calls of two
-    tokens or more against each other (one kernel, every token eager). Calls
-    without capture may take the lazy (reassociated) decay, and one-token
-    calls have their own geometry: those are compared within tolerance."""
+    one call (the pages' determinism contract), and capture calls of 2 to 8
+    tokens against each other (one kernel, the short one, every token eager;
+    so are calls of 9 tokens or more, on the general kernel). Across the two
+    kernels the cross-lane sums may group differently (C5), as may calls
+    without capture (the lazy decay) and one-token calls (their own
+    geometry): those are compared within tolerance."""
     w = Workload("cap", 0, 64, 32, 2, 4, 9, 2)
     x = make_inputs(w, seed=15)
     out, st, cap = run(x, capture=True)
     assert_equal(cap[:, -1], st, "capture[T-1] == state_out")
+    cut8 = {n: x[n][:, :8] for n in ("q", "k", "v", "g", "beta")}
+    out8, st8, cap8 = run(dict(cut8, state_in=x["state_in"]), capture=True)
+    assert_equal(cap8[:, -1], st8, "8 tokens: capture[T-1] == state_out")
     for t in range(w.n_tokens):
         cut = {n: x[n][:, :t + 1] for n in ("q", "k", "v", "g", "beta")}
         o_t, s_t = run(dict(cut, state_in=x["state_in"]))
         close(cap[:, t], s_t, f"capture[{t}] vs state after {t + 1} tokens")
         close(o_t, out[:, :t + 1], f"outputs of the first {t + 1} tokens")
-        if t >= 1:
+        if 1 <= t < 8:
             o_c, s_c, c_c = run(dict(cut, state_in=x["state_in"]), capture=True)
-            assert_equal(c_c, cap[:, :t + 1], f"capture of a {t + 1}-token call is a prefix")
-            assert_equal(o_c, out[:, :t + 1], f"outputs of a {t + 1}-token capture call")
+            assert_equal(c_c, cap8[:, :t + 1], f"capture of a {t + 1}-token call is a prefix")
+            assert_equal(o_c, out8[:, :t + 1], f"outputs of a {t + 1}-token capture call")
+            close(c_c, cap[:, :t + 1], f"{t + 1}-token capture vs the 9-token call's")
+            close(o_c, out[:, :t + 1], f"{t + 1}-token outputs vs the 9-token call's")
+    cut10 = {n: np.concatenate([x[n], x[n][:, -1:]], axis=1) for n in ("q", "k", "v", "g", "beta")}
+    out10, _, cap10 = run(dict(cut10, state_in=x["state_in"]), capture=True)
+    assert_equal(cap10[:, :9], cap, "capture of a 9-token call is a prefix of a 10-token call's")
+    assert_equal(out10[:, :9], out, "outputs of a 9-token capture call")
     o2, s2 = run(x)
     close(o2, out, "output without capture")
     close(s2, st, "state_out without capture")
@@ -1089,9 +1100,15 @@ def test_one_token_sizes_past_the_size_word(shape, capture):
     (128, 2, 1, 128, 8, 2),     # more than 127 value heads per key head
     (128, 5, 3, 6, 5, 3),       # 5 tokens of an 8-token kernel, ragged rows
     (128, 1, 1, 1, 2, 70000),   # sequences past one launch's 65535
+    (64, 2047, 1, 1, 3, 1),     # D_k = 64 and 32: 16 and 32 rows a workgroup
+    (64, 2048, 1, 1, 3, 1),
+    (64, 5, 3, 6, 7, 3),
+    (32, 2047, 1, 1, 4, 1),
+    (32, 2048, 1, 1, 4, 1),
+    (32, 37, 2, 6, 6, 3),
 ], ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
 def test_short_sizes_at_and_past_the_size_word(shape, capture):
-    """Calls of 2 to 8 tokens at D_k = 128 take the short kernel when their
+    """Calls of 2 to 8 tokens take the short kernel when their
     sizes fit its size word (d_v, key heads, value heads per key head and
     n_tokens - 1 in one 32-bit argument) and the general multi-token kernel
     past it; more than 65535 sequences take several launches. Against the
