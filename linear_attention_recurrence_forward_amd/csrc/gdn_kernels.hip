@@ -1709,7 +1709,7 @@ struct Geometry {
   const void *kernel;
   bool decode;  // gdn_decode (one token) rather than gdn_recurrent
   const void *wide = nullptr;  // one token, GQA ratio above 65535: gdn_decode_wide
-  // Multi-token calls of at most 8 tokens: gdn_short (short_rows rows per
+  // Multi-token calls of 2 to 8 tokens: gdn_short (short_rows rows per
   // block) when the sizes fit its size word, else `kernel`.
   const void *shortk = nullptr;
   int short_rows = 0, short_threads = 0;
@@ -1755,18 +1755,22 @@ constexpr Geometry make_decode_geometry() {
 //                workgroups) runs 3.14 -> 2.93 us with one row per lane and
 //                two waves (768 workgroups); from two sequences on the
 //                two-row grid is faster again (4.05 vs 4.29 us).
-//   2 to 8 tokens at D_k = 128: gdn_short, one row per lane, 16 lanes per
-//                row, 4 waves, every input requested before the token loop
-//                and the k/q rows staged once per workgroup (general kernel
-//                -> gdn_short: 4-token verify with capture 5.21 -> 5.15 us,
-//                without capture 4.77 -> 3.57 us; 2 tokens with capture 4.08
-//                -> 3.71 us; 8 tokens without capture 5.38 -> 4.56 us; one
-//                dense-shape sequence of 4 tokens 4.19 -> 3.19 us; the
-//                64-sequence batch of 4 tokens with capture 150.5 -> 137.9
-//                us). Staging the rows per wave instead of per workgroup put
-//                four times the row requests ahead of the state's in each
-//                compute unit's queue: 4-token verify 5.29 us, 8 tokens
-//                9.12 us.
+//   2 to 8 tokens: gdn_short, one row per lane (8 cells at D_k = 128, 4
+//                below), 4 waves, every input requested before the token
+//                loop and the k/q rows staged once per workgroup (general
+//                kernel -> gdn_short: 4-token verify with capture 5.21 ->
+//                5.15 us, without capture 4.77 -> 3.57 us; 2 tokens with
+//                capture 4.08 -> 3.71 us; 8 tokens without capture 5.38 ->
+//                4.56 us; one dense-shape sequence of 4 tokens 4.19 -> 3.19
+//                us; the 64-sequence batch of 4 tokens with capture 150.5 ->
+//                137.9 us; the 8-token D_k = 32 case 3.97 -> 2.58 us; a
+//                4-token D_k = 64 verify 3.43 -> 2.64 us). Staging the rows
+//                per wave instead of per workgroup put four times the row
+//                requests ahead of the state's in each compute unit's
+//                queue (4-token verify 5.29 us, 8 tokens 9.12 us). Past 8
+//                tokens a token loop reading each token's columns during the
+//                previous one lost to the general kernel (16 tokens 8.38
+//                against 6.88 us; the 64-sequence batch 114 against 80 us).
 //   two or more: two rows per lane (each k/q register feeds two rows, which
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
 //                tokens against one row per lane), 16 lanes per row, 4 waves.
