@@ -1505,14 +1505,25 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_decode_wide(
 }
 
 // Sizes of a short multi-token launch in one 32-bit word: d_v in bits 0-10,
-// rb_shift in 11-14, n_k_heads in 15-21, n_v_heads / n_k_heads in 22-28,
+// kh_bits in 11-14, n_k_heads in 15-21, n_v_heads / n_k_heads in 22-28,
 // n_tokens - 1 in 29-31.
 constexpr uint32_t kShortNk = 7, kShortGroups = 7, kShortTok = 3;
 
+// Key-head bits of a short launch's grid x: at least 3, so that the row
+// blocks of a head (2^kh_bits apart in x, and the y stride a multiple of
+// that) run on one of the 8 XCDs, which take workgroups round-robin, and
+// its k and q rows are fetched into one L2 instead of all eight.
+uint32_t short_kh_bits(uint32_t n_k_heads) {
+  uint32_t b = 3;
+  while ((1u << b) < n_k_heads) ++b;
+  return b;
+}
+
 // Short multi-token calls (2 <= n_tokens <= NT; speculative
-// verification): the one-token kernel's layout (grid, preloaded arguments,
-// L lanes per row, one row per lane, straight-line code) extended to NT
-// tokens. Every input is requested before the token loop, in the order it
+// verification): the one-token kernel's layout (preloaded arguments, L
+// lanes per row, one row per lane, straight-line code) extended to NT
+// tokens. Grid: x = (row block << kh_bits) | key head (see short_kh_bits),
+// y = value head of the key head, z = sequence. Every input is requested before the token loop, in the order it
 // is needed: g and beta (lane t holds token t's), each token's k and q rows
 // (requested once per workgroup, 2 to 8 bytes a lane, the rows spread over
 // the waves, and parked in LDS, from which each lane reads its columns), v,
@@ -1547,16 +1558,16 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   constexpr int RPW = (2 * NT + WAVES - 1) / WAVES;  // rows per wave
 
   const uint32_t d_v = sizes & ((1u << kPackDv) - 1u);
-  const uint32_t rb_shift = (sizes >> kPackDv) & ((1u << kPackRb) - 1u);
+  const uint32_t kh_bits = (sizes >> kPackDv) & ((1u << kPackRb) - 1u);
   const uint32_t n_k = (sizes >> (kPackDv + kPackRb)) & ((1u << kShortNk) - 1u);
   const uint32_t groups = (sizes >> (kPackDv + kPackRb + kShortNk)) & ((1u << kShortGroups) - 1u);
   const uint32_t n_tok = (sizes >> (kPackDv + kPackRb + kShortNk + kShortGroups)) + 1u;
   const uint32_t n_v = groups * n_k;
-  const uint32_t rb = blockIdx.x & ((1u << rb_shift) - 1u);
-  const uint32_t kh = blockIdx.x >> rb_shift;
+  const uint32_t kh = blockIdx.x & ((1u << kh_bits) - 1u);
+  const uint32_t rb = blockIdx.x >> kh_bits;
   const uint32_t vh = kh + n_k * blockIdx.y;
   const uint32_t s = blockIdx.z;
-  if (rb * ROWS >= d_v) return;  // padding of the row blocks: the whole workgroup
+  if (kh >= n_k) return;  // padding of the key heads: the whole workgroup
 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1885,8 +1896,8 @@ bool short_fits(const Geometry &geo, uint32_t d_v, uint32_t n_k_heads, uint32_t 
   if (geo.shortk == nullptr) return false;
   const uint32_t groups = n_v_heads / n_k_heads;
   const uint32_t row_blocks = (d_v + geo.short_rows - 1) / geo.short_rows;
-  return d_v >> kPackDv == 0 && ceil_log2(row_blocks) >> kPackRb == 0 &&
-         n_k_heads >> kShortNk == 0 && groups >> kShortGroups == 0;
+  return d_v >> kPackDv == 0 && row_blocks <= 128 && n_k_heads >> kShortNk == 0 &&
+         groups >> kShortGroups == 0;
 }
 
 }  // namespace
@@ -1897,11 +1908,14 @@ uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_k_heads, uint32_t n_
       pick_geometry(d_k, d_v, (uint64_t)n_v_heads * n_seqs, n_tokens, capture, false, false);
   if (geo.kernel == nullptr) return 0;
   // One-token and short grids pad each head's row blocks to a power of two.
-  const bool short_grid = short_fits(geo, d_v, n_k_heads, n_v_heads);
-  const int rows = short_grid ? geo.short_rows : geo.rows_per_block;
-  const uint64_t row_blocks = (d_v + rows - 1) / rows;
-  const uint64_t padded =
-      geo.decode || short_grid ? uint64_t(1) << ceil_log2(row_blocks) : row_blocks;
+  if (short_fits(geo, d_v, n_k_heads, n_v_heads)) {
+    // Short grids pad the key heads to a power of two (at least 8).
+    const uint64_t row_blocks = (d_v + geo.short_rows - 1) / geo.short_rows;
+    return (row_blocks << short_kh_bits(n_k_heads)) * (n_v_heads / n_k_heads) * n_seqs;
+  }
+  // One-token grids pad each head's row blocks to a power of two.
+  const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
+  const uint64_t padded = geo.decode ? uint64_t(1) << ceil_log2(row_blocks) : row_blocks;
   return padded * n_v_heads * n_seqs;
 }
 
@@ -1966,12 +1980,14 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
   }
 
   if (short_fits(geo, f.d_v, f.n_k_heads, f.n_v_heads)) {
-    // At most 8 tokens: the one-token grid and argument layout (see above),
-    // the sizes word carrying n_tokens - 1; one launch per 65535 sequences.
+    // At most 8 tokens: the one-token argument layout (see above), the
+    // sizes word carrying kh_bits and n_tokens - 1; grid x = (row block <<
+    // kh_bits) | key head; one launch per 65535 sequences.
     constexpr uint32_t kMaxGrid = 65535;
-    const uint32_t rb_shift = ceil_log2((f.d_v + geo.short_rows - 1) / geo.short_rows);
+    const uint32_t row_blocks = (f.d_v + geo.short_rows - 1) / geo.short_rows;
+    const uint32_t kh_bits = short_kh_bits(f.n_k_heads);
     const uint32_t groups = f.n_v_heads / f.n_k_heads;
-    uint32_t sizes = f.d_v | rb_shift << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
+    uint32_t sizes = f.d_v | kh_bits << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
                      groups << (kPackDv + kPackRb + kShortNk) |
                      (f.n_tokens - 1) << (kPackDv + kPackRb + kShortNk + kShortGroups);
     const uint64_t state_seq = (uint64_t)f.n_v_heads * f.d_v * f.d_k;                // floats
@@ -1992,7 +2008,7 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
       t.capture = f.capture != nullptr ? f.capture + s0 * f.n_tokens * state_seq : nullptr;
       t.q_scale = f.q_scale;
       void *args[] = {&state_in, &k, &q, &g, &v, &beta, &sizes, &t};
-      const hipError_t e = hipLaunchKernel(geo.shortk, dim3(f.n_k_heads << rb_shift, groups, ns),
+      const hipError_t e = hipLaunchKernel(geo.shortk, dim3(row_blocks << kh_bits, groups, ns),
                                            dim3(geo.short_threads), args, 0, stream);
       if (e != hipSuccess) return e;
     }
