@@ -1451,8 +1451,20 @@ struct DecodeTail {
 };
 
 // Sizes of a one-token launch in one 32-bit word: d_v in bits 0-10,
-// rb_shift in 11-14, n_k_heads in 15-24, n_v_heads / n_k_heads in 25-31.
+// kh_bits in 11-14, n_k_heads in 15-24, n_v_heads / n_k_heads in 25-31.
 constexpr uint32_t kPackDv = 11, kPackRb = 4, kPackNk = 10, kPackGroups = 7;
+
+// Key-head bits of a one-token or short launch's grid x = (row block <<
+// kh_bits) | key head: at least 3, so that the row blocks of a head
+// (2^kh_bits apart in x, and the y stride a multiple of that) run on one of
+// the 8 XCDs, which take workgroups round-robin, and its k, q and v rows
+// are fetched into one L2 instead of all eight. Padding key heads exit at
+// once.
+uint32_t xcd_kh_bits(uint32_t n_k_heads) {
+  uint32_t b = 3;
+  while ((1u << b) < n_k_heads) ++b;
+  return b;
+}
 
 // The one-token kernel. The six arrays that the loads address (state, k,
 // q, g, v, beta) and the size word are the first 13 kernel-argument dwords,
@@ -1461,23 +1473,26 @@ constexpr uint32_t kPackDv = 11, kPackRb = 4, kPackNk = 10, kPackGroups = 7;
 // Reading v and beta's bases from it cost single-layer decode 2.75 against
 // 2.69 us; q's, 2.76 (y waits for q). The grid's own sizes would be such a
 // read too (they live in the implicit kernel arguments), hence the size
-// word. Grid: x = (key head kh << rb_shift) | row block, the row blocks of
-// a head padded to a power of two (padding blocks exit at once); y = g, one
-// of the n_v_heads / n_k_heads value heads of a key head; z = sequence
+// word. Grid: XO (XCD order): x = (row block << kh_bits) | key head kh
+// (see xcd_kh_bits); else x = (kh << rb_shift) | row block, the order of
+// the state in memory, a head's row blocks padded to a power of two. y = g,
+// one of the n_v_heads / n_k_heads value heads of a key head; z = sequence
 // within the launch. vh = kh + g * n_k_heads (the modulo GQA map, no
-// division), and the workgroups run in the order of the state in memory
-// (sequence, value head, row block); a key-head-major order measured 44.9
-// against 42.4 us on the 64-sequence batch.
-template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
+// division). XCD order against memory order: single-layer decode (one row
+// per lane, 768 workgroups) 2.61 -> 2.52 us, bf16 2.68 -> 2.57 us; the
+// 64-sequence batch (two rows per lane, 16,384 workgroups) 41.8 -> 42.0 us,
+// so that grid keeps the memory order.
+template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK, bool XO>
 __global__ __launch_bounds__(WAVES * 64) void gdn_decode(
     const float *state_in, const void *k_in, const void *q_in, const float *g_in,
     const void *v_in, const float *beta_in, uint32_t sizes, DecodeTail a) {
   const uint32_t d_v = sizes & ((1u << kPackDv) - 1u);
-  const uint32_t rb_shift = (sizes >> kPackDv) & ((1u << kPackRb) - 1u);
+  const uint32_t bits = (sizes >> kPackDv) & ((1u << kPackRb) - 1u);  // kh_bits or rb_shift
   const uint32_t n_k_heads = (sizes >> (kPackDv + kPackRb)) & ((1u << kPackNk) - 1u);
   const uint32_t n_v_heads = (sizes >> (kPackDv + kPackRb + kPackNk)) * n_k_heads;
-  const uint32_t rb = blockIdx.x & ((1u << rb_shift) - 1u);
-  const uint32_t kh = blockIdx.x >> rb_shift;
+  const uint32_t lo = blockIdx.x & ((1u << bits) - 1u), hi = blockIdx.x >> bits;
+  const uint32_t kh = XO ? lo : hi, rb = XO ? hi : lo;
+  if (XO && kh >= n_k_heads) return;  // padding of the key heads: the whole workgroup
   const uint32_t vh = kh + n_k_heads * blockIdx.y;
   const DecodePtrs p{state_in, k_in, q_in, g_in, beta_in, v_in, a.output, a.state_out, a.capture};
   decode_token<DK, C, R, WAVES, CAPTURE, IO, NK>(p, d_v, n_v_heads, n_k_heads, blockIdx.z, vh,
@@ -1509,20 +1524,11 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_decode_wide(
 // n_tokens - 1 in 29-31.
 constexpr uint32_t kShortNk = 7, kShortGroups = 7, kShortTok = 3;
 
-// Key-head bits of a short launch's grid x: at least 3, so that the row
-// blocks of a head (2^kh_bits apart in x, and the y stride a multiple of
-// that) run on one of the 8 XCDs, which take workgroups round-robin, and
-// its k and q rows are fetched into one L2 instead of all eight.
-uint32_t short_kh_bits(uint32_t n_k_heads) {
-  uint32_t b = 3;
-  while ((1u << b) < n_k_heads) ++b;
-  return b;
-}
 
 // Short multi-token calls (2 <= n_tokens <= NT; speculative
 // verification): the one-token kernel's layout (preloaded arguments, L
 // lanes per row, one row per lane, straight-line code) extended to NT
-// tokens. Grid: x = (row block << kh_bits) | key head (see short_kh_bits),
+// tokens. Grid: x = (row block << kh_bits) | key head (see xcd_kh_bits),
 // y = value head of the key head, z = sequence. Every input is requested before the token loop, in the order it
 // is needed: g and beta (lane t holds token t's), each token's k and q rows
 // (requested once per workgroup, 2 to 8 bytes a lane, the rows spread over
@@ -1724,6 +1730,7 @@ struct Geometry {
   // block) when the sizes fit its size word, else `kernel`.
   const void *shortk = nullptr;
   int short_rows = 0, short_threads = 0;
+  bool xcd_order = false;  // gdn_decode's grid order (its XO)
 };
 
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
@@ -1743,12 +1750,14 @@ constexpr Geometry with_short(Geometry geo) {
   return geo;
 }
 
-template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK>
+template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK, bool XO>
 constexpr Geometry make_decode_geometry() {
-  return Geometry{
+  Geometry geo{
       WAVES * (64 / (DK / C)) * R, WAVES * 64,
-      reinterpret_cast<const void *>(&gdn_decode<DK, C, R, WAVES, CAPTURE, IO, NK>), true,
+      reinterpret_cast<const void *>(&gdn_decode<DK, C, R, WAVES, CAPTURE, IO, NK, XO>), true,
       reinterpret_cast<const void *>(&gdn_decode_wide<DK, C, R, WAVES, CAPTURE, IO, NK>)};
+  geo.xcd_order = XO;
+  return geo;
 }
 
 // Launch geometries, chosen by measurement on MI355X (graph-replayed calls on
@@ -1806,7 +1815,7 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
   constexpr int NK1 = NK == 2 ? 1 : NK;  // one-token calls have no ring group
   switch (d_k) {
     case 32: {
-      if (one_token) return make_decode_geometry<32, 4, 1, 4, CAPTURE, IO, NK1>();
+      if (one_token) return make_decode_geometry<32, 4, 1, 4, CAPTURE, IO, NK1, true>();
       const Geometry geo = make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NK>();
       if (n_tokens <= 4) return with_short<32, 4, 4, 4, CAPTURE, IO, NK1>(geo);
       if (n_tokens <= 8) return with_short<32, 4, 4, 8, CAPTURE, IO, NK1>(geo);
@@ -1818,8 +1827,8 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
         // batch of the MoE shape at D_k = 64: 12.9 -> 12.4 us); one row per
         // lane below (one dense-shape sequence: 2.19 vs 2.25 us).
         if (heads * ((d_v + 31) / 32) < kComputeUnits)
-          return make_decode_geometry<64, 4, 1, 4, CAPTURE, IO, NK1>();
-        return make_decode_geometry<64, 4, 2, 4, CAPTURE, IO, NK1>();
+          return make_decode_geometry<64, 4, 1, 4, CAPTURE, IO, NK1, true>();
+        return make_decode_geometry<64, 4, 2, 4, CAPTURE, IO, NK1, false>();
       }
       const Geometry geo = make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
       if (n_tokens <= 4) return with_short<64, 4, 4, 4, CAPTURE, IO, NK1>(geo);
@@ -1832,8 +1841,8 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
         // dense-shape layer of one sequence: 192 workgroups) is spread over
         // four times as many workgroups of one row per lane and two waves.
         if (heads * ((d_v + 31) / 32) < kComputeUnits)
-          return make_decode_geometry<128, 8, 1, 2, CAPTURE, IO, NK1>();
-        return make_decode_geometry<128, 8, 2, 4, CAPTURE, IO, NK1>();
+          return make_decode_geometry<128, 8, 1, 2, CAPTURE, IO, NK1, true>();
+        return make_decode_geometry<128, 8, 2, 4, CAPTURE, IO, NK1, false>();
       }
       Geometry geo;
       if constexpr (CAPTURE) {
@@ -1911,12 +1920,19 @@ uint64_t grid_blocks(uint32_t d_k, uint32_t d_v, uint32_t n_k_heads, uint32_t n_
   if (short_fits(geo, d_v, n_k_heads, n_v_heads)) {
     // Short grids pad the key heads to a power of two (at least 8).
     const uint64_t row_blocks = (d_v + geo.short_rows - 1) / geo.short_rows;
-    return (row_blocks << short_kh_bits(n_k_heads)) * (n_v_heads / n_k_heads) * n_seqs;
+    return (row_blocks << xcd_kh_bits(n_k_heads)) * (n_v_heads / n_k_heads) * n_seqs;
   }
-  // One-token grids pad each head's row blocks to a power of two.
   const uint64_t row_blocks = (d_v + geo.rows_per_block - 1) / geo.rows_per_block;
-  const uint64_t padded = geo.decode ? uint64_t(1) << ceil_log2(row_blocks) : row_blocks;
-  return padded * n_v_heads * n_seqs;
+  if (geo.decode) {
+    const uint32_t groups = n_v_heads / n_k_heads;
+    const bool wide = d_v >> kPackDv != 0 || n_k_heads >> kPackNk != 0 ||
+                      groups >> kPackGroups != 0;
+    // One-token grids pad the key heads to a power of two (at least 8), or
+    // (past the size word) each head's row blocks.
+    if (!wide && geo.xcd_order) return (row_blocks << xcd_kh_bits(n_k_heads)) * groups * n_seqs;
+    return (uint64_t(1) << ceil_log2(row_blocks)) * n_v_heads * n_seqs;
+  }
+  return row_blocks * n_v_heads * n_seqs;
 }
 
 hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
@@ -1930,12 +1946,13 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
 
   const uint64_t io = f.bf16 ? 2 : 4;
   if (geo.decode) {
-    // One token: grid x = (key head << rb_shift) | row block, the row blocks
-    // padded to 2^rb_shift; y = value head of the key head; z = sequence,
-    // one launch per 65535 sequences with every base moved to the launch's
-    // first sequence (sequences are independent and T = 1). Sizes past the
-    // size word take gdn_decode_wide: x = (value head << rb_shift) | row
-    // block, y = sequence.
+    // One token: grid x = (row block << kh_bits) | key head (XCD order) or
+    // (key head << rb_shift) | row block; y = value head of the key head; z
+    // = sequence, one launch per 65535 sequences with
+    // every base moved to the launch's first sequence (sequences are
+    // independent and T = 1). Sizes past the size word take
+    // gdn_decode_wide: x = (value head << rb_shift) | row block, y =
+    // sequence.
     constexpr uint32_t kMaxGrid = 65535;
     const uint32_t rb_shift = ceil_log2(row_blocks);
     const uint32_t groups = f.n_v_heads / f.n_k_heads;
@@ -1962,10 +1979,12 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
       t.q_scale = f.q_scale;
       hipError_t e;
       if (!wide) {
-        uint32_t sizes = f.d_v | rb_shift << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
+        const uint32_t bits = geo.xcd_order ? xcd_kh_bits(f.n_k_heads) : rb_shift;
+        const uint32_t gx = geo.xcd_order ? row_blocks << bits : f.n_k_heads << bits;
+        uint32_t sizes = f.d_v | bits << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
                          groups << (kPackDv + kPackRb + kPackNk);
         void *args[] = {&state_in, &k, &q, &g, &v, &beta, &sizes, &t};
-        e = hipLaunchKernel(geo.kernel, dim3(f.n_k_heads << rb_shift, groups, ns),
+        e = hipLaunchKernel(geo.kernel, dim3(gx, groups, ns),
                             dim3(geo.threads), args, 0, stream);
       } else {
         uint32_t d_v = f.d_v, n_v = f.n_v_heads, n_k = f.n_k_heads, magic = kh_magic;
@@ -1985,7 +2004,7 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
     // kh_bits) | key head; one launch per 65535 sequences.
     constexpr uint32_t kMaxGrid = 65535;
     const uint32_t row_blocks = (f.d_v + geo.short_rows - 1) / geo.short_rows;
-    const uint32_t kh_bits = short_kh_bits(f.n_k_heads);
+    const uint32_t kh_bits = xcd_kh_bits(f.n_k_heads);
     const uint32_t groups = f.n_v_heads / f.n_k_heads;
     uint32_t sizes = f.d_v | kh_bits << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
                      groups << (kPackDv + kPackRb + kShortNk) |
