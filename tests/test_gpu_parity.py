@@ -848,14 +848,19 @@ def close_special(gpu, expected, what):
 
 
 SPECIAL_SHAPES = [
-    # d_k, d_v, n_k, n_v, T, S: one-token and multi-token geometries, one row
-    # per lane (small grids) and two (256 workgroups or more), all D_k
+    # d_k, d_v, n_k, n_v, T, S: one-token and long multi-token geometries, one
+    # row per lane (small grids) and two (256 workgroups or more), all D_k
     (128, 72, 2, 8, 1, 2),
     (128, 96, 8, 96, 1, 1),
     (128, 72, 2, 8, 40, 2),
     (128, 96, 8, 96, 40, 1),
     (64, 40, 2, 8, 40, 2),
     (32, 24, 1, 4, 40, 3),
+    # short calls (2 to 8 tokens: the short kernel), every D_k
+    (128, 72, 2, 8, 4, 2),
+    (128, 40, 2, 8, 7, 2),
+    (64, 40, 2, 8, 3, 2),
+    (32, 24, 1, 4, 8, 3),
 ]
 
 
