@@ -743,7 +743,9 @@ GRAPH_CASES = {
     "multi_token": (WORKLOADS["prefill"].with_(n_tokens=100, n_seqs=2), {}),
     "multi_token_normk": (WORKLOADS["prefill"].with_(n_tokens=100, n_seqs=2),
                           dict(normalize_k=True)),
-    "capture": (WORKLOADS["spec_verify"], dict(capture=True)),
+    "capture": (WORKLOADS["spec_verify"], dict(capture=True)),           # short kernel
+    "short": (WORKLOADS["spec_verify"], {}),
+    "capture_long": (WORKLOADS["spec_verify"].with_(n_tokens=12), dict(capture=True)),
 }
 
 
@@ -751,7 +753,8 @@ GRAPH_CASES = {
 def test_graph_replay(case):
     """Captured into a HIP graph and replayed several times (with eager work and
     synchronisations between replays): every replay matches the eager call, for
-    the one-token, multi-token, key-normalised and capture kernels."""
+    the one-token kernel, the short kernel with and without capture, and the
+    general multi-token kernel plain, key-normalised and with capture."""
     w, opts = GRAPH_CASES[case]
     x = make_inputs(w)
     d = dev(x)
