@@ -1839,9 +1839,10 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
       if (one_token) {
         // A grid of two-row workgroups that leaves compute units idle (one
         // dense-shape layer of one sequence: 192 workgroups) is spread over
-        // four times as many workgroups of one row per lane and two waves.
+        // eight times as many workgroups of one row per lane and one wave
+        // (1,536 workgroups; two waves: 2.52 against 2.50 us, four: 2.63).
         if (heads * ((d_v + 31) / 32) < kComputeUnits)
-          return make_decode_geometry<128, 8, 1, 2, CAPTURE, IO, NK1, true>();
+          return make_decode_geometry<128, 8, 1, 1, CAPTURE, IO, NK1, true>();
         return make_decode_geometry<128, 8, 2, 4, CAPTURE, IO, NK1, false>();
       }
       Geometry geo;
