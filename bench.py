@@ -59,7 +59,7 @@ RESIDENT_TARGET_BYTES = 1 << 30  # input sets cycled per run: >= 4x the cache
 METRIC = "GDN decode µs/layer + state HBM GB/s (%peak); prefill tokens/s at n_tokens=512"
 KERNEL_NAME = "gdn_recurrent"      # multi-token forward calls
 DECODE_KERNEL_NAME = "gdn_decode"  # one-token forward calls
-SHORT_KERNEL_NAME = "gdn_short"    # 2 to 8 tokens
+SHORT_KERNEL_NAME = "gdn_short"    # 2 to 8 tokens, and 9 to 16 on small grids
 NAMES = ("q", "k", "v", "g", "beta", "state_in")
 # The headline line's other workloads: (name, timed steps, warm-up steps). Each
 # timed region covers tens of milliseconds of GPU work whatever --steps is
@@ -180,7 +180,8 @@ def workload_info(name: str, io: str = "f32"):
     w = WORKLOADS[name]
     if w.n_tokens == 1:
         kernel = DECODE_KERNEL_NAME
-    elif w.n_tokens <= 8:
+    elif w.n_tokens <= 8 or (w.n_tokens <= 16 and w.n_v_heads * w.n_seqs * w.d_v <= 16384
+                             and (not w.capture or w.d_k < 128)):
         kernel = SHORT_KERNEL_NAME
     else:
         kernel = KERNEL_NAME

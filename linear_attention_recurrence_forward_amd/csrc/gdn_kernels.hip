@@ -59,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "gdn_launch.h"
 
 namespace gdn {
@@ -1520,9 +1522,16 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_decode_wide(
 }
 
 // Sizes of a short multi-token launch in one 32-bit word: d_v in bits 0-10,
-// kh_bits in 11-14, n_k_heads in 15-21, n_v_heads / n_k_heads in 22-28,
-// n_tokens - 1 in 29-31.
-constexpr uint32_t kShortNk = 7, kShortGroups = 7, kShortTok = 3;
+// kh_bits in 11-13, n_k_heads in 14-20, n_v_heads / n_k_heads in 21-27,
+// n_tokens - 1 in 28-31.
+constexpr uint32_t kShortKb = 3, kShortNk = 7, kShortGroups = 7, kShortTok = 4;
+
+// f(std::integral_constant<int, I>{}) for each I in order: a token loop
+// unrolled with each token's index a compile-time constant.
+template <typename F, int... I>
+__device__ __forceinline__ void for_tokens(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 
 
 // Short multi-token calls (2 <= n_tokens <= NT; speculative
@@ -1556,7 +1565,11 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   constexpr uint32_t SL = KQ_BYTES / RB;
   constexpr uint32_t EPL = RB / IB;
   static_assert((EPL == 1 || EPL == 2) && SL <= 64 && SL * RB == KQ_BYTES, "k/q staging");
-  static_assert(NT >= 2 && NT <= 8, "2 to 8 tokens");
+  static_assert(NT >= 2 && NT <= 16, "2 to 16 tokens");
+  // Past 8 tokens, each token's columns are read from LDS two tokens ahead
+  // instead of all before the loop, and the state is requested before the
+  // (larger) k/q staging.
+  constexpr bool JIT = NT > 8;
   static_assert(DK % C == 0 && C % 4 == 0 && 64 % L == 0, "bad geometry");
   // Token t's k row is row 2t of the slot, its q row 2t + 1; wave w requests
   // rows w, w + WAVES, ... and parks them for the whole workgroup.
@@ -1564,10 +1577,10 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   constexpr int RPW = (2 * NT + WAVES - 1) / WAVES;  // rows per wave
 
   const uint32_t d_v = sizes & ((1u << kPackDv) - 1u);
-  const uint32_t kh_bits = (sizes >> kPackDv) & ((1u << kPackRb) - 1u);
-  const uint32_t n_k = (sizes >> (kPackDv + kPackRb)) & ((1u << kShortNk) - 1u);
-  const uint32_t groups = (sizes >> (kPackDv + kPackRb + kShortNk)) & ((1u << kShortGroups) - 1u);
-  const uint32_t n_tok = (sizes >> (kPackDv + kPackRb + kShortNk + kShortGroups)) + 1u;
+  const uint32_t kh_bits = (sizes >> kPackDv) & ((1u << kShortKb) - 1u);
+  const uint32_t n_k = (sizes >> (kPackDv + kShortKb)) & ((1u << kShortNk) - 1u);
+  const uint32_t groups = (sizes >> (kPackDv + kShortKb + kShortNk)) & ((1u << kShortGroups) - 1u);
+  const uint32_t n_tok = (sizes >> (kPackDv + kShortKb + kShortNk + kShortGroups)) + 1u;
   const uint32_t n_v = groups * n_k;
   const uint32_t kh = blockIdx.x & ((1u << kh_bits) - 1u);
   const uint32_t rb = blockIdx.x >> kh_bits;
@@ -1585,12 +1598,28 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   const uint64_t tok0 = (uint64_t)s * n_tok;  // (s, token 0) in token-major order
   auto tclamp = [&](uint32_t t) { return t < n_tok ? t : n_tok - 1; };
 
+  // The state rows (head_bytes is host-checked < 2^32, a multiple of
+  // ROW_BYTES).
+  const uint32_t head_bytes = d_v * ROW_BYTES;
+  const uint64_t head = ((uint64_t)s * n_v + vh) * d_v * DK;
+  const uint32_t cell = row * ROW_BYTES + 16 * sub;
+  f4 st[NV];
+  auto load_state = [&]() {
+    const rsrc_t s_in = buffer(state_in + head, head_bytes);
+#pragma unroll
+    for (int m = 0; m < NV; ++m) st[m] = load4_stream(s_in, cell + m * 16 * L);
+  };
+
   // g and beta: lane t requests token t's (clamped).
   const uint32_t gb_step = n_v * 4;
   const uint32_t gb_ext = (n_tok - 1) * gb_step + 4;
   const uint32_t tl = tclamp(lane);
   const float g_l = load1(buffer(g_in + tok0 * n_v + vh, gb_ext), tl * gb_step);
   const float b_l = load1(buffer(beta_in + tok0 * n_v + vh, gb_ext), tl * gb_step);
+  if constexpr (JIT) {
+    load_state();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // k and q rows: staging lane l holds elements EPL * l ... of each.
   const uint32_t kq_step = n_k * KQ_BYTES;
   const uint32_t kq_ext = (n_tok - 1) * kq_step + KQ_BYTES;
@@ -1614,15 +1643,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   typename Io<IO>::R1 vr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) vr[t] = Io<IO>::raw1(v_rs, row * IB, uniform(tclamp(t) * v_step));
-  // The state rows (head_bytes is host-checked < 2^32, a multiple of
-  // ROW_BYTES).
-  const uint32_t head_bytes = d_v * ROW_BYTES;
-  const uint64_t head = ((uint64_t)s * n_v + vh) * d_v * DK;
-  const uint32_t cell = row * ROW_BYTES + 16 * sub;
-  const rsrc_t s_in = buffer(state_in + head, head_bytes);
-  f4 st[NV];
-#pragma unroll
-  for (int m = 0; m < NV; ++m) st[m] = load4_stream(s_in, cell + m * 16 * L);
+  if constexpr (!JIT) load_state();
   __builtin_amdgcn_sched_barrier(0);
   const float alpha_l = expf(-g_l);
   __builtin_amdgcn_sched_barrier(0);
@@ -1641,81 +1662,152 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
     }
   }
   __syncthreads();
-  f4 kc[NT][NV], qc[NT][NV];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int m = 0; m < NV; ++m) {
-      kc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][0][m * 4 * L + 4 * sub]);
-      qc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][1][m * 4 * L + 4 * sub]);
+  if constexpr (!JIT) {
+    f4 kc[NT][NV], qc[NT][NV];
+  #pragma unroll
+    for (int t = 0; t < NT; ++t)
+  #pragma unroll
+      for (int m = 0; m < NV; ++m) {
+        kc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][0][m * 4 * L + 4 * sub]);
+        qc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][1][m * 4 * L + 4 * sub]);
+      }
+    // Per-token factors, wave-uniform: alpha, beta and (NK) the key row's
+    // 1 / sqrt(sum k^2 + kNormEps), folded into sk and delta.
+    float alpha[NT], bs[NT], inv[NT];
+  #pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      alpha[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_l), t));
+      const float beta = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b_l), t));
+      inv[t] = 1.f;
+      if constexpr (NORMK) {
+        float ss = 0.f;
+  #pragma unroll
+        for (int m = 0; m < NV; ++m)
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kc[t][m][e], kc[t][m][e], ss);
+        inv[t] = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
+      }
+      bs[t] = beta * inv[t];
     }
-  // Per-token factors, wave-uniform: alpha, beta and (NK) the key row's
-  // 1 / sqrt(sum k^2 + kNormEps), folded into sk and delta.
-  float alpha[NT], bs[NT], inv[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    alpha[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_l), t));
-    const float beta = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b_l), t));
-    inv[t] = 1.f;
-    if constexpr (NORMK) {
-      float ss = 0.f;
-#pragma unroll
-      for (int m = 0; m < NV; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kc[t][m][e], kc[t][m][e], ss);
-      inv[t] = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
-    }
-    bs[t] = beta * inv[t];
-  }
-  float v[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) v[t] = Io<IO>::widen1(vr[t]);
-  // The store addresses and q_scale, from kernel-argument memory: requested
-  // here and waited for once.
-  void *const out = a.output;
-  float *const s_out_p = a.state_out, *const cap_p = a.capture;
-  const float qsc = a.q_scale;
-  asm volatile("" ::"s"(out), "s"(s_out_p), "s"(cap_p), "s"(qsc));
-  // Every request has completed before the first store (the loop waits for
-  // no memory, so its stores, inside per-token branches, never delay a
-  // load's wait).
-  __builtin_amdgcn_s_waitcnt(kWaitVmAll);
+    float v[NT];
+  #pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = Io<IO>::widen1(vr[t]);
+    // The store addresses and q_scale, from kernel-argument memory: requested
+    // here and waited for once.
+    void *const out = a.output;
+    float *const s_out_p = a.state_out, *const cap_p = a.capture;
+    const float qsc = a.q_scale;
+    asm volatile("" ::"s"(out), "s"(s_out_p), "s"(cap_p), "s"(qsc));
+    // Every request has completed before the first store (the loop waits for
+    // no memory, so its stores, inside per-token branches, never delay a
+    // load's wait).
+    __builtin_amdgcn_s_waitcnt(kWaitVmAll);
 
-  // A row past d_v stores at offset head_bytes, outside its descriptor: the
-  // hardware drops it (the immediate offsets added stay below ROW_BYTES).
-  const uint32_t sc = ok ? cell : head_bytes;
-  const rsrc_t o_rs = buffer(static_cast<char *>(out) + v0, v_ext);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (t >= (int)n_tok) break;
-#pragma unroll
-    for (int m = 0; m < NV; ++m) st[m] *= alpha[t];
-    float part = 0.f;
-#pragma unroll
-    for (int m = 0; m < NV; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) part = __builtin_fmaf(st[m][e], kc[t][m][e], part);
-    const float d = __builtin_fmaf(-inv[t], group_sum<L>(part), v[t]) * bs[t];
-#pragma unroll
-    for (int m = 0; m < NV; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st[m][e] = __builtin_fmaf(d, kc[t][m][e], st[m][e]);
-    if constexpr (CAPTURE) {
-      const rsrc_t ct = buffer(cap_p + ((tok0 + t) * n_v + vh) * d_v * DK, head_bytes);
-#pragma unroll
-      for (int m = 0; m < NV; ++m) store4_stream(ct, sc + m * 16 * L, st[m]);
+    // A row past d_v stores at offset head_bytes, outside its descriptor: the
+    // hardware drops it (the immediate offsets added stay below ROW_BYTES).
+    const uint32_t sc = ok ? cell : head_bytes;
+    const rsrc_t o_rs = buffer(static_cast<char *>(out) + v0, v_ext);
+  #pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= (int)n_tok) break;
+  #pragma unroll
+      for (int m = 0; m < NV; ++m) st[m] *= alpha[t];
+      float part = 0.f;
+  #pragma unroll
+      for (int m = 0; m < NV; ++m)
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) part = __builtin_fmaf(st[m][e], kc[t][m][e], part);
+      const float d = __builtin_fmaf(-inv[t], group_sum<L>(part), v[t]) * bs[t];
+  #pragma unroll
+      for (int m = 0; m < NV; ++m)
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) st[m][e] = __builtin_fmaf(d, kc[t][m][e], st[m][e]);
+      if constexpr (CAPTURE) {
+        const rsrc_t ct = buffer(cap_p + ((tok0 + t) * n_v + vh) * d_v * DK, head_bytes);
+  #pragma unroll
+        for (int m = 0; m < NV; ++m) store4_stream(ct, sc + m * 16 * L, st[m]);
+      }
+      float py = 0.f;
+  #pragma unroll
+      for (int m = 0; m < NV; ++m)
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) py = __builtin_fmaf(st[m][e], qc[t][m][e], py);
+      const float y = group_sum<L>(py);
+      if (sub == 0 && ok) Io<IO>::store1(o_rs, row * IB, uniform(t * v_step), y * qsc);
     }
-    float py = 0.f;
+    const rsrc_t s_out = buffer(s_out_p + head, head_bytes);
 #pragma unroll
-    for (int m = 0; m < NV; ++m)
+    for (int m = 0; m < NV; ++m) store4_stream(s_out, sc + m * 16 * L, st[m]);
+  } else {
+    // The store addresses and q_scale, then every request complete (as above).
+    void *const out = a.output;
+    float *const s_out_p = a.state_out, *const cap_p = a.capture;
+    const float qsc = a.q_scale;
+    asm volatile("" ::"s"(out), "s"(s_out_p), "s"(cap_p), "s"(qsc));
+    __builtin_amdgcn_s_waitcnt(kWaitVmAll);
+    const uint32_t sc = ok ? cell : head_bytes;
+    const rsrc_t o_rs = buffer(static_cast<char *>(out) + v0, v_ext);
+    f4 kc[NT][NV], qc[NT][NV];  // indexed by compile-time tokens: a few live
+    auto cols = [&](int t) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) py = __builtin_fmaf(st[m][e], qc[t][m][e], py);
-    const float y = group_sum<L>(py);
-    if (sub == 0 && ok) Io<IO>::store1(o_rs, row * IB, uniform(t * v_step), y * qsc);
+      for (int m = 0; m < NV; ++m) {
+        kc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][0][m * 4 * L + 4 * sub]);
+        qc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][1][m * 4 * L + 4 * sub]);
+      }
+    };
+    cols(0);
+    cols(1);
+    float v[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = Io<IO>::widen1(vr[t]);
+    for_tokens(
+        [&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          if (t >= (int)n_tok) return;
+          if constexpr (t + 2 < NT) cols(t + 2);
+          const float alpha =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_l), t));
+          const float beta =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b_l), t));
+          float inv = 1.f;
+          if constexpr (NORMK) {
+            float ss = 0.f;
+#pragma unroll
+            for (int m = 0; m < NV; ++m)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kc[t][m][e], kc[t][m][e], ss);
+            inv = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
+          }
+#pragma unroll
+          for (int m = 0; m < NV; ++m) st[m] *= alpha;
+          float part = 0.f;
+#pragma unroll
+          for (int m = 0; m < NV; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part = __builtin_fmaf(st[m][e], kc[t][m][e], part);
+          const float d = __builtin_fmaf(-inv, group_sum<L>(part), v[t]) * (beta * inv);
+#pragma unroll
+          for (int m = 0; m < NV; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[m][e] = __builtin_fmaf(d, kc[t][m][e], st[m][e]);
+          if constexpr (CAPTURE) {
+            const rsrc_t ct = buffer(cap_p + ((tok0 + t) * n_v + vh) * d_v * DK, head_bytes);
+#pragma unroll
+            for (int m = 0; m < NV; ++m) store4_stream(ct, sc + m * 16 * L, st[m]);
+          }
+          float py = 0.f;
+#pragma unroll
+          for (int m = 0; m < NV; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) py = __builtin_fmaf(st[m][e], qc[t][m][e], py);
+          const float y = group_sum<L>(py);
+          if (sub == 0 && ok) Io<IO>::store1(o_rs, row * IB, uniform(t * v_step), y * qsc);
+        },
+        std::make_integer_sequence<int, NT>{});
+    const rsrc_t s_out = buffer(s_out_p + head, head_bytes);
+#pragma unroll
+    for (int m = 0; m < NV; ++m) store4_stream(s_out, sc + m * 16 * L, st[m]);
   }
-  const rsrc_t s_out = buffer(s_out_p + head, head_bytes);
-#pragma unroll
-  for (int m = 0; m < NV; ++m) store4_stream(s_out, sc + m * 16 * L, st[m]);
 }
 
 // ---------------------------------------------------------------- geometry
@@ -1808,9 +1900,20 @@ constexpr Geometry make_decode_geometry() {
 // Compute units of an MI355X.
 constexpr uint64_t kComputeUnits = 256;
 
+// Calls of 9 to 16 tokens take gdn_short only up to this many rows (n_v_heads
+// * n_seqs * d_v), and at D_k = 128 only without capture: past it the general
+// kernel's two-row layout does more work per request (the 64-sequence batch
+// of 16 tokens: 97.0 against 79.1 us; a 12-token D_k = 64 batch 25.7 against
+// 23.1 us); below it gdn_short (4-token-verify shape at 9, 12 and 16 tokens:
+// 5.70 -> 4.96, 6.44 -> 5.50, 6.90 -> 6.26 us; D_k = 64 at 12 tokens 4.97 ->
+// 4.03 us, with capture 5.44 -> 4.42 us). D_k = 128 capture calls of 12 or
+// 16 tokens measured 2-5% slower on it.
+constexpr uint64_t kShort16MaxRows = 16384;
+
 // heads: n_v_heads * n_seqs.
 template <bool CAPTURE, typename IO, int NK>
 Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
+  const bool short16 = n_tokens <= 16 && heads * d_v <= kShort16MaxRows;
   const bool one_token = n_tokens == 1;
   constexpr int NK1 = NK == 2 ? 1 : NK;  // one-token calls have no ring group
   switch (d_k) {
@@ -1819,6 +1922,7 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
       const Geometry geo = make_geometry<32, 4, 2, 4, 4, CAPTURE, IO, NK>();
       if (n_tokens <= 4) return with_short<32, 4, 4, 4, CAPTURE, IO, NK1>(geo);
       if (n_tokens <= 8) return with_short<32, 4, 4, 8, CAPTURE, IO, NK1>(geo);
+      if (short16) return with_short<32, 4, 4, 16, CAPTURE, IO, NK1>(geo);
       return geo;
     }
     case 64: {
@@ -1833,6 +1937,7 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
       const Geometry geo = make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
       if (n_tokens <= 4) return with_short<64, 4, 4, 4, CAPTURE, IO, NK1>(geo);
       if (n_tokens <= 8) return with_short<64, 4, 4, 8, CAPTURE, IO, NK1>(geo);
+      if (short16) return with_short<64, 4, 4, 16, CAPTURE, IO, NK1>(geo);
       return geo;
     }
     case 128: {
@@ -1860,6 +1965,7 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
       }
       if (n_tokens <= 4) return with_short<128, 8, 4, 4, CAPTURE, IO, NK1>(geo);
       if (n_tokens <= 8) return with_short<128, 8, 4, 8, CAPTURE, IO, NK1>(geo);
+      if (short16 && !CAPTURE) return with_short<128, 8, 4, 16, CAPTURE, IO, NK1>(geo);
       return geo;
     }
     default:
@@ -2007,9 +2113,9 @@ hipError_t enqueue_forward(const ForwardArgs &f, hipStream_t stream) {
     const uint32_t row_blocks = (f.d_v + geo.short_rows - 1) / geo.short_rows;
     const uint32_t kh_bits = xcd_kh_bits(f.n_k_heads);
     const uint32_t groups = f.n_v_heads / f.n_k_heads;
-    uint32_t sizes = f.d_v | kh_bits << kPackDv | f.n_k_heads << (kPackDv + kPackRb) |
-                     groups << (kPackDv + kPackRb + kShortNk) |
-                     (f.n_tokens - 1) << (kPackDv + kPackRb + kShortNk + kShortGroups);
+    uint32_t sizes = f.d_v | kh_bits << kPackDv | f.n_k_heads << (kPackDv + kShortKb) |
+                     groups << (kPackDv + kShortKb + kShortNk) |
+                     (f.n_tokens - 1) << (kPackDv + kShortKb + kShortNk + kShortGroups);
     const uint64_t state_seq = (uint64_t)f.n_v_heads * f.d_v * f.d_k;                // floats
     const uint64_t kq_seq = (uint64_t)f.n_tokens * f.n_k_heads * f.d_k * io;         // bytes
     const uint64_t v_seq = (uint64_t)f.n_tokens * f.n_v_heads * f.d_v * io;          // bytes

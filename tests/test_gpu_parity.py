@@ -745,6 +745,7 @@ GRAPH_CASES = {
                           dict(normalize_k=True)),
     "capture": (WORKLOADS["spec_verify"], dict(capture=True)),           # short kernel
     "short": (WORKLOADS["spec_verify"], {}),
+    "short16": (WORKLOADS["spec_verify"].with_(n_tokens=14), {}),
     "capture_long": (WORKLOADS["spec_verify"].with_(n_tokens=12), dict(capture=True)),
 }
 
@@ -859,11 +860,13 @@ SPECIAL_SHAPES = [
     (128, 96, 8, 96, 40, 1),
     (64, 40, 2, 8, 40, 2),
     (32, 24, 1, 4, 40, 3),
-    # short calls (2 to 8 tokens: the short kernel), every D_k
+    # short calls (2 to 16 tokens: the short kernel), every D_k
     (128, 72, 2, 8, 4, 2),
     (128, 40, 2, 8, 7, 2),
     (64, 40, 2, 8, 3, 2),
     (32, 24, 1, 4, 8, 3),
+    (64, 40, 2, 8, 12, 2),
+    (128, 40, 2, 8, 16, 2),
 ]
 
 
@@ -1114,6 +1117,12 @@ def test_one_token_sizes_past_the_size_word(shape, capture):
     (32, 2047, 1, 1, 4, 1),
     (32, 2048, 1, 1, 4, 1),
     (32, 37, 2, 6, 6, 3),
+    (128, 5, 3, 6, 13, 3),      # 9 to 16 tokens: the 16-token instance (capture at
+    (64, 37, 2, 6, 16, 2),      # D_k = 128 takes the general kernel)
+    (32, 24, 1, 4, 11, 3),
+    (64, 2047, 1, 1, 10, 1),    # 2047 rows, within the 16-token instance's row limit
+    (128, 128, 8, 128, 9, 1),   # 16,384 rows: the limit
+    (128, 128, 8, 136, 9, 1),   # past it: the general kernel
 ], ids=lambda s: "dk%d_dv%d_hk%d_hv%d_t%d_s%d" % s)
 def test_short_sizes_at_and_past_the_size_word(shape, capture):
     """Calls of 2 to 8 tokens take the short kernel when their
