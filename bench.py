@@ -27,8 +27,10 @@ Prints one JSON line. The single-layer decode line (the default) also carries
 one object per other workload of the headline metric: "prefill" (512-token
 prefill, tokens/s), "batched_decode", "spec_verify" and "rollback", each with
 its own roofline and CPU baseline, "state_copy", the library's copy kernel
-moving exactly the decode call's state bytes, measured the same way: the floor
-beside the decode figure, and "tiny", the smallest configuration (D_k = D_v =
+(the rollback kernel, index 0) moving exactly the decode call's state bytes,
+measured the same way: a reference beside the decode figure (it reads its
+index before its copy, so it is no lower bound), and "tiny", the smallest
+configuration (D_k = D_v =
 32, 8 tokens, 2 value heads), whose call is all launch and latency
 (--no-extra leaves them out). Every CPU
 baseline times the oracle on one core and on all the host's cores (threads
@@ -166,9 +168,9 @@ def workload_info(name: str, io: str = "f32"):
     spec_verify shape (one state slice read and written per sequence, plus the
     index array); 'state_copy' is the same copy kernel on the single-layer
     decode shape (one token, index 0): it reads and writes exactly that call's
-    state bytes and nothing else, the floor the decode call is measured
-    against (the HIP runtime's own device-to-device copy of those bytes is
-    slower)."""
+    state bytes and nothing else, a reference beside the decode call (it
+    reads its index before the copy, so it is no lower bound; the HIP
+    runtime's own device-to-device copy of those bytes is slower)."""
     if name == "rollback":
         w = WORKLOADS["spec_verify"]
         return (w, "gdn_rollback_kernel", w.state_bytes() + 4 * w.n_seqs,
@@ -779,7 +781,7 @@ def main(argv=None):
     if not args.no_cpu_baseline and plain:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, rollback=m["rollback"])
     for e in extras:
-        # The copy floor is a reference point, not a workload of the metric.
+        # The state copy is a reference point, not a workload of the metric.
         cpu = (None if args.no_cpu_baseline or e["name"] == "state_copy" else
                cpu_baseline(e["w"], args.cpu_seconds, rollback=e["rollback"]))
         line[e["name"]] = extra_object(e, cpu)
