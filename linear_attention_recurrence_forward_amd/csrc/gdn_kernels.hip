@@ -45,15 +45,19 @@
 //   * Every access goes through a buffer resource (a 128-bit scalar
 //     descriptor: base address and size in bytes) plus a 32-bit per-lane byte
 //     offset that is fixed for the whole loop; per-token bases advance with
-//     scalar arithmetic only. Every offset is computed in range; the
-//     descriptor size is a bound, not a mechanism the code relies on.
+//     scalar arithmetic only. Every load offset is computed in range (rows
+//     past d_v read a valid row); the one-token and short kernels give the
+//     stores of such rows the offset of the descriptor's size, which the
+//     hardware drops, so that no store sits in a branch.
 //   * Optionally (NK) every key row is used L2-normalised, its factor folded
 //     into sk and delta: computed per token, or a ring group ahead in calls of
 //     16 tokens or more.
 // Kernels: gdn_decode for a single decode token (HBM-bound on the state read
 // and write; straight-line code, every input base and its sizes preloaded
 // into scalar registers), gdn_decode_wide for one-token calls with sizes
-// past gdn_decode's size word, and gdn_recurrent for multi-token calls
+// past gdn_decode's size word, gdn_short for 2 to 8 tokens (9 to 16 on small
+// grids; the one-token kernel's form, every input requested before an
+// unrolled token loop), and gdn_recurrent for longer multi-token calls
 // (bound by VALU issue; two rows per lane share each k/q register).
 
 #include <hip/hip_runtime.h>
@@ -1481,9 +1485,9 @@ uint32_t xcd_kh_bits(uint32_t n_k_heads) {
 // one of the n_v_heads / n_k_heads value heads of a key head; z = sequence
 // within the launch. vh = kh + g * n_k_heads (the modulo GQA map, no
 // division). XCD order against memory order: single-layer decode (one row
-// per lane, 768 workgroups) 2.61 -> 2.52 us, bf16 2.68 -> 2.57 us; the
-// 64-sequence batch (two rows per lane, 16,384 workgroups) 41.8 -> 42.0 us,
-// so that grid keeps the memory order.
+// per lane, then 768 two-wave workgroups) 2.61 -> 2.52 us, bf16 2.68 ->
+// 2.57 us; the 64-sequence batch (two rows per lane, 8,192 workgroups)
+// 41.8 -> 42.0 us, so that grid keeps the memory order.
 template <int DK, int C, int R, int WAVES, bool CAPTURE, typename IO, int NK, bool XO>
 __global__ __launch_bounds__(WAVES * 64) void gdn_decode(
     const float *state_in, const void *k_in, const void *q_in, const float *g_in,
@@ -1865,8 +1869,9 @@ constexpr Geometry make_decode_geometry() {
 //                where that grid has fewer workgroups than the chip has
 //                compute units: one sequence of the dense shape (192
 //                workgroups) runs 3.14 -> 2.93 us with one row per lane and
-//                two waves (768 workgroups); from two sequences on the
-//                two-row grid is faster again (4.05 vs 4.29 us).
+//                two waves (768 workgroups; one wave since, below); from two
+//                sequences on the two-row grid is faster again (4.05 vs
+//                4.29 us).
 //   2 to 8 tokens: gdn_short, one row per lane (8 cells at D_k = 128, 4
 //                below), 4 waves, every input requested before the token
 //                loop and the k/q rows staged once per workgroup (general
@@ -1879,20 +1884,21 @@ constexpr Geometry make_decode_geometry() {
 //                4-token D_k = 64 verify 3.43 -> 2.64 us). Staging the rows
 //                per wave instead of per workgroup put four times the row
 //                requests ahead of the state's in each compute unit's
-//                queue (4-token verify 5.29 us, 8 tokens 9.12 us). Past 8
-//                tokens a token loop reading each token's columns during the
-//                previous one lost to the general kernel (16 tokens 8.38
-//                against 6.88 us; the 64-sequence batch 114 against 80 us).
-//   two or more: two rows per lane (each k/q register feeds two rows, which
+//                queue (4-token verify 5.29 us, 8 tokens 9.12 us). 9 to 16
+//                tokens: the unrolled 16-token instance on grids of at most
+//                16,384 rows (see kShort16MaxRows); a rolled token loop
+//                reading each token's columns during the previous one had
+//                lost to the general kernel (16 tokens 8.38 against 6.88 us).
+//   longer     : two rows per lane (each k/q register feeds two rows, which
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
 //                tokens against one row per lane), 16 lanes per row, 4 waves.
 //                Without capture an eight-token prefetch ring and lazy group
 //                (512-token prefill 221 -> 206 us against four tokens without
 //                the lazy form). With capture, which runs eagerly and is bound
 //                by its writes, one row per lane (twice the waves) and a
-//                four-token ring: 4-token verify 5.88 -> 5.64 us. The two-row geometry was
-//                best or within 2% of the best measured variant from 2 tokens
-//                up (2 to 512), so one token is the only short-run case. At
+//                four-token ring: 4-token verify 5.88 -> 5.64 us. Among this
+//                kernel's geometries the two-row one was best or within 2% of
+//                the best measured variant from 2 tokens up (2 to 512). At
 //                D_k = 64, 16 lanes per row (4 cells each), two waves and an
 //                eight-token ring (twice the waves of 8 lanes per row with
 //                8 cells): 512-token prefill 139 -> 96 us, 16 tokens 8.1 ->
