@@ -57,6 +57,31 @@ def test_algorithmic_bytes(bench, name, shape, capture, total):
     assert alg16 == expected_bytes(*shape, capture=capture, io=2)
 
 
+@pytest.mark.parametrize("shape,capture,kernel", [
+    ((128, 128, 16, 48, 1, 1), False, "gdn_decode"),
+    ((128, 128, 8, 8, 2, 8), True, "gdn_short"),
+    ((32, 32, 1, 2, 8, 1), False, "gdn_short"),
+    ((128, 128, 8, 8, 12, 8), False, "gdn_short"),      # 8,192 rows
+    ((128, 128, 8, 8, 12, 8), True, "gdn_recurrent"),   # D_k = 128 capture past 8
+    ((64, 64, 8, 8, 16, 8), True, "gdn_short"),
+    ((128, 128, 8, 136, 9, 1), False, "gdn_recurrent"),  # 17,408 rows
+    ((128, 128, 8, 8, 17, 8), False, "gdn_recurrent"),
+])
+def test_kernel_of_a_workload(bench, shape, capture, kernel):
+    """The kernel a bench line names follows the library's choice: one token
+    the one-token kernel, 2 to 8 tokens the short kernel, 9 to 16 the short
+    kernel on grids of at most 16,384 rows (not with capture at D_k = 128),
+    longer the general one."""
+    dk, dv, hk, hv, t, s = shape
+    WORKLOADS["kernel_probe"] = WORKLOADS["spec_verify"].with_(
+        name="kernel_probe", d_k=dk, d_v=dv, n_k_heads=hk, n_v_heads=hv, n_tokens=t,
+        n_seqs=s, capture=capture)
+    try:
+        assert bench.workload_info("kernel_probe")[1] == kernel
+    finally:
+        del WORKLOADS["kernel_probe"]
+
+
 def test_rollback_bytes(bench):
     w, kernel, alg, _ = bench.workload_info("rollback")
     state = w.d_k * w.d_v * w.n_v_heads * w.n_seqs
