@@ -1668,9 +1668,9 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
   __syncthreads();
   if constexpr (!JIT) {
     f4 kc[NT][NV], qc[NT][NV];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < NT; ++t)
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < NV; ++m) {
         kc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][0][m * 4 * L + 4 * sub]);
         qc[t][m] = *reinterpret_cast<const f4 *>(&slot[t][1][m * 4 * L + 4 * sub]);
@@ -1678,23 +1678,23 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
     // Per-token factors, wave-uniform: alpha, beta and (NK) the key row's
     // 1 / sqrt(sum k^2 + kNormEps), folded into sk and delta.
     float alpha[NT], bs[NT], inv[NT];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < NT; ++t) {
       alpha[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha_l), t));
       const float beta = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b_l), t));
       inv[t] = 1.f;
       if constexpr (NORMK) {
         float ss = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < NV; ++m)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(kc[t][m][e], kc[t][m][e], ss);
         inv[t] = __builtin_amdgcn_rsqf(group_sum<L>(ss) + kNormEps);
       }
       bs[t] = beta * inv[t];
     }
     float v[NT];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < NT; ++t) v[t] = Io<IO>::widen1(vr[t]);
     // The store addresses and q_scale, from kernel-argument memory: requested
     // here and waited for once.
@@ -1711,30 +1711,30 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_short(
     // hardware drops it (the immediate offsets added stay below ROW_BYTES).
     const uint32_t sc = ok ? cell : head_bytes;
     const rsrc_t o_rs = buffer(static_cast<char *>(out) + v0, v_ext);
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t >= (int)n_tok) break;
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < NV; ++m) st[m] *= alpha[t];
       float part = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < NV; ++m)
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) part = __builtin_fmaf(st[m][e], kc[t][m][e], part);
       const float d = __builtin_fmaf(-inv[t], group_sum<L>(part), v[t]) * bs[t];
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < NV; ++m)
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) st[m][e] = __builtin_fmaf(d, kc[t][m][e], st[m][e]);
       if constexpr (CAPTURE) {
         const rsrc_t ct = buffer(cap_p + ((tok0 + t) * n_v + vh) * d_v * DK, head_bytes);
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < NV; ++m) store4_stream(ct, sc + m * 16 * L, st[m]);
       }
       float py = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < NV; ++m)
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) py = __builtin_fmaf(st[m][e], qc[t][m][e], py);
       const float y = group_sum<L>(py);
       if (sub == 0 && ok) Io<IO>::store1(o_rs, row * IB, uniform(t * v_step), y * qsc);
