@@ -1971,7 +1971,9 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
       }
       if (n_tokens <= 4) return with_short<128, 8, 4, 4, CAPTURE, IO, NK1>(geo);
       if (n_tokens <= 8) return with_short<128, 8, 4, 8, CAPTURE, IO, NK1>(geo);
-      if (short16 && !CAPTURE) return with_short<128, 8, 4, 16, CAPTURE, IO, NK1>(geo);
+      if constexpr (!CAPTURE) {
+        if (short16) return with_short<128, 8, 4, 16, CAPTURE, IO, NK1>(geo);
+      }
       return geo;
     }
     default:

@@ -592,6 +592,64 @@ def test_bf16_exact_probe():
             assert_equal(g_, e_, f"bf16 exact probe {what}")
 
 
+# Shapes that reach every compiled forward kernel instance (per D_k): the
+# one-token kernel on a small grid (one row per lane) and on one of 256 or
+# more two-row workgroups, and its form past the size word, the short
+# kernel's 4-, 8- and 16-token instances, and the general kernel on a small
+# grid (one row per lane) and a large one (two rows per lane; with capture
+# one row per lane), with key normalisation per token (fewer than 16
+# tokens) and a ring group ahead (20 tokens). d_v, n_k, n_v, T, S.
+INSTANCE_CLASSES = {
+    "decode_small": (24, 2, 4, 1, 1),
+    "decode_large": (40, 16, 64, 1, 4),
+    "short4": (24, 2, 4, 3, 2),
+    "short8": (24, 2, 4, 6, 2),
+    "short16": (24, 2, 4, 13, 2),
+    "general_small": (24, 2, 4, 20, 2),
+    "general_large": (40, 16, 64, 20, 4),
+    # 9 to 15 tokens on the general kernel (per-token key factors): past the
+    # short kernel's row limit (two rows per lane), and past its size word on
+    # a small grid (one row per lane)
+    "general_mid_large": (40, 16, 128, 12, 4),
+    "general_mid_wide": (2100, 1, 1, 12, 1),
+    # one token past the one-token kernel's size word, small and large grids
+    "decode_wide_small": (2100, 1, 2, 1, 1),
+    "decode_wide_large": (2100, 1, 8, 1, 2),
+}
+
+
+@pytest.mark.parametrize("normalize_k", [False, True], ids=["rawk", "normk"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("capture", [False, True], ids=["plain", "capture"])
+@pytest.mark.parametrize("cls", sorted(INSTANCE_CLASSES))
+@pytest.mark.parametrize("dk", [32, 64, 128])
+def test_every_kernel_instance(dk, cls, capture, io, normalize_k):
+    """Every template instance the library compiles runs on some case here
+    (head dimension x kernel and geometry x capture x I/O type x key
+    normalisation), against the oracle: f32 within the usual tolerance, bf16
+    output within one bf16 step of the bf16 oracle."""
+    dv, hk, hv, t, s_ = INSTANCE_CLASSES[cls]
+    w = Workload("inst", 0, dk, dv, hk, hv, t, s_)
+    x = make_inputs(w, seed=300 + dk + 7 * t + hv)
+    bq = q_scale_bits_for(dk)
+    what = f"dk={dk} {cls} capture={capture} {io} normalize_k={normalize_k}"
+    if io == "f32":
+        got = run(x, q_scale_bits=bq, capture=capture, normalize_k=normalize_k)
+        exp = ref(x, q_scale_bits=bq, capture=capture, normalize_k=normalize_k)
+        close(got[0], exp[0], f"{what} output")
+    else:
+        bits, _ = bf16_inputs(x)
+        got = run_bf16(x, bits, q_scale_bits=bq, capture=capture, normalize_k=normalize_k)
+        exp = oracle.reference_bf16(bits["q"], bits["k"], bits["v"], x["g"], x["beta"],
+                                    x["state_in"], q_scale_bits=bq, capture=capture,
+                                    normalize_k=normalize_k)
+        bf16_close(got[0], exp[0], f"{what} output")
+    close(got[1], exp[1], f"{what} state_out")
+    if capture:
+        close(got[2], exp[2], f"{what} capture")
+        assert_equal(got[2][:, -1], got[1], f"{what} capture[T-1] == state_out")
+
+
 # ------------------------------------------------------------------ rollback
 
 @pytest.mark.parametrize("name", ["spec_verify", "tiny"])
