@@ -51,7 +51,8 @@
 //     hardware drops, so that no store sits in a branch.
 //   * Optionally (NK) every key row is used L2-normalised, its factor folded
 //     into sk and delta: computed per token, or a ring group ahead in calls of
-//     16 tokens or more.
+//     16 tokens or more (with shared staging, by the wave that stages the row,
+//     which stages it scaled).
 // Kernels: gdn_decode for a single decode token (HBM-bound on the state read
 // and write; straight-line code, every input base and its sizes preloaded
 // into scalar registers), gdn_decode_wide for one-token calls with sizes
@@ -82,6 +83,7 @@ constexpr int kDppRor8 = 0x128;       // row_ror:8: lane -> lane ^ 8 (per 16)
 constexpr int kDppShr1 = 0x111;       // row_shr:1: lane - 1 (per 16)
 constexpr int kDppShr2 = 0x112;       // row_shr:2: lane - 2 (per 16)
 constexpr int kDppShr4 = 0x114;       // row_shr:4: lane - 4 (per 16)
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15: lane 15 of the row below
 // ds_swizzle bit mode (offset bit 15 = 0): and_mask 0x1f, or_mask 0,
 // xor_mask 0x10 -> lane ^ 16 within each group of 32.
 constexpr int kSwizzleXor16 = 0x1F | (0x10 << 10);
@@ -642,8 +644,29 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
     }
   };
 
-  // Key normalisation in multi-token calls: the factors 1 / sqrt(sum k^2 +
-  // kNormEps) of a ring group's NB key rows are computed one group ahead.
+  // Shared staging (multi-token calls without capture, and without the
+  // per-token key normalisation, which sums each key row in the wave that
+  // loads it; the group-ahead normalisation computes each row's factor in
+  // the wave that stages it, see staged_norms). All waves of a workgroup need the same k and q rows, so
+  // instead of every wave loading every token's rows, each wave loads NB /
+  // WAVES tokens of the next ring group and stages them, widened to f32, in
+  // a workgroup LDS block (two of them, one per alternate group); one
+  // workgroup barrier per group publishes the block. Every wave of a
+  // workgroup runs the same token loop, so every wave reaches every barrier.
+  // Four times fewer row requests, and no staging write per token: the
+  // 512-token prefill went from 177 to 169 us, its key-normalised form from
+  // 204 to 187 us. Not at D_k = 32, where a wave's rows are a quarter as
+  // long and the per-group barrier costs more than the loads it saves
+  // (a D_k = 32 prefill ran 106 us without it, 118 us with it).
+  constexpr bool SHARE = !CAPTURE && NK != 1 && DK >= 64 && NB % WAVES == 0;
+  constexpr int TPW = SHARE ? NB / WAVES : 1;  // tokens a wave stages per group
+  // Group-ahead key normalisation with shared staging: the staged keys are
+  // scaled by their factors, and step() runs as without normalisation.
+  constexpr bool SNORM = SHARE && NK == 2;
+
+  // Key normalisation in multi-token calls without shared staging (D_k = 32,
+  // capture): the factors 1 / sqrt(sum k^2 + kNormEps) of a ring group's NB
+  // key rows are computed one group ahead.
   // LPT = 64 / NB lanes share a token's row, each summing the squares of EPT
   // consecutive elements; a butterfly over the LPT lanes and one reciprocal
   // square root give the token's factor, parked in a per-wave LDS slot and
@@ -651,7 +674,7 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
   // square root per group instead of a wave-wide sum per token. A lane's
   // slice is requested in KP parts (two when it holds 8 or more elements, at
   // the group's start and middle) to bound the registers in flight.
-  constexpr bool GNORM = NK == 2;
+  constexpr bool GNORM = NK == 2 && !SHARE;
   constexpr uint32_t LPT = 64 / NB;
   constexpr uint32_t EPT = DK / LPT;
   static_assert(!GNORM || EPT == 2 || EPT % 4 == 0, "key row split");
@@ -732,33 +755,79 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
     return c;
   };
 
-  // Shared staging (multi-token calls without capture, and without the
-  // per-token key normalisation, which sums each key row in the wave that
-  // loads it). All waves of a workgroup need the same k and q rows, so
-  // instead of every wave loading every token's rows, each wave loads NB /
-  // WAVES tokens of the next ring group and stages them, widened to f32, in
-  // a workgroup LDS block (two of them, one per alternate group); one
-  // workgroup barrier per group publishes the block. Every wave of a
-  // workgroup runs the same token loop, so every wave reaches every barrier.
-  // Four times fewer row requests, and no staging write per token: the
-  // 512-token prefill went from 177 to 169 us, its key-normalised form from
-  // 204 to 187 us. Not at D_k = 32, where a wave's rows are a quarter as
-  // long and the per-group barrier costs more than the loads it saves
-  // (a D_k = 32 prefill ran 106 us without it, 118 us with it).
-  constexpr bool SHARE = !CAPTURE && NK != 1 && DK >= 64 && NB % WAVES == 0;
-  constexpr int TPW = SHARE ? NB / WAVES : 1;  // tokens a wave stages per group
   __shared__ __attribute__((aligned(16)))
   float grp_lds[SHARE ? 2 : 1][SHARE ? NB : 1][SHARE ? 2 * DK : 1];
-  // This lane's part of a token's rows, widened, into a staged row pair.
-  auto stage_rows = [&](const Tok &x, float *dst) {
+  // This lane's part of a token's rows, widened, into a staged row pair; the
+  // key row scaled by ks (SNORM).
+  auto stage_rows = [&](const Tok &x, float *dst, float ks) {
     float kw[EPL], qw[EPL];
     widen<IO, EPL>(x.kr, kw);
     widen<IO, EPL>(x.qr, qw);
     if (SLANES == 64 || lane < SLANES) {
 #pragma unroll
       for (uint32_t e = 0; e < EPL; ++e) {
-        dst[EPL * lane + e] = kw[e];
+        dst[EPL * lane + e] = SNORM ? kw[e] * ks : kw[e];
         dst[DK + EPL * lane + e] = qw[e];
+      }
+    }
+  };
+  // SNORM: the factors 1 / sqrt(sum k^2 + kNormEps) of the TPW (2 or 4) key
+  // rows this wave stages, from the parts its lanes hold. Each lane sums the
+  // squares of its part of every row; swapping the wave halves of rows 2i
+  // and 2i+1 and adding leaves row 2i's partials in lanes 0-31 and row
+  // 2i+1's in lanes 32-63 of one register. With four rows, swapping the odd
+  // 16-lane rows of the first such register with the even ones of the second
+  // and adding gives one register whose 16-lane rows hold the partials of
+  // key rows 0, 2, 1 and 3; a butterfly within 16 lanes completes every sum.
+  // With two rows the butterfly leaves half sums, and adding the row below's
+  // lane 15 completes them in lanes 31 and 63. Wave-uniform results, a few
+  // cross-lane steps per group for the wave's rows instead of a butterfly
+  // and a factor multiply per token.
+  auto staged_norms = [&](const Tok (&b)[TPW], float (&inv)[TPW]) {
+    static_assert(!SNORM || TPW == 2 || TPW == 4, "two or four staged rows");
+    if constexpr (SNORM) {
+      float ss[TPW];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        float kw[EPL];
+        widen<IO, EPL>(b[i].kr, kw);
+        ss[i] = 0.f;
+#pragma unroll
+        for (uint32_t e = 0; e < EPL; ++e) ss[i] = __builtin_fmaf(kw[e], kw[e], ss[i]);
+        if (SLANES < 64 && lane >= SLANES) ss[i] = 0.f;  // repeated parts
+      }
+      // The swap's results are vector elements: each is cast to a plain value
+      // before the bit cast, which otherwise reads the vector's first element
+      // whatever the index (clang 22).
+      float h[TPW / 2];
+#pragma unroll
+      for (int i = 0; i < TPW / 2; ++i) {
+        const auto w = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ss[2 * i]),
+                                                        __builtin_bit_cast(uint32_t, ss[2 * i + 1]),
+                                                        false, false);
+        h[i] = __builtin_bit_cast(float, (uint32_t)w[0]) +
+               __builtin_bit_cast(float, (uint32_t)w[1]);
+      }
+      auto lane_value = [](float x, int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+      };
+      if constexpr (TPW == 2) {
+        float x = group_sum<16>(h[0]);
+        x += dpp<kDppBcast15>(x);
+        x = __builtin_amdgcn_rsqf(x + kNormEps);
+        inv[0] = lane_value(x, 31);
+        inv[1] = lane_value(x, 63);
+      } else {
+        const auto w = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, h[0]),
+                                                        __builtin_bit_cast(uint32_t, h[1]),
+                                                        false, false);
+        float x = group_sum<16>(__builtin_bit_cast(float, (uint32_t)w[0]) +
+                                __builtin_bit_cast(float, (uint32_t)w[1]));
+        x = __builtin_amdgcn_rsqf(x + kNormEps);
+        inv[0] = lane_value(x, 0);
+        inv[1] = lane_value(x, 32);
+        inv[2] = lane_value(x, 16);
+        inv[3] = lane_value(x, 48);
       }
     }
   };
@@ -809,10 +878,11 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
     // (512-token prefill 183.5 -> 178.5 us; dropping it after the write
     // instead: 185.4 us). raise: not raised yet by the caller.
     if (raise) __builtin_amdgcn_s_setprio(1);
-    // Normalised keys (NK): sk = c * inv * (cells . k) and the write adds
-    // delta * inv along the raw k, the same as using k * inv throughout.
+    // Normalised keys (NK, unless the staged keys are already scaled): sk =
+    // c * inv * (cells . k) and the write adds delta * inv along the raw k,
+    // the same as using k * inv throughout.
     float cs = c, bs = b;
-    if constexpr (NORMK) {
+    if constexpr (NORMK && !SNORM) {
       cs = c * kq.inv;
       bs = b * kq.inv;
     }
@@ -1041,8 +1111,10 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
         const uint32_t tk = wave * TPW + i;
         load_token(tk < T ? tk : T - 1, buf[i]);
       }
+      float ks[TPW] = {};
+      if constexpr (SNORM) staged_norms(buf, ks);
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[0][wave * TPW + i]);
+      for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[0][wave * TPW + i], ks[i]);
       __syncthreads();
       // Every request so far (state, the first chunk's g and beta, the first
       // group's v) completes before the loop. The compiler orders these
@@ -1184,8 +1256,10 @@ __global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
       }
       if constexpr (SHARE) {
         // Stage this wave's share of the next group, publish, switch blocks.
+        float ks[TPW] = {};
+        if constexpr (SNORM) staged_norms(buf, ks);
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[gb ^ 1][wave * TPW + i]);
+        for (int i = 0; i < TPW; ++i) stage_rows(buf[i], grp_lds[gb ^ 1][wave * TPW + i], ks[i]);
         store_held();
         __syncthreads();
         gb ^= 1;
