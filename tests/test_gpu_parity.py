@@ -783,6 +783,24 @@ def test_normalize_k_workloads():
             close(g_, e, f"{name}: raw keys {what}")
 
 
+
+def test_long_run_drift_normalised_keys():
+    """Key normalisation over a long run (T = 2048, raw keys of varied norms
+    and one all-zero row) on the two-row D_k = 128 multi-token kernel, whose
+    staging waves compute each key row's factor and stage the row scaled:
+    within tolerance of the oracle and the f64 shadow."""
+    shape = (128, 32, 2, 256, 2048, 1)
+    w = Workload("long_normk", 0, *shape, fold_q_scale=True, g_high=0.5)
+    x = raw_keys(make_inputs(w, seed=6), seed=8)
+    got = run(x, normalize_k=True)
+    for precision in ("f32", "f64"):
+        exp = ref(x, precision=precision, normalize_k=True)
+        for g_, e_, arr in zip(got, exp, ("output", "state_out")):
+            assert np.all(np.isfinite(g_)), arr
+            MARGINS.setdefault("drift_T2048_normk_32x256", {}).setdefault(arr, {})[
+                f"gpu_vs_{'oracle' if precision == 'f32' else 'f64'}"] = tol_used(g_, e_)
+            close(g_, e_, f"long-run normalised keys {arr} vs {precision}")
+
 # ------------------------------------------------------------------ plumbing
 
 def test_side_stream():
