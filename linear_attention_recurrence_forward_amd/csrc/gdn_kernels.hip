@@ -386,11 +386,7 @@ constexpr float kNormEps = 1e-6f;
 // gdn_decode. CAPTURE: also write the per-token state. IO: element
 // type of q, k, v and output (float or __bf16). NK: 0, or use every key row
 // as k / sqrt(sum k^2 + kNormEps), its factor computed per token (1) or a ring
-// group ahead (2; see GNORM).
-// Kernels with group-ahead factors ask for 3 waves per SIMD: the prefetch of
-// the next group's key rows would otherwise take the D_k = 128 instance one
-// register past the 168 that 3 waves allow (the compiler then spills two
-// values outside the token loop instead).
+// group ahead (2; see GNORM and SNORM).
 // Leading parameters (preloaded): the state base; d_v, n_k_heads, n_v_heads,
 // n_tokens; row_blocks (workgroups per (sequence, value head)) and groups
 // (value heads per key head) with host-computed reciprocals for the
@@ -399,7 +395,7 @@ constexpr float kNormEps = 1e-6f;
 // bits 0-7, 8-15 and 16-23 of shifts; and n_blocks, the grid size (the
 // grid's own size lives in kernel-argument memory).
 template <int DK, int C, int R, int WAVES, int NB, bool CAPTURE, typename IO, int NK>
-__global__ __launch_bounds__(WAVES * 64, NK == 2 ? 3 : 1) void gdn_recurrent(
+__global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(
     const float *state_in, uint32_t d_v, uint32_t n_k_heads, uint32_t n_v_heads,
     uint32_t n_tokens, uint32_t row_blocks, uint32_t groups, uint32_t rb_magic,
     uint32_t g_magic, uint32_t kh_magic, uint32_t shifts, uint32_t n_blocks, KernelArgs a) {
