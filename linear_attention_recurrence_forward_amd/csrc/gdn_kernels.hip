@@ -1972,7 +1972,11 @@ constexpr Geometry make_decode_geometry() {
 //                D_k = 64, 16 lanes per row (4 cells each), two waves and an
 //                eight-token ring (twice the waves of 8 lanes per row with
 //                8 cells): 512-token prefill 139 -> 96 us, 16 tokens 8.1 ->
-//                7.1 us, a 4-token verify with capture 4.6 -> 3.8 us. At
+//                7.1 us, a 4-token verify with capture 4.6 -> 3.8 us; four
+//                waves without capture (512 tokens of 16 sequences 213 ->
+//                199 us, of 64 sequences 800 -> 720 us, D_v = 128 115 ->
+//                103 us, key-normalised 91 -> 87 us, 1 to 4 sequences 1-3%
+//                faster; capture calls ~3% slower, so they keep two). At
 //                D_k = 32, 8 lanes per row and two waves (32 rows, so a D_v
 //                = 32 head has no padding waves; four waves had two of them):
 //                512 tokens of 16 sequences 118 -> 108 us, of 64 sequences
@@ -2014,7 +2018,13 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
           return make_decode_geometry<64, 4, 1, 4, CAPTURE, IO, NK1, true>();
         return make_decode_geometry<64, 4, 2, 4, CAPTURE, IO, NK1, false>();
       }
-      const Geometry geo = make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
+      // Four waves without capture (each staging wave loads two tokens of a
+      // ring group instead of four); two with capture.
+      Geometry geo;
+      if constexpr (CAPTURE)
+        geo = make_geometry<64, 4, 2, 2, 8, CAPTURE, IO, NK>();
+      else
+        geo = make_geometry<64, 4, 2, 4, 8, CAPTURE, IO, NK>();
       if (n_tokens <= 4) return with_short<64, 4, 4, 4, CAPTURE, IO, NK1>(geo);
       if (n_tokens <= 8) return with_short<64, 4, 4, 8, CAPTURE, IO, NK1>(geo);
       if (short16) return with_short<64, 4, 4, 16, CAPTURE, IO, NK1>(geo);
