@@ -2046,10 +2046,14 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
       } else {
         // Below one two-row workgroup per compute unit the waves run their
         // token loops nearly alone: one row per lane (half the work per wave
-        // and token) and two waves per workgroup. One dense-shape sequence
-        // of 512 tokens: 125.4 -> 116.9 us; of 64 tokens: 19.4 -> 18.9 us.
+        // and token). One dense-shape sequence of 512 tokens: 125.4 -> 116.9
+        // us; of 64 tokens: 19.4 -> 18.9 us. Four waves per workgroup rather
+        // than two (each staging wave loads two tokens of a ring group
+        // instead of four): 512 tokens 105.4 -> 102.6 us, 2048 tokens 407 ->
+        // 397 us, key-normalised 112.2 -> 108.6 us, the MoE head count 103.5
+        // -> 97.4 us.
         if (heads * ((d_v + 31) / 32) < kComputeUnits)
-          geo = make_geometry<128, 8, 1, 2, 8, CAPTURE, IO, NK>();
+          geo = make_geometry<128, 8, 1, 4, 8, CAPTURE, IO, NK>();
         else
           geo = make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NK>();
       }
