@@ -165,8 +165,10 @@ gdn_status gdn_check_params(const gdn_params *p) {
     return GDN_ERR_SIZE_OVERFLOW;
   // The grid (one-token and short calls: key heads padded to a power of two,
   // at least 8, or on the memory-order and wide one-token grids a head's row
-  // blocks) times the threads per block (at most 256) must stay below 2^32
-  // work-items, for every kernel, with or without capture.
+  // blocks) times the threads per block must stay below 2^32 work-items, for
+  // every kernel, with or without capture. Blocks have at most 256 threads,
+  // except the multi-token kernel's 512-thread geometry, which is chosen only
+  // for grids of at most 256 blocks.
   for (bool cap : {false, true}) {
     const uint64_t blocks = gdn::grid_blocks(p->d_k, p->d_v, p->n_k_heads, p->n_v_heads,
                                              p->n_seqs, p->n_tokens, cap);

@@ -767,20 +767,21 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(
       }
     }
   };
-  // SNORM: the factors 1 / sqrt(sum k^2 + kNormEps) of the TPW (2 or 4) key
-  // rows this wave stages, from the parts its lanes hold. Each lane sums the
-  // squares of its part of every row; swapping the wave halves of rows 2i
+  // SNORM: the factors 1 / sqrt(sum k^2 + kNormEps) of the TPW (1, 2 or 4)
+  // key rows this wave stages, from the parts its lanes hold. Each lane sums
+  // the squares of its part of every row; swapping the wave halves of rows 2i
   // and 2i+1 and adding leaves row 2i's partials in lanes 0-31 and row
-  // 2i+1's in lanes 32-63 of one register. With four rows, swapping the odd
-  // 16-lane rows of the first such register with the even ones of the second
-  // and adding gives one register whose 16-lane rows hold the partials of
-  // key rows 0, 2, 1 and 3; a butterfly within 16 lanes completes every sum.
-  // With two rows the butterfly leaves half sums, and adding the row below's
-  // lane 15 completes them in lanes 31 and 63. Wave-uniform results, a few
-  // cross-lane steps per group for the wave's rows instead of a butterfly
-  // and a factor multiply per token.
+  // 2i+1's in lanes 32-63 of one register (one row: the row with itself).
+  // With four rows, swapping the odd 16-lane rows of the first such register
+  // with the even ones of the second and adding gives one register whose
+  // 16-lane rows hold the partials of key rows 0, 2, 1 and 3; a butterfly
+  // within 16 lanes completes every sum. With one or two rows the butterfly
+  // leaves half sums, and adding the row below's lane 15 completes them in
+  // lanes 31 and 63. Wave-uniform results, a few cross-lane steps per group
+  // for the wave's rows instead of a butterfly and a factor multiply per
+  // token.
   auto staged_norms = [&](const Tok (&b)[TPW], float (&inv)[TPW]) {
-    static_assert(!SNORM || TPW == 2 || TPW == 4, "two or four staged rows");
+    static_assert(!SNORM || TPW == 1 || TPW == 2 || TPW == 4, "1, 2 or 4 staged rows");
     if constexpr (SNORM) {
       float ss[TPW];
 #pragma unroll
@@ -795,24 +796,26 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_recurrent(
       // The swap's results are vector elements: each is cast to a plain value
       // before the bit cast, which otherwise reads the vector's first element
       // whatever the index (clang 22).
-      float h[TPW / 2];
+      constexpr int NH = TPW > 1 ? TPW / 2 : 1;  // row pairs
+      float h[NH];
 #pragma unroll
-      for (int i = 0; i < TPW / 2; ++i) {
+      for (int i = 0; i < NH; ++i) {
+        const float odd = ss[TPW > 1 ? 2 * i + 1 : 0];
         const auto w = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ss[2 * i]),
-                                                        __builtin_bit_cast(uint32_t, ss[2 * i + 1]),
-                                                        false, false);
+                                                        __builtin_bit_cast(uint32_t, odd), false,
+                                                        false);
         h[i] = __builtin_bit_cast(float, (uint32_t)w[0]) +
                __builtin_bit_cast(float, (uint32_t)w[1]);
       }
       auto lane_value = [](float x, int l) {
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
       };
-      if constexpr (TPW == 2) {
+      if constexpr (TPW <= 2) {
         float x = group_sum<16>(h[0]);
         x += dpp<kDppBcast15>(x);
         x = __builtin_amdgcn_rsqf(x + kNormEps);
         inv[0] = lane_value(x, 31);
-        inv[1] = lane_value(x, 63);
+        if constexpr (TPW == 2) inv[1] = lane_value(x, 63);
       } else {
         const auto w = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, h[0]),
                                                         __builtin_bit_cast(uint32_t, h[1]),
@@ -2052,8 +2055,17 @@ Geometry pick(uint32_t d_k, uint32_t d_v, uint64_t heads, uint32_t n_tokens) {
         // instead of four): 512 tokens 105.4 -> 102.6 us, 2048 tokens 407 ->
         // 397 us, key-normalised 112.2 -> 108.6 us, the MoE head count 103.5
         // -> 97.4 us.
+        // Two rows per lane from one two-row workgroup per compute unit on:
+        // eight waves per workgroup while that grid (64 rows each) fits the
+        // chip in one round (each staging wave loads one token of a ring
+        // group; 512 tokens of two dense-shape sequences 111.5 -> 106.5 us,
+        // of three and four MoE-shape sequences 111.5 -> 106.0 and 113.6 ->
+        // 108.8 us), four past it (one 512-thread workgroup fits a compute
+        // unit: three dense-shape sequences took 209 against 132 us).
         if (heads * ((d_v + 31) / 32) < kComputeUnits)
           geo = make_geometry<128, 8, 1, 4, 8, CAPTURE, IO, NK>();
+        else if (heads * ((d_v + 63) / 64) <= kComputeUnits)
+          geo = make_geometry<128, 8, 2, 8, 8, CAPTURE, IO, NK>();
         else
           geo = make_geometry<128, 8, 2, 4, 8, CAPTURE, IO, NK>();
       }

@@ -328,13 +328,20 @@ def test_decay_extremes():
                  "zero state, beta = 0: zero outputs through the growth tokens")
 
 
-@pytest.mark.parametrize("shape", [(128, 128, 2, 4, 2048, 1), (128, 32, 2, 256, 2048, 1)],
-                         ids=["one_row_kernel", "two_row_kernel"])
+DRIFT_SHAPES = {
+    "one_row_kernel": (128, 128, 2, 4, 2048, 1),
+    # two rows per lane: eight waves per workgroup (a grid of at most 256
+    # workgroups of 64 rows), and four
+    "two_row_eight_waves": (128, 32, 2, 256, 2048, 1),
+    "two_row_four_waves": (128, 32, 2, 512, 2048, 1),
+}
+
+
+@pytest.mark.parametrize("shape", list(DRIFT_SHAPES.values()), ids=list(DRIFT_SHAPES))
 def test_long_run_drift(shape):
     """A long run (T = 2048) stays within tolerance of the oracle and the f64
     shadow: no drift from the exp, the lazy decay's reassociation or the
-    reduction order; on the one-row and the two-row (256 workgroups)
-    D_k = 128 multi-token kernels."""
+    reduction order; on every D_k = 128 multi-token layout."""
     w = Workload("long", 0, *shape, fold_q_scale=True, g_high=0.5)
     x = make_inputs(w, seed=5)
     got = run(x)
@@ -606,7 +613,13 @@ INSTANCE_CLASSES = {
     "short8": (24, 2, 4, 6, 2),
     "short16": (24, 2, 4, 13, 2),
     "general_small": (24, 2, 4, 20, 2),
-    "general_large": (40, 16, 64, 20, 4),
+    "general_large": (40, 16, 128, 20, 4),
+    # two rows per lane, eight waves: D_k = 128 grids of 256 workgroups of 64
+    # rows or fewer, past the one-row layout's threshold
+    "general_mid_grid": (128, 16, 96, 20, 1),
+    # the same layout for 9 to 16 tokens (per-token key factors): 128 key
+    # heads, past the short kernel's size word
+    "general_mid_grid_nk128": (128, 128, 128, 12, 1),
     # 9 to 15 tokens on the general kernel (per-token key factors): past the
     # short kernel's row limit (two rows per lane), and past its size word on
     # a small grid (one row per lane)
@@ -727,10 +740,13 @@ NORM_SHAPES = [
     # lane) and a call of exactly 16 tokens
     (32, 24, 1, 2, 40, 1),
     (128, 32, 1, 2, 16, 1),
-    # the two-row D_k = 128 multi-token kernel, per-token and group-ahead
-    # factors
+    # 13 tokens on the short kernel's 16-token instance (per-token factors)
     (128, 40, 4, 64, 13, 2),
+    # the two-row D_k = 128 multi-token layouts, group-ahead factors: eight
+    # waves per workgroup, and four (past 256 workgroups of 64 rows; tokens
+    # after the last ring group)
     (128, 72, 8, 96, 20, 1),
+    (128, 40, 16, 320, 21, 1),
 ]
 
 
@@ -784,12 +800,14 @@ def test_normalize_k_workloads():
 
 
 
-def test_long_run_drift_normalised_keys():
+@pytest.mark.parametrize("layout", ["two_row_eight_waves", "two_row_four_waves"])
+def test_long_run_drift_normalised_keys(layout):
     """Key normalisation over a long run (T = 2048, raw keys of varied norms
-    and one all-zero row) on the two-row D_k = 128 multi-token kernel, whose
-    staging waves compute each key row's factor and stage the row scaled:
-    within tolerance of the oracle and the f64 shadow."""
-    shape = (128, 32, 2, 256, 2048, 1)
+    and one all-zero row) on the two-row D_k = 128 multi-token layouts, whose
+    staging waves (one or two key rows each per ring group) compute each key
+    row's factor and stage the row scaled: within tolerance of the oracle and
+    the f64 shadow."""
+    shape = DRIFT_SHAPES[layout]
     w = Workload("long_normk", 0, *shape, fold_q_scale=True, g_high=0.5)
     x = raw_keys(make_inputs(w, seed=6), seed=8)
     got = run(x, normalize_k=True)
@@ -797,7 +815,7 @@ def test_long_run_drift_normalised_keys():
         exp = ref(x, precision=precision, normalize_k=True)
         for g_, e_, arr in zip(got, exp, ("output", "state_out")):
             assert np.all(np.isfinite(g_)), arr
-            MARGINS.setdefault("drift_T2048_normk_32x256", {}).setdefault(arr, {})[
+            MARGINS.setdefault(f"drift_T2048_normk_32x{shape[3]}", {}).setdefault(arr, {})[
                 f"gpu_vs_{'oracle' if precision == 'f32' else 'f64'}"] = tol_used(g_, e_)
             close(g_, e_, f"long-run normalised keys {arr} vs {precision}")
 
