@@ -819,6 +819,33 @@ def test_long_run_drift_normalised_keys(layout):
                 f"gpu_vs_{'oracle' if precision == 'f32' else 'f64'}"] = tol_used(g_, e_)
             close(g_, e_, f"long-run normalised keys {arr} vs {precision}")
 
+
+# D_k = 128 multi-token calls of 17 tokens (past the short kernel) on both
+# sides of each layout threshold: value heads x sequences x row blocks of 32
+# rows below 256 (one row per lane) or not, and row blocks of 64 rows at most
+# 256 (two rows per lane, eight waves) or past it (four waves).
+THRESHOLD_SHAPES = {
+    "one_row_252": (128, 128, 1, 63, 17, 1),
+    "two_row_eight_waves_128": (128, 128, 1, 64, 17, 1),
+    "two_row_eight_waves_256": (128, 128, 1, 128, 17, 1),
+    "two_row_four_waves_258": (128, 128, 1, 129, 17, 1),
+}
+
+
+@pytest.mark.parametrize("normalize_k", [False, True], ids=["rawk", "normk"])
+@pytest.mark.parametrize("shape", list(THRESHOLD_SHAPES.values()), ids=list(THRESHOLD_SHAPES))
+def test_layout_thresholds(shape, normalize_k):
+    """Shapes on both sides of the multi-token layout thresholds against the
+    oracle (keys of varied norms when normalised in the kernel)."""
+    w = Workload("threshold", 0, *shape, fold_q_scale=True)
+    x = make_inputs(w, seed=sum(shape))
+    if normalize_k:
+        x = raw_keys(x, seed=sum(shape) + 1)
+    got = run(x, normalize_k=normalize_k)
+    exp = ref(x, normalize_k=normalize_k)
+    for g_, e_, what in zip(got, exp, ("output", "state_out")):
+        close(g_, e_, f"{shape} normalize_k={normalize_k} {what}")
+
 # ------------------------------------------------------------------ plumbing
 
 def test_side_stream():
