@@ -1964,7 +1964,10 @@ constexpr Geometry make_decode_geometry() {
 //                lost to the general kernel (16 tokens 8.38 against 6.88 us).
 //   longer     : two rows per lane (each k/q register feeds two rows, which
 //                halves k/q operand traffic per cell: 418 -> 289 us at 512
-//                tokens against one row per lane), 16 lanes per row, 4 waves.
+//                tokens against one row per lane), 16 lanes per row, 4 waves
+//                (at D_k = 128 eight while the grid fits the chip in one
+//                round, and one row per lane on grids below one workgroup per
+//                compute unit; see pick()).
 //                Without capture an eight-token prefetch ring and lazy group
 //                (512-token prefill 221 -> 206 us against four tokens without
 //                the lazy form). With capture, which runs eagerly and is bound
